@@ -1,0 +1,234 @@
+"""ctypes binding of liblora_sgmv.so (argument marshalling only).
+
+Every computation runs in the HIP library; this module only turns torch
+tensors and numpy arrays into the pointers and sizes of the C ABI declared
+in include/lora_sgmv.h, and raises LoraError on a non-zero status. There is
+no fallback path: if the library is not built, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblora_sgmv.so")
+
+LORA_OK = 0
+LORA_INVALID_ARGUMENT = 1
+LORA_UNSUPPORTED = 2
+LORA_WORKSPACE_TOO_SMALL = 3
+LORA_DEVICE_ERROR = 4
+
+OP_SHRINK, OP_EXPAND, OP_FUSED, OP_BACKWARD = 0, 1, 2, 3
+GRAD_ACCUMULATE = 1
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[{status}] {msg}")
+        self.status = status
+
+
+class CAdapters(ctypes.Structure):
+    _fields_ = [("num_adapters", ctypes.c_int32), ("h_in", ctypes.c_int32),
+                ("h_out", ctypes.c_int32), ("A_ptrs", ctypes.c_void_p),
+                ("B_ptrs", ctypes.c_void_p), ("ranks", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p)]
+
+
+class CSegments(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("num_segments", ctypes.c_int32),
+                ("seg_starts", ctypes.c_void_p), ("seg_adapter", ctypes.c_void_p),
+                ("token_rows", ctypes.c_void_p)]
+
+
+EXPORTS = ["lora_segments_from_ids", "lora_workspace_size", "lora_sgmv_shrink", "lora_sgmv_expand",
+           "lora_sgmv_fused", "lora_packed_backward", "lora_status_string", "lora_last_error",
+           "lora_version"]
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m lora_adapter_batching_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.lora_segments_from_ids.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P]
+    lib.lora_workspace_size.argtypes = [ctypes.c_int, ctypes.POINTER(CAdapters),
+                                        ctypes.POINTER(CSegments), ctypes.POINTER(ctypes.c_size_t)]
+    lib.lora_sgmv_shrink.argtypes = [P, I64, ctypes.POINTER(CAdapters), ctypes.POINTER(CSegments),
+                                     P, I64, P, ctypes.c_size_t, P]
+    lib.lora_sgmv_expand.argtypes = [P, I64, ctypes.POINTER(CAdapters), ctypes.POINTER(CSegments),
+                                     P, I64, P, ctypes.c_size_t, P]
+    lib.lora_sgmv_fused.argtypes = [P, I64, ctypes.POINTER(CAdapters), ctypes.POINTER(CSegments),
+                                    P, I64, P, I64, P, ctypes.c_size_t, P]
+    lib.lora_packed_backward.argtypes = [P, I64, P, I64, P, I64, ctypes.POINTER(CAdapters),
+                                         ctypes.POINTER(CSegments), P, I64, P, P, ctypes.c_uint32,
+                                         P, ctypes.c_size_t, P]
+    lib.lora_status_string.restype = ctypes.c_char_p
+    lib.lora_status_string.argtypes = [ctypes.c_int]
+    lib.lora_last_error.restype = ctypes.c_char_p
+    lib.lora_version.restype = ctypes.c_int
+    for name in EXPORTS:
+        if name not in ("lora_status_string", "lora_last_error", "lora_version"):
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != LORA_OK:
+        lib = load()
+        raise LoraError(status, lib.lora_last_error().decode())
+
+
+def _ptr(t) -> int:
+    """Device or host address of a torch tensor / numpy array (0 for None)."""
+    if t is None:
+        return 0
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class Adapters:
+    """Adapters resident on the GPU: device pointer tables + host ranks/scales.
+
+    A, B: sequences of device bf16 tensors, A[i] [r_i, h_in], B[i] [h_out, r_i]
+    (None allowed for rank 0). The pointer tables are int64 device tensors,
+    so they can be rewritten in place between calls.
+    """
+
+    def __init__(self, A: Sequence, B: Sequence, ranks, scales, h_in: int, h_out: int,
+                 device=None):
+        import torch
+        self.A, self.B = list(A), list(B)
+        self.ranks = np.ascontiguousarray(ranks, dtype=np.int32)
+        self.scales = np.ascontiguousarray(scales, dtype=np.float32)
+        self.h_in, self.h_out = int(h_in), int(h_out)
+        dev = device if device is not None else "cuda"
+        self.A_ptrs = torch.tensor([_ptr(a) for a in self.A], dtype=torch.int64, device=dev)
+        self.B_ptrs = torch.tensor([_ptr(b) for b in self.B], dtype=torch.int64, device=dev)
+        self._c = CAdapters(len(self.ranks), self.h_in, self.h_out, _ptr(self.A_ptrs),
+                            _ptr(self.B_ptrs), self.ranks.ctypes.data, self.scales.ctypes.data)
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+class Segments:
+    """A batch in sorted-position order cut into one-adapter segments.
+
+    seg_starts [S+1] and seg_adapter [S] are host arrays; token_rows is an
+    optional int32 device tensor (row of x/y used by each sorted position).
+    """
+
+    def __init__(self, seg_starts, seg_adapter, token_rows=None):
+        self.seg_starts = np.ascontiguousarray(seg_starts, dtype=np.int32)
+        self.seg_adapter = np.ascontiguousarray(seg_adapter, dtype=np.int32)
+        self.token_rows = token_rows
+        S = int(self.seg_adapter.shape[0])
+        T = int(self.seg_starts[-1]) if self.seg_starts.size else 0
+        self._c = CSegments(T, S, self.seg_starts.ctypes.data if S or self.seg_starts.size else 0,
+                            self.seg_adapter.ctypes.data if S else 0, _ptr(token_rows))
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self._c.num_tokens)
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def segments_from_ids(ids: np.ndarray, num_adapters: int):
+    """Host bookkeeping: (perm [T], seg_starts [N+2], seg_adapter [N+1])."""
+    lib = load()
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T = int(ids.shape[0])
+    perm = np.zeros(max(T, 1), np.int32)
+    starts = np.zeros(num_adapters + 2, np.int32)
+    adap = np.zeros(num_adapters + 1, np.int32)
+    _check(lib.lora_segments_from_ids(ids.ctypes.data if T else None, T, int(num_adapters),
+                                      perm.ctypes.data, starts.ctypes.data, adap.ctypes.data))
+    return perm[:T], starts, adap
+
+
+def workspace_size(op: int, adapters: Adapters, segments: Optional[Segments] = None) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check(lib.lora_workspace_size(op, adapters.c, segments.c if segments is not None else None,
+                                   ctypes.byref(n)))
+    return int(n.value)
+
+
+def new_workspace(op: int, adapters: Adapters, segments: Optional[Segments] = None, device="cuda"):
+    """A zero-filled workspace tensor of the size `op` needs."""
+    import torch
+    n = workspace_size(op, adapters, segments)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _ws(ws):
+    if ws is None:
+        return 0, 0
+    return _ptr(ws), int(ws.numel() * ws.element_size())
+
+
+def sgmv_shrink(x, adapters: Adapters, segments: Segments, u, ws=None, stream=None):
+    lib = load()
+    wp, wb = _ws(ws)
+    _check(lib.lora_sgmv_shrink(_ptr(x), x.stride(0), adapters.c, segments.c, _ptr(u), u.stride(0),
+                                wp, wb, _stream_handle(stream)))
+
+
+def sgmv_expand(u, adapters: Adapters, segments: Segments, y, ws=None, stream=None):
+    lib = load()
+    wp, wb = _ws(ws)
+    _check(lib.lora_sgmv_expand(_ptr(u), u.stride(0), adapters.c, segments.c, _ptr(y), y.stride(0),
+                                wp, wb, _stream_handle(stream)))
+
+
+def sgmv_fused(x, adapters: Adapters, segments: Segments, y, u_save=None, ws=None, stream=None):
+    lib = load()
+    wp, wb = _ws(ws)
+    ldu = u_save.stride(0) if u_save is not None else 0
+    _check(lib.lora_sgmv_fused(_ptr(x), x.stride(0), adapters.c, segments.c, _ptr(y), y.stride(0),
+                               _ptr(u_save), ldu, wp, wb, _stream_handle(stream)))
+
+
+def packed_backward(x, dy, u, adapters: Adapters, segments: Segments, dx, dA_ptrs, dB_ptrs,
+                    flags: int = 0, ws=None, stream=None):
+    """dA_ptrs / dB_ptrs: int64 device tensors of fp32 gradient addresses."""
+    lib = load()
+    wp, wb = _ws(ws)
+    _check(lib.lora_packed_backward(
+        _ptr(x), x.stride(0) if x is not None else 0, _ptr(dy), dy.stride(0) if dy is not None else 0,
+        _ptr(u), u.stride(0) if u is not None else 0, adapters.c, segments.c, _ptr(dx),
+        dx.stride(0) if dx is not None else 0, _ptr(dA_ptrs), _ptr(dB_ptrs), int(flags), wp, wb,
+        _stream_handle(stream)))
+
+
+def version() -> int:
+    return int(load().lora_version())

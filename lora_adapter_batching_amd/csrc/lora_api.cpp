@@ -1,0 +1,678 @@
+// lora_api.cpp -- C ABI, host-side validation, token bookkeeping, the work
+// planner (segment scheduler) and launch orchestration of the MI355X
+// multi-adapter LoRA library. See include/lora_sgmv.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/lora_sgmv.h"
+#include "lora_plan.h"
+
+namespace lora {
+hipError_t launch_fwd(const FwdPlan& P, hipStream_t stream);
+hipError_t launch_transpose(const TransposePlan& P, hipStream_t stream);
+hipError_t launch_wgrad(const WgradPlan& P, int grid, hipStream_t stream);
+int wgrad_items_for_rank(int rank, int h_in, int h_out);
+}  // namespace lora
+
+using namespace lora;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+// ---------------------------------------------------------------------------
+// Tunables of the planner
+// ---------------------------------------------------------------------------
+constexpr int kMaxKs = 16;            // largest split of the shrink reduction
+constexpr int kMaxPartials = 512;     // tiles * ks in split modes (bounds the workspace)
+constexpr int kMaxDepTiles = 1024 - kCtrTiles;  // counter slots
+constexpr size_t kCounterBytes = 4096;
+constexpr int kMinKChunk = 256;       // smallest k-chunk of a split shrink
+constexpr int kMaxSlots = kMaxJobs;   // adapters per backward group
+
+struct DeviceInfo {
+  int cus = 256;
+  int wall_khz = 100000;
+};
+
+DeviceInfo device_info() {
+  static std::mutex mu;
+  static DeviceInfo cache[64];
+  static bool have[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DeviceInfo{};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!have[dev]) {
+    DeviceInfo d;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      d.cus = v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) == hipSuccess && v > 0)
+      d.wall_khz = v;
+    cache[dev] = d;
+    have[dev] = true;
+  }
+  return cache[dev];
+}
+
+int round_up(int a, int b) { return (a + b - 1) / b * b; }
+// Row length of a split-K partial tile: the kernels write 32 * RB rows with
+// RB = 1, 2 or 4 rank blocks of 32.
+int rpad_for(int rmax) { return rmax <= 32 ? 32 : (rmax <= 64 ? 64 : 128); }
+int64_t round_up64(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct ActiveSeg {
+  int tok0, ntok, adapter, rank;
+  float scale;
+};
+
+// ---------------------------------------------------------------------------
+// Validation (host mirrors only; no HIP call)
+// ---------------------------------------------------------------------------
+int check_adapters(const lora_adapters_t* a) {
+  if (!a) return fail(LORA_INVALID_ARGUMENT, "adapters is NULL");
+  if (a->num_adapters < 1) return fail(LORA_INVALID_ARGUMENT, "num_adapters must be >= 1");
+  if (a->h_in <= 0 || a->h_out <= 0)
+    return fail(LORA_INVALID_ARGUMENT, "h_in and h_out must be positive");
+  if ((a->h_in & 7) || (a->h_out & 7))
+    return fail(LORA_INVALID_ARGUMENT, "h_in (%d) and h_out (%d) must be multiples of 8", a->h_in,
+                a->h_out);
+  if (!a->ranks || !a->scales) return fail(LORA_INVALID_ARGUMENT, "ranks/scales host arrays are NULL");
+  for (int i = 0; i < a->num_adapters; ++i) {
+    if (a->ranks[i] < 0) return fail(LORA_INVALID_ARGUMENT, "rank of adapter %d is negative", i);
+    if (a->ranks[i] > LORA_MAX_RANK)
+      return fail(LORA_UNSUPPORTED, "rank %d of adapter %d exceeds %d", a->ranks[i], i, LORA_MAX_RANK);
+    if (!std::isfinite(a->scales[i])) return fail(LORA_INVALID_ARGUMENT, "scale of adapter %d is not finite", i);
+  }
+  return LORA_OK;
+}
+
+int check_segments(const lora_segments_t* s, int N) {
+  if (!s) return fail(LORA_INVALID_ARGUMENT, "segments is NULL");
+  if (s->num_tokens < 0 || s->num_segments < 0)
+    return fail(LORA_INVALID_ARGUMENT, "num_tokens and num_segments must be >= 0");
+  if (s->num_segments == 0) {
+    if (s->num_tokens != 0) return fail(LORA_INVALID_ARGUMENT, "tokens present but no segments");
+    return LORA_OK;
+  }
+  if (!s->seg_starts || !s->seg_adapter)
+    return fail(LORA_INVALID_ARGUMENT, "seg_starts/seg_adapter host arrays are NULL");
+  if (s->seg_starts[0] != 0) return fail(LORA_INVALID_ARGUMENT, "seg_starts[0] must be 0");
+  for (int g = 0; g < s->num_segments; ++g) {
+    if (s->seg_starts[g + 1] < s->seg_starts[g])
+      return fail(LORA_INVALID_ARGUMENT, "seg_starts decreases at segment %d", g);
+    const int a = s->seg_adapter[g];
+    if (a < -1 || a >= N) return fail(LORA_INVALID_ARGUMENT, "seg_adapter[%d] = %d outside [-1, %d)", g, a, N);
+  }
+  if (s->seg_starts[s->num_segments] != s->num_tokens)
+    return fail(LORA_INVALID_ARGUMENT, "seg_starts[S] = %d differs from num_tokens = %d",
+                s->seg_starts[s->num_segments], s->num_tokens);
+  return LORA_OK;
+}
+
+std::vector<ActiveSeg> active_segments(const lora_adapters_t* a, const lora_segments_t* s) {
+  std::vector<ActiveSeg> v;
+  for (int g = 0; g < s->num_segments; ++g) {
+    const int ad = s->seg_adapter[g];
+    const int n = s->seg_starts[g + 1] - s->seg_starts[g];
+    if (ad < 0 || n == 0 || a->ranks[ad] == 0) continue;
+    v.push_back(ActiveSeg{s->seg_starts[g], n, ad, a->ranks[ad], a->scales[ad]});
+  }
+  return v;
+}
+
+int check_rows(const void* p, int64_t ld, int width, const char* name, bool needed) {
+  if (!needed) return LORA_OK;
+  if (!p) return fail(LORA_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned16(p)) return fail(LORA_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  if (ld < width) return fail(LORA_INVALID_ARGUMENT, "row stride of %s (%lld) is below its width %d", name,
+                              (long long)ld, width);
+  if (ld & 7) return fail(LORA_INVALID_ARGUMENT, "row stride of %s (%lld) is not a multiple of 8", name,
+                          (long long)ld);
+  return LORA_OK;
+}
+
+int check_u(const float* u, int64_t ldu, int rmax, const char* name) {
+  if (!u) return fail(LORA_INVALID_ARGUMENT, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(u) & 3u) return fail(LORA_INVALID_ARGUMENT, "%s is not 4-byte aligned", name);
+  if (ldu < rmax) return fail(LORA_INVALID_ARGUMENT, "row stride of %s (%lld) is below the largest rank used (%d)",
+                              name, (long long)ldu, rmax);
+  return LORA_OK;
+}
+
+int max_rank_all(const lora_adapters_t* a) {
+  int r = 0;
+  for (int i = 0; i < a->num_adapters; ++i) r = std::max(r, a->ranks[i]);
+  return r;
+}
+int max_rank_used(const std::vector<ActiveSeg>& v) {
+  int r = 0;
+  for (const auto& s : v) r = std::max(r, s.rank);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout
+// ---------------------------------------------------------------------------
+struct WsLayout {
+  size_t counters = 0, partials = 0, du = 0, urec = 0, bt = 0, at = 0, total = 0;
+  int64_t lddu = 0;
+  int64_t bt_slot = 0, at_slot = 0;  // elements per slot
+};
+
+WsLayout ws_layout(int op, const lora_adapters_t* a, const lora_segments_t* s) {
+  WsLayout L;
+  const int rmax = max_rank_all(a);
+  const int rpad = rpad_for(rmax);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (off + bytes + 255) / 256 * 256;
+    return o;
+  };
+  if (op == LORA_OP_EXPAND) {
+    L.total = 0;
+    return L;
+  }
+  L.counters = take(kCounterBytes);
+  L.partials = take((size_t)kMaxPartials * kTileM * rpad * sizeof(float));
+  if (op == LORA_OP_BACKWARD) {
+    const int64_t T = s ? s->num_tokens : 0;
+    L.lddu = round_up(std::max(rmax, 1), 4);
+    L.du = take((size_t)T * L.lddu * sizeof(float));
+    L.urec = take((size_t)T * L.lddu * sizeof(float));
+    const int slots = std::min(a->num_adapters, kMaxSlots);
+    L.bt_slot = round_up64((int64_t)rmax * a->h_out, 8);
+    L.at_slot = round_up64((int64_t)a->h_in * round_up(std::max(rmax, 1), 8), 8);
+    L.bt = take((size_t)slots * L.bt_slot * 2);
+    L.at = take((size_t)slots * L.at_slot * 2);
+  }
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Planner: forward-style launches
+// ---------------------------------------------------------------------------
+// Orders segments so that heavy work is dispatched first (longest first),
+// which lets the in-order workgroup dispatcher balance ranks and lengths.
+void order_by_cost(std::vector<ActiveSeg>& v, int K, int N) {
+  std::stable_sort(v.begin(), v.end(), [&](const ActiveSeg& x, const ActiveSeg& y) {
+    const double cx = (double)cdiv(x.ntok, kTileM) * (2.0 * K + 4.0 * N + 2.0 * x.rank * (K + N) / 8.0);
+    const double cy = (double)cdiv(y.ntok, kTileM) * (2.0 * K + 4.0 * N + 2.0 * y.rank * (K + N) / 8.0);
+    return cx > cy;
+  });
+}
+
+struct FwdCall {
+  int mode_op;  // LORA_OP_SHRINK / EXPAND / FUSED
+  const uint16_t* X;
+  int64_t ldx;
+  uint16_t* Y;
+  int64_t ldy;
+  float* U;
+  int64_t ldu;
+  bool write_u;
+  const uint64_t* Wtab;
+  const uint64_t* Vtab;
+  const uint16_t* Wslots;
+  const uint16_t* Vslots;
+  int64_t w_slot_elems, v_slot_elems;
+  int v_round;
+  int scale_in_shrink;
+  int K, N;
+  const int32_t* token_rows;
+  float* partials;
+  int32_t* counters;
+  int rmax;  // largest rank of the adapters (partials row length)
+};
+
+int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int>& slot_of,
+            hipStream_t stream) {
+  if (segs.empty()) return LORA_OK;
+  const DeviceInfo dev = device_info();
+  const int cus = dev.cus;
+  order_by_cost(segs, c.K, c.N);
+  // split into launches of at most kMaxSeg segments
+  for (size_t base = 0; base < segs.size(); base += kMaxSeg) {
+    const int ns = (int)std::min<size_t>(kMaxSeg, segs.size() - base);
+    FwdPlan P;
+    std::memset(&P, 0, sizeof(P));
+    P.X = c.X; P.ldx = c.ldx; P.Y = c.Y; P.ldy = c.ldy; P.U = c.U; P.ldu = c.ldu;
+    P.Wtab = c.Wtab; P.Vtab = c.Vtab; P.Wslots = c.Wslots; P.Vslots = c.Vslots;
+    P.w_slot_elems = c.w_slot_elems; P.v_slot_elems = c.v_slot_elems;
+    P.token_rows = c.token_rows; P.partials = c.partials; P.counters = c.counters;
+    P.K = c.K; P.N = c.N; P.v_round = c.v_round; P.scale_in_shrink = c.scale_in_shrink;
+    P.write_u = c.write_u ? 1 : 0;
+    P.rpad = rpad_for(c.rmax);
+    int tiles = 0;
+    for (int i = 0; i < ns; ++i) {
+      const ActiveSeg& s = segs[base + i];
+      P.seg_tok0[i] = s.tok0;
+      P.seg_ntok[i] = s.ntok;
+      P.seg_tile0[i] = tiles;
+      P.seg_adapter[i] = s.adapter;
+      P.seg_scale[i] = s.scale;
+      P.seg_rank[i] = (uint8_t)s.rank;
+      P.seg_slot[i] = (uint8_t)(slot_of.empty() ? 0 : slot_of[s.adapter]);
+      tiles += cdiv(s.ntok, kTileM);
+    }
+    P.n_seg = ns;
+    P.n_tiles = tiles;
+    const int nblocks = cdiv(c.N, 32);
+    const int target = 2 * cus;
+    auto choose_ks = [&]() {
+      int ks = 1;
+      if (tiles < cus) ks = cdiv(target, tiles);
+      ks = std::min({ks, kMaxKs, std::max(1, c.K / kMinKChunk), std::max(1, kMaxPartials / tiles)});
+      ks = std::max(ks, 1);
+      const int kchunk = round_up(cdiv(c.K, ks), 64);
+      P.kchunk = kchunk;
+      P.ks = cdiv(c.K, kchunk);
+    };
+    auto choose_nc = [&]() {
+      int nc = std::max(1, cdiv(target, tiles));
+      nc = std::min(nc, std::max(1, nblocks / 4));  // at least one block per wave
+      P.nblk = cdiv(nblocks, nc);
+      P.nc = cdiv(nblocks, P.nblk);
+    };
+    P.spin_ticks = (int)std::min<int64_t>((int64_t)dev.wall_khz * 1000 / 5000, 1 << 30);  // 200 us
+    if (c.mode_op == LORA_OP_SHRINK) {
+      P.mode = kModeShrink;
+      choose_ks();
+      if (P.ks > 1 && tiles > kMaxDepTiles) { P.ks = 1; P.kchunk = round_up(c.K, 64); }
+      P.n_items_a = tiles * P.ks;
+      P.grid = P.n_items_a;
+    } else if (c.mode_op == LORA_OP_EXPAND) {
+      P.mode = kModeExpand;
+      choose_nc();
+      P.n_items_a = tiles * P.nc;
+      P.grid = P.n_items_a;
+    } else {
+      if (tiles >= cus / 2 || tiles > kMaxDepTiles) {
+        P.mode = kModeFusedTile;
+        P.ks = 1;
+        P.kchunk = round_up(c.K, 64);
+        int nc = std::max(1, cus / tiles);
+        nc = std::min(nc, std::max(1, nblocks / 4));
+        P.nblk = cdiv(nblocks, nc);
+        P.nc = cdiv(nblocks, P.nblk);
+        P.n_items_a = tiles * P.nc;
+        P.grid = P.n_items_a;
+      } else {
+        P.mode = kModeFusedDep;
+        choose_ks();
+        choose_nc();
+        P.n_items_a = tiles * P.ks;
+        P.n_items_b = tiles * P.nc;
+        P.grid = P.n_items_a + P.n_items_b;
+      }
+    }
+    if (P.grid <= 0) continue;
+    const hipError_t e = launch_fwd(P, stream);
+    if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return LORA_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need)
+    return fail(LORA_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the %zu needed", ws_bytes, need);
+  if (need > 0 && !ws) return fail(LORA_INVALID_ARGUMENT, "workspace is NULL");
+  if (need > 0 && (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return fail(LORA_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  return LORA_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* lora_status_string(int status) {
+  switch (status) {
+    case LORA_OK: return "ok";
+    case LORA_INVALID_ARGUMENT: return "invalid argument";
+    case LORA_UNSUPPORTED: return "unsupported";
+    case LORA_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case LORA_DEVICE_ERROR: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* lora_last_error(void) { return g_last_error.c_str(); }
+
+int lora_version(void) { return 100; }
+
+int lora_segments_from_ids(const int32_t* ids, int32_t T, int32_t N, int32_t* perm,
+                           int32_t* seg_starts, int32_t* seg_adapter) {
+  g_last_error.clear();
+  if (T < 0 || N < 1) return fail(LORA_INVALID_ARGUMENT, "num_tokens must be >= 0 and num_adapters >= 1");
+  if ((T > 0 && (!ids || !perm)) || !seg_starts || !seg_adapter)
+    return fail(LORA_INVALID_ARGUMENT, "NULL array");
+  // stable counting sort; key N stands for "no adapter" (-1) and sorts last
+  std::vector<int32_t> count((size_t)N + 2, 0);
+  for (int32_t t = 0; t < T; ++t) {
+    const int32_t id = ids[t];
+    if (id < -1 || id >= N) return fail(LORA_INVALID_ARGUMENT, "ids[%d] = %d outside [-1, %d)", t, id, N);
+    count[(size_t)(id < 0 ? N : id) + 1]++;
+  }
+  for (int32_t k = 0; k <= N; ++k) count[(size_t)k + 1] += count[(size_t)k];
+  for (int32_t k = 0; k <= N + 1; ++k) seg_starts[k] = count[(size_t)k];
+  for (int32_t k = 0; k < N; ++k) seg_adapter[k] = k;
+  seg_adapter[N] = -1;
+  for (int32_t t = 0; t < T; ++t) {
+    const int32_t key = ids[t] < 0 ? N : ids[t];
+    perm[count[(size_t)key]++] = t;
+  }
+  return LORA_OK;
+}
+
+int lora_workspace_size(int op, const lora_adapters_t* adapters, const lora_segments_t* segments,
+                        size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(LORA_INVALID_ARGUMENT, "bytes is NULL");
+  if (op < LORA_OP_SHRINK || op > LORA_OP_BACKWARD) return fail(LORA_INVALID_ARGUMENT, "unknown op %d", op);
+  int st = check_adapters(adapters);
+  if (st) return st;
+  if (op == LORA_OP_BACKWARD) {
+    if (!segments) return fail(LORA_INVALID_ARGUMENT, "segments is NULL");
+    if (segments->num_tokens < 0) return fail(LORA_INVALID_ARGUMENT, "num_tokens must be >= 0");
+  }
+  *bytes = ws_layout(op, adapters, segments).total;
+  return LORA_OK;
+}
+
+static int common_checks(const lora_adapters_t* adapters, const lora_segments_t* segments) {
+  int st = check_adapters(adapters);
+  if (st) return st;
+  return check_segments(segments, adapters->num_adapters);
+}
+
+int lora_sgmv_shrink(const void* x, int64_t ldx, const lora_adapters_t* adapters,
+                     const lora_segments_t* segments, float* u, int64_t ldu, void* ws,
+                     size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int st = common_checks(adapters, segments);
+  if (st) return st;
+  const auto segs = active_segments(adapters, segments);
+  if (segs.empty()) return LORA_OK;
+  if ((st = check_rows(x, ldx, adapters->h_in, "x", true))) return st;
+  if ((st = check_u(u, ldu, max_rank_used(segs), "u"))) return st;
+  if (!adapters->A_ptrs) return fail(LORA_INVALID_ARGUMENT, "A_ptrs is NULL");
+  const WsLayout L = ws_layout(LORA_OP_SHRINK, adapters, segments);
+  if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+  FwdCall c{};
+  c.mode_op = LORA_OP_SHRINK;
+  c.X = static_cast<const uint16_t*>(x); c.ldx = ldx;
+  c.U = u; c.ldu = ldu;
+  c.Wtab = adapters->A_ptrs; c.v_round = 1;
+  c.K = adapters->h_in; c.N = adapters->h_out;
+  c.token_rows = segments->token_rows;
+  c.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
+  c.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.counters);
+  c.rmax = max_rank_all(adapters);
+  return run_fwd(c, segs, {}, static_cast<hipStream_t>(stream));
+}
+
+int lora_sgmv_expand(const float* u, int64_t ldu, const lora_adapters_t* adapters,
+                     const lora_segments_t* segments, void* y, int64_t ldy, void* ws,
+                     size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int st = common_checks(adapters, segments);
+  if (st) return st;
+  const auto segs = active_segments(adapters, segments);
+  if (segs.empty()) return LORA_OK;
+  if ((st = check_rows(y, ldy, adapters->h_out, "y", true))) return st;
+  if ((st = check_u(u, ldu, max_rank_used(segs), "u"))) return st;
+  if (!adapters->B_ptrs) return fail(LORA_INVALID_ARGUMENT, "B_ptrs is NULL");
+  (void)ws;
+  (void)ws_bytes;
+  FwdCall c{};
+  c.mode_op = LORA_OP_EXPAND;
+  c.Y = static_cast<uint16_t*>(y); c.ldy = ldy;
+  c.U = const_cast<float*>(u); c.ldu = ldu;
+  c.Vtab = adapters->B_ptrs; c.v_round = 1;
+  c.K = adapters->h_in; c.N = adapters->h_out;
+  c.token_rows = segments->token_rows;
+  c.rmax = max_rank_all(adapters);
+  return run_fwd(c, segs, {}, static_cast<hipStream_t>(stream));
+}
+
+int lora_sgmv_fused(const void* x, int64_t ldx, const lora_adapters_t* adapters,
+                    const lora_segments_t* segments, void* y, int64_t ldy, float* u_save,
+                    int64_t ldu, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int st = common_checks(adapters, segments);
+  if (st) return st;
+  const auto segs = active_segments(adapters, segments);
+  if (segs.empty()) return LORA_OK;
+  if ((st = check_rows(x, ldx, adapters->h_in, "x", true))) return st;
+  if ((st = check_rows(y, ldy, adapters->h_out, "y", true))) return st;
+  if (u_save && (st = check_u(u_save, ldu, max_rank_used(segs), "u_save"))) return st;
+  if (!adapters->A_ptrs || !adapters->B_ptrs) return fail(LORA_INVALID_ARGUMENT, "A_ptrs/B_ptrs is NULL");
+  const WsLayout L = ws_layout(LORA_OP_FUSED, adapters, segments);
+  if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+  FwdCall c{};
+  c.mode_op = LORA_OP_FUSED;
+  c.X = static_cast<const uint16_t*>(x); c.ldx = ldx;
+  c.Y = static_cast<uint16_t*>(y); c.ldy = ldy;
+  c.U = u_save; c.ldu = ldu; c.write_u = u_save != nullptr;
+  c.Wtab = adapters->A_ptrs; c.Vtab = adapters->B_ptrs; c.v_round = 1;
+  c.K = adapters->h_in; c.N = adapters->h_out;
+  c.token_rows = segments->token_rows;
+  c.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
+  c.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.counters);
+  c.rmax = max_rank_all(adapters);
+  return run_fwd(c, segs, {}, static_cast<hipStream_t>(stream));
+}
+
+int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t lddy, const float* u,
+                         int64_t ldu, const lora_adapters_t* adapters,
+                         const lora_segments_t* segments, void* dx, int64_t lddx,
+                         const uint64_t* dA_ptrs, const uint64_t* dB_ptrs, uint32_t flags,
+                         void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int st = common_checks(adapters, segments);
+  if (st) return st;
+  if (flags & ~LORA_GRAD_ACCUMULATE) return fail(LORA_INVALID_ARGUMENT, "unknown flags 0x%x", flags);
+  const bool accumulate = (flags & LORA_GRAD_ACCUMULATE) != 0;
+  const int N = adapters->num_adapters;
+  const auto segs = active_segments(adapters, segments);
+  // adapters whose gradients this call writes
+  std::vector<int> with_tokens(N, 0);
+  for (const auto& s : segs) with_tokens[s.adapter] = 1;
+  bool any_zero_fill = false;
+  if (!accumulate)
+    for (int i = 0; i < N; ++i)
+      if (adapters->ranks[i] > 0 && !with_tokens[i]) any_zero_fill = true;
+  if (segs.empty() && !any_zero_fill) return LORA_OK;
+  if (!dA_ptrs || !dB_ptrs) return fail(LORA_INVALID_ARGUMENT, "dA_ptrs/dB_ptrs is NULL");
+  if (!segs.empty()) {
+    if ((st = check_rows(x, ldx, adapters->h_in, "x", true))) return st;
+    if ((st = check_rows(dy, lddy, adapters->h_out, "dy", true))) return st;
+    if ((st = check_rows(dx, lddx, adapters->h_in, "dx", dx != nullptr))) return st;
+    if (u && (st = check_u(u, ldu, max_rank_used(segs), "u"))) return st;
+    if (!adapters->A_ptrs || !adapters->B_ptrs) return fail(LORA_INVALID_ARGUMENT, "A_ptrs/B_ptrs is NULL");
+  }
+  const WsLayout L = ws_layout(LORA_OP_BACKWARD, adapters, segments);
+  if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+  float* partials = reinterpret_cast<float*>(wsb + L.partials);
+  int32_t* counters = reinterpret_cast<int32_t*>(wsb + L.counters);
+  float* dU = reinterpret_cast<float*>(wsb + L.du);
+  const int rmax = max_rank_all(adapters);
+
+  // u for dB: the caller's, or recomputed into the workspace
+  const float* Uuse = u;
+  int64_t lduse = ldu;
+  if (!segs.empty() && !u) {
+    FwdCall c{};
+    c.mode_op = LORA_OP_SHRINK;
+    c.X = static_cast<const uint16_t*>(x); c.ldx = ldx;
+    c.U = reinterpret_cast<float*>(wsb + L.urec); c.ldu = L.lddu;
+    c.Wtab = adapters->A_ptrs; c.v_round = 1;
+    c.K = adapters->h_in; c.N = adapters->h_out;
+    c.token_rows = segments->token_rows;
+    c.partials = partials; c.counters = counters; c.rmax = rmax;
+    if ((st = run_fwd(c, segs, {}, strm))) return st;
+    Uuse = c.U;
+    lduse = L.lddu;
+  }
+
+  // adapter groups of at most kMaxSlots, in order of first appearance
+  std::vector<int> order;
+  {
+    std::vector<int> seen(N, 0);
+    for (const auto& s : segs)
+      if (!seen[s.adapter]) { seen[s.adapter] = 1; order.push_back(s.adapter); }
+  }
+  std::vector<int> slot_of(N, 0);
+  for (size_t g0 = 0; g0 < order.size(); g0 += kMaxSlots) {
+    const int ng = (int)std::min<size_t>(kMaxSlots, order.size() - g0);
+    std::vector<int> in_group(N, 0);
+    TransposePlan T;
+    std::memset(&T, 0, sizeof(T));
+    T.A_tab = adapters->A_ptrs; T.B_tab = adapters->B_ptrs;
+    T.Bt = reinterpret_cast<uint16_t*>(wsb + L.bt);
+    T.At = reinterpret_cast<uint16_t*>(wsb + L.at);
+    T.bt_slot_elems = L.bt_slot; T.at_slot_elems = L.at_slot;
+    T.h_in = adapters->h_in; T.h_out = adapters->h_out;
+    T.n_slots = ng;
+    int grmax = 0;
+    for (int k = 0; k < ng; ++k) {
+      const int a = order[g0 + k];
+      in_group[a] = 1;
+      slot_of[a] = k;
+      T.slot_adapter[k] = a;
+      T.slot_rank[k] = adapters->ranks[a];
+      grmax = std::max(grmax, adapters->ranks[a]);
+    }
+    T.tb_cols = cdiv(grmax, 64);
+    T.tiles_b = cdiv(adapters->h_out, 64) * T.tb_cols;
+    T.ta_cols = cdiv(adapters->h_in, 64);
+    T.tiles_a = cdiv(round_up(grmax, 8), 64) * T.ta_cols;
+    hipError_t e = launch_transpose(T, strm);
+    if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "transpose launch failed: %s", hipGetErrorString(e));
+
+    std::vector<ActiveSeg> gsegs;
+    for (const auto& s : segs)
+      if (in_group[s.adapter]) gsegs.push_back(s);
+    // du = s B^T dy (kept in the workspace) and dx += A^T du
+    FwdCall c{};
+    c.mode_op = dx ? LORA_OP_FUSED : LORA_OP_SHRINK;
+    c.X = static_cast<const uint16_t*>(dy); c.ldx = lddy;
+    c.Y = static_cast<uint16_t*>(dx); c.ldy = lddx;
+    c.U = dU; c.ldu = L.lddu; c.write_u = true;
+    c.Wslots = T.Bt; c.Vslots = T.At;
+    c.w_slot_elems = L.bt_slot; c.v_slot_elems = L.at_slot;
+    c.v_round = 8; c.scale_in_shrink = 1;
+    c.K = adapters->h_out; c.N = adapters->h_in;
+    c.token_rows = segments->token_rows;
+    c.partials = partials; c.counters = counters; c.rmax = rmax;
+    if ((st = run_fwd(c, gsegs, slot_of, strm))) return st;
+  }
+
+  // weight gradients: one job per adapter (split if it has too many segments)
+  struct Job { int adapter, rank, accum; float scale; std::vector<std::pair<int, int>> segs; };
+  std::vector<Job> jobs;
+  {
+    std::vector<std::vector<std::pair<int, int>>> per(N);
+    for (const auto& s : segs) per[s.adapter].push_back({s.tok0, s.ntok});
+    for (int a = 0; a < N; ++a) {
+      if (adapters->ranks[a] == 0) continue;
+      if (per[a].empty()) {
+        if (!accumulate) jobs.push_back(Job{a, adapters->ranks[a], 0, adapters->scales[a], {}});
+        continue;
+      }
+      for (size_t k = 0; k < per[a].size(); k += kMaxJobSeg) {
+        Job j{a, adapters->ranks[a], (accumulate || k > 0) ? 1 : 0, adapters->scales[a], {}};
+        for (size_t q = k; q < std::min(per[a].size(), k + kMaxJobSeg); ++q) j.segs.push_back(per[a][q]);
+        jobs.push_back(std::move(j));
+      }
+    }
+  }
+  // heavy jobs first; continuation jobs of one adapter must land in later launches
+  std::vector<size_t> idx(jobs.size());
+  for (size_t i = 0; i < idx.size(); ++i) idx[i] = i;
+  auto tokens_of = [&](const Job& j) {
+    int64_t n = 0;
+    for (auto& p : j.segs) n += p.second;
+    return n;
+  };
+  std::stable_sort(idx.begin(), idx.end(), [&](size_t p, size_t q) {
+    const Job &a = jobs[p], &b = jobs[q];
+    if (a.accum != b.accum && a.adapter == b.adapter) return a.accum < b.accum;
+    return tokens_of(a) * (int64_t)(a.rank + 16) > tokens_of(b) * (int64_t)(b.rank + 16);
+  });
+  std::vector<int> done(jobs.size(), 0);
+  size_t remaining = jobs.size();
+  while (remaining > 0) {
+    WgradPlan W;
+    std::memset(&W, 0, sizeof(W));
+    W.x = static_cast<const uint16_t*>(x); W.ldx = ldx;
+    W.dy = static_cast<const uint16_t*>(dy); W.lddy = lddy;
+    W.U = Uuse; W.ldu = lduse; W.dU = dU; W.lddu = L.lddu;
+    W.dA_tab = dA_ptrs; W.dB_tab = dB_ptrs; W.token_rows = segments->token_rows;
+    W.h_in = adapters->h_in; W.h_out = adapters->h_out;
+    int nj = 0, nseg = 0, grid = 0;
+    std::vector<int> adapter_in_launch(N, 0);
+    for (size_t ii = 0; ii < idx.size(); ++ii) {
+      const size_t j = idx[ii];
+      if (done[j]) continue;
+      const Job& J = jobs[j];
+      if (adapter_in_launch[J.adapter]) continue;  // keeps an adapter's parts ordered
+      if (nj >= kMaxJobs || nseg + (int)J.segs.size() > kMaxJobSeg) break;
+      // a continuation part may only run after its first part
+      bool earlier_pending = false;
+      for (size_t q = 0; q < jobs.size(); ++q)
+        if (!done[q] && q != j && jobs[q].adapter == J.adapter && jobs[q].accum < J.accum) earlier_pending = true;
+      if (earlier_pending) continue;
+      W.job_adapter[nj] = J.adapter;
+      W.job_seg0[nj] = nseg;
+      W.job_nseg[nj] = (int)J.segs.size();
+      W.job_accum[nj] = J.accum;
+      W.job_scale[nj] = J.scale;
+      W.job_rank[nj] = J.rank;
+      for (auto& p : J.segs) { W.seg_tok0[nseg] = p.first; W.seg_ntok[nseg] = p.second; ++nseg; }
+      grid += wgrad_items_for_rank(J.rank, adapters->h_in, adapters->h_out);
+      adapter_in_launch[J.adapter] = 1;
+      done[j] = 1;
+      --remaining;
+      ++nj;
+    }
+    if (nj == 0) return fail(LORA_DEVICE_ERROR, "internal planner error (no weight-gradient job placed)");
+    W.n_jobs = nj;
+    const hipError_t e = launch_wgrad(W, grid, strm);
+    if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "weight-gradient launch failed: %s", hipGetErrorString(e));
+  }
+  return LORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// lora_device.h -- gfx950 device helpers: 16-byte global accesses, bf16
+// conversions and the bf16 MFMA wrappers used by the LoRA kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// bf16 bit pattern -> float (exact).
+__device__ __forceinline__ float bf2f(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)));
+}
+
+// Unpack 8 bf16 (one 16-byte chunk) to floats.
+__device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = __builtin_bit_cast(float, v[q] << 16);
+    f[2 * q + 1] = __builtin_bit_cast(float, v[q] & 0xffff0000u);
+  }
+}
+// Pack 8 floats to 8 bf16 (round to nearest even).
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = f2bf(f[2 * q]) | (f2bf(f[2 * q + 1]) << 16);
+  return v;
+}
+
+// Split 8 fp32 values into bf16 hi + lo parts (hi = rne(f), lo = rne(f - hi)),
+// so an MFMA pair on (hi, lo) carries ~16 mantissa bits of the fp32 operand.
+__device__ __forceinline__ void split8(const float (&f)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    __bf16 h = static_cast<__bf16>(f[e]);
+    hi[e] = h;
+    lo[e] = static_cast<__bf16>(f[e] - static_cast<float>(h));
+  }
+}
+
+// D = A(32x16) * B(16x32) + C. Lane l supplies A[l%32][8(l/32)+e] and
+// B[8(l/32)+e][l%32] (e = 0..7) and holds D[8(i/4)+4(l/32)+(i%4)][l%32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// D = A(16x32) * B(32x16) + C. Lane l supplies A[l%16][8(l/16)+e] and
+// B[8(l/16)+e][l%16] and holds D[4(l/16)+i][l%16] (i = 0..3).
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero_acc16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Expand-output permutation. Row m of a 32x32 MFMA output block is written
+// to column colmap(m) of the block, so that lane l's 16 results (rows
+// 8(i/4)+4h+(i%4), h = l/32) land on columns 16(i/8) + 8h + (i%8): two runs
+// of 8 contiguous bf16, i.e. two 16-byte accesses per lane.
+__device__ __forceinline__ int colmap(int m) {
+  return (m & 16) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
+}
+
+}  // namespace lora

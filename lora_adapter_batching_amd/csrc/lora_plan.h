@@ -1,0 +1,123 @@
+// lora_plan.h -- launch plans shared by the host planner and the gfx950
+// kernels of the multi-adapter LoRA library. Internal; not part of the ABI.
+//
+// A plan travels by value as the kernel argument, so a call needs no
+// host-to-device copy of metadata: segment tables live in the kernel-argument
+// segment and are read with scalar loads.
+#pragma once
+#include <stdint.h>
+
+namespace lora {
+
+constexpr int kThreads = 256;  // 4 wave64 per workgroup
+constexpr int kTileM = 32;     // tokens per tile (the N side of a 32x32 MFMA)
+constexpr int kMaxSeg = 128;   // segments per forward launch
+constexpr int kMaxJobs = 64;   // adapter jobs per weight-gradient launch
+constexpr int kMaxJobSeg = 128;
+
+// Forward-style launch modes (also used for the backward du/dx pass).
+enum FwdMode : int32_t {
+  kModeShrink = 0,     // items: (tile, k-chunk). ks == 1 writes U; ks > 1: last arriver sums
+  kModeExpand = 1,     // items: (tile, n-chunk). U is read from memory
+  kModeFusedTile = 2,  // items: (tile, n-chunk). Each computes the tile's full shrink on chip
+  kModeFusedDep = 3,   // items [0, a): (tile, k-chunk) shrink parts; [a, a+b): (tile, n-chunk)
+                       // expands that wait on the tile's counter, then sum the parts
+};
+
+// Counter layout inside the workspace (int32 words).
+constexpr int kCtrDone = 0;      // workgroups finished (kModeFusedDep)
+constexpr int kCtrTiles = 64;    // per-tile arrival counters start here
+
+struct FwdPlan {
+  const uint16_t* X;  // shrink input rows, bf16 (x forward, dy backward)
+  int64_t ldx;
+  uint16_t* Y;  // expand in/out rows, bf16 (y forward, dx backward)
+  int64_t ldy;
+  float* U;  // fp32 [T, ldu] sorted positions: input (expand) / output (shrink, save)
+  int64_t ldu;
+  const uint64_t* Wtab;  // per adapter: shrink weight [rank, K] row-major (ld = K); or null
+  const uint64_t* Vtab;  // per adapter: expand weight [N, ldv] row-major; or null
+  const uint16_t* Wslots;  // used when Wtab is null: slot s at Wslots + s * w_slot_elems
+  const uint16_t* Vslots;
+  int64_t w_slot_elems;
+  int64_t v_slot_elems;
+  const int32_t* token_rows;  // row of X/Y for each sorted position, or null
+  float* partials;            // split-K partial sums [tile][ks][32][rpad]
+  int32_t* counters;          // workspace counters (zero on entry and on exit)
+  int32_t K;                  // shrink reduction length
+  int32_t N;                  // expand output width
+  int32_t v_round;            // expand weight row stride = round_up(rank, v_round)
+  int32_t mode;
+  int32_t scale_in_shrink;  // 1: u = s * (W x) and expand unscaled; 0: y += s * V u
+  int32_t write_u;          // kModeFusedTile/kModeFusedDep: also store U
+  int32_t n_seg;
+  int32_t n_tiles;
+  int32_t ks;        // k-chunks per tile
+  int32_t kchunk;    // elements per k-chunk (multiple of 8)
+  int32_t nc;        // n-chunks per tile
+  int32_t nblk;      // 32-column blocks per n-chunk
+  int32_t rpad;      // row length of a partial tile (multiple of 32)
+  int32_t n_items_a;
+  int32_t n_items_b;
+  int32_t xcd_remap;    // 1: map consecutive items of phase A to the same XCD
+  int32_t grid;         // launched workgroups
+  int32_t spin_ticks;   // wall-clock ticks an expand waits before computing the shrink itself
+  int32_t seg_tok0[kMaxSeg];
+  int32_t seg_ntok[kMaxSeg];
+  int32_t seg_tile0[kMaxSeg];
+  int32_t seg_adapter[kMaxSeg];
+  float seg_scale[kMaxSeg];
+  uint8_t seg_rank[kMaxSeg];
+  uint8_t seg_slot[kMaxSeg];
+};
+
+// Weight-gradient launch: items are (job, kind, column chunk); a job is one
+// adapter (or part of its segments) whose token reduction the item owns.
+struct WgradPlan {
+  const uint16_t* x;  // bf16 rows (dA operand)
+  int64_t ldx;
+  const uint16_t* dy;  // bf16 rows (dB operand)
+  int64_t lddy;
+  const float* U;  // fp32 [T, ldu] sorted positions (dB operand)
+  int64_t ldu;
+  const float* dU;  // fp32 [T, lddu] sorted positions (dA operand)
+  int64_t lddu;
+  const uint64_t* dA_tab;  // per adapter fp32 [r, h_in]
+  const uint64_t* dB_tab;  // per adapter fp32 [h_out, r]
+  const int32_t* token_rows;
+  int32_t h_in;
+  int32_t h_out;
+  int32_t n_jobs;
+  int32_t cw;      // columns per item (multiple of 128)
+  int32_t nb_db;   // items per job for dB
+  int32_t nb_da;   // items per job for dA
+  int32_t job_adapter[kMaxJobs];
+  int32_t job_seg0[kMaxJobs];
+  int32_t job_nseg[kMaxJobs];
+  int32_t job_accum[kMaxJobs];
+  float job_scale[kMaxJobs];
+  int32_t job_rank[kMaxJobs];
+  int32_t seg_tok0[kMaxJobSeg];
+  int32_t seg_ntok[kMaxJobSeg];
+};
+
+// Transposed copies of the adapter weights for the backward du/dx pass.
+struct TransposePlan {
+  const uint64_t* A_tab;  // per adapter bf16 [r, h_in]
+  const uint64_t* B_tab;  // per adapter bf16 [h_out, r]
+  uint16_t* Bt;           // slot s: [r, h_out] at Bt + s * bt_slot_elems
+  uint16_t* At;           // slot s: [h_in, round_up(r, 8)] at At + s * at_slot_elems
+  int64_t bt_slot_elems;
+  int64_t at_slot_elems;
+  int32_t h_in;
+  int32_t h_out;
+  int32_t n_slots;
+  int32_t tiles_b;  // 64x64 tiles per slot for B: ceil(h_out/64) * tb_cols
+  int32_t tiles_a;  // 64x64 tiles per slot for A: ceil(r8_max/64) * ta_cols
+  int32_t tb_cols;  // ceil(r_max/64)
+  int32_t ta_cols;  // ceil(h_in/64)
+  int32_t slot_adapter[kMaxJobs];
+  int32_t slot_rank[kMaxJobs];
+};
+
+}  // namespace lora

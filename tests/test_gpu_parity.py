@@ -1,0 +1,337 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
+the same seeded inputs. Element-by-element at oracle-friendly sizes, sampled
+rows (or whole adapters) at the full workload sizes.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from helpers import BF16_TOL, FP32_TOL, GpuProblem, oracle_batch, rel_err, to_f64
+from workloads import make_config, make_custom
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import lora_adapter_batching_amd as L
+    L.load()
+    yield
+
+
+def _L():
+    import lora_adapter_batching_amd as L
+    return L
+
+
+def _run_fused(gp, u=True, ws=None):
+    L = _L()
+    import torch
+    y = gp.new_y()
+    uu = gp.new_u() if u else None
+    if ws is None:
+        ws = L.new_workspace(L.OP_FUSED, gp.adapters, gp.segments)
+    L.sgmv_fused(gp.x, gp.adapters, gp.segments, y, uu, ws)
+    torch.cuda.synchronize()
+    return y, uu
+
+
+def _check_forward(gp, ob, y, u=None, rows=None):
+    """Compare y (and u) at sorted positions `rows` (all if None)."""
+    if rows is None:
+        y_ref, u_ref = ob.forward()
+        rows = np.arange(gp.prob.T)
+    else:
+        y_ref, u_ref = ob.forward_tokens(rows)
+    yg = gp.sorted_rows(y)[rows]
+    err = rel_err(yg, y_ref)
+    assert err <= BF16_TOL, f"y rel err {err:.3e}"
+    if u is not None:
+        ug = to_f64(u)[rows]
+        a = ob.token_adapter()[rows]
+        for i in np.unique(a):
+            if i < 0 or gp.prob.ranks[i] == 0:
+                continue
+            m = a == i
+            r = int(gp.prob.ranks[i])
+            e = rel_err(ug[m, :r], u_ref[m, :r])
+            assert e <= FP32_TOL, f"u rel err {e:.3e} (adapter {i})"
+    return err
+
+
+# ---------------------------------------------------------------------------
+# Tiny workload (16 decode tokens, 4 adapters of rank 8)
+# ---------------------------------------------------------------------------
+def test_tiny_fused_shrink_expand():
+    L = _L()
+    import torch
+    prob = make_config("tiny")
+    gp = GpuProblem(prob)
+    ob = oracle_batch(prob)
+    assert np.array_equal(gp.perm, ob.perm)
+    _say("tiny fused")
+    y, u = _run_fused(gp)
+    _check_forward(gp, ob, y, u)
+    _say("tiny shrink + expand")
+    u2 = gp.new_u()
+    ws = L.new_workspace(L.OP_SHRINK, gp.adapters, gp.segments)
+    L.sgmv_shrink(gp.x, gp.adapters, gp.segments, u2, ws)
+    y2 = gp.new_y()
+    L.sgmv_expand(u2, gp.adapters, gp.segments, y2)
+    torch.cuda.synchronize()
+    _check_forward(gp, ob, y2, u2)
+
+
+# ---------------------------------------------------------------------------
+# Mixed ranks, ragged shapes, -1 ids, empty segments, token_rows
+# ---------------------------------------------------------------------------
+def _mixed_problem(seed, T=300, h_in=264, h_out=200, y0=True):
+    rng = np.random.default_rng(100 + seed)
+    ranks = [8, 24, 12, 0, 128, 64, 16, 40, 1]
+    ids = rng.integers(-1, len(ranks), size=T).astype(np.int32)
+    ids[ids == 7] = 5  # adapter 7 gets no tokens (empty segment)
+    return make_custom(seed, h_in, h_out, ranks, scales="random", ids=ids, y0=y0)
+
+
+@pytest.mark.parametrize("use_token_rows", [False, True])
+def test_mixed_ranks_ragged(use_token_rows):
+    L = _L()
+    import torch
+    prob = _mixed_problem(1)
+    gp = GpuProblem(prob, use_token_rows=use_token_rows)
+    ob = oracle_batch(prob)
+    assert np.array_equal(gp.perm, ob.perm)
+    _say(f"mixed fused token_rows={use_token_rows}")
+    y, u = _run_fused(gp)
+    _check_forward(gp, ob, y, u)
+    _say(f"mixed shrink/expand token_rows={use_token_rows}")
+    u2 = gp.new_u()
+    L.sgmv_shrink(gp.x, gp.adapters, gp.segments, u2, L.new_workspace(L.OP_SHRINK, gp.adapters, gp.segments))
+    y2 = gp.new_y()
+    L.sgmv_expand(u2, gp.adapters, gp.segments, y2)
+    torch.cuda.synchronize()
+    _check_forward(gp, ob, y2, u2)
+    # rows of tokens without a LoRA contribution are untouched (bitwise)
+    a = ob.token_adapter()
+    skip = np.array([i < 0 or prob.ranks[i] == 0 for i in a])
+    y0 = gp.sorted_rows(gp.y_init)
+    assert np.array_equal(gp.sorted_rows(y)[skip], y0[skip])
+
+
+def test_fused_tile_mode_many_tokens():
+    """Enough tiles that the planner picks the on-chip (fused-tile) mode."""
+    prob = make_custom(7, 520, 392, [16, 32, 8, 72], scales="random",
+                       seg_lens=[1500, 7, 1333, 33, 800, 700, 1], seg_adapter=[0, 1, 2, 3, 1, 0, 3])
+    gp = GpuProblem(prob)
+    ob = oracle_batch(prob)
+    _say("fused-tile mode, 4374 tokens")
+    y, u = _run_fused(gp)
+    _check_forward(gp, ob, y, u)
+
+
+def test_many_segments_split_launches():
+    """More active segments than one launch plan holds."""
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 9, size=300).astype(np.int32)
+    ad = rng.integers(-1, 6, size=300).astype(np.int32)
+    prob = make_custom(8, 128, 96, [8, 16, 32, 4, 0, 48], scales="random", seg_lens=lens, seg_adapter=ad)
+    gp = GpuProblem(prob)
+    ob = oracle_batch(prob)
+    _say("300 segments fused")
+    y, u = _run_fused(gp)
+    _check_forward(gp, ob, y, u)
+
+
+def test_determinism_and_workspace_reuse():
+    L = _L()
+    import torch
+    prob = _mixed_problem(2, y0=False)
+    gp = GpuProblem(prob)
+    ws = L.new_workspace(L.OP_FUSED, gp.adapters, gp.segments)
+    _say("fused x3 same workspace")
+    outs = []
+    for _ in range(3):
+        y, _ = _run_fused(gp, ws=ws)
+        outs.append(to_f64(y))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    assert int(ws[:4096].to(torch.int32).abs().sum().item()) == 0, "counters not returned to zero"
+
+
+def test_noop_cases():
+    L = _L()
+    import torch
+    # rank-0 and zero-B adapters leave y unchanged
+    prob = make_custom(9, 64, 48, [0, 8], ids=np.array([0, 1, 1, 0, 1], np.int32), y0=True)
+    prob.B[1][:] = 0
+    gp = GpuProblem(prob)
+    _say("noop fused")
+    y, _ = _run_fused(gp)
+    assert np.array_equal(to_f64(y), to_f64(gp.y_init))
+    # empty batch
+    seg = L.Segments(np.array([0], np.int32), np.zeros(0, np.int32))
+    y0 = torch.zeros((0, 48), dtype=torch.bfloat16, device="cuda")
+    L.sgmv_fused(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"), gp.adapters, seg, y0,
+                 None, L.new_workspace(L.OP_FUSED, gp.adapters, seg))
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads
+# ---------------------------------------------------------------------------
+def test_decode_qwen3_4b_projections_full():
+    projs = make_config("decode")
+    for name, prob in projs.items():
+        gp = GpuProblem(prob)
+        ob = oracle_batch(prob)
+        assert np.array_equal(gp.perm, ob.perm)
+        _say(f"decode {name} {prob.h_in}->{prob.h_out}")
+        y, u = _run_fused(gp)
+        _check_forward(gp, ob, y, u)
+
+
+def _sample_rows(gp, n=96, seed=0):
+    rng = np.random.default_rng(seed)
+    st = gp.seg_starts
+    edges = set()
+    for g in range(len(st) - 1):
+        if st[g + 1] > st[g]:
+            edges.update([int(st[g]), int(st[g + 1]) - 1])
+    rows = set(int(r) for r in rng.choice(gp.prob.T, size=min(n, gp.prob.T), replace=False))
+    rows.update(list(edges)[:64])
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def test_prefill_llama3_8b_sampled():
+    prob = make_config("prefill")
+    gp = GpuProblem(prob)
+    ob = oracle_batch(prob)
+    _say("prefill 8192 tok 4096->4096")
+    y, u = _run_fused(gp)
+    _check_forward(gp, ob, y, u, rows=_sample_rows(gp))
+
+
+def test_hetero_mlp_up_sampled():
+    prob = make_config("hetero")
+    gp = GpuProblem(prob)
+    ob = oracle_batch(prob)
+    assert np.array_equal(gp.perm, ob.perm)
+    _say("hetero 4096 tok 4096->14336")
+    y, u = _run_fused(gp)
+    _check_forward(gp, ob, y, u, rows=_sample_rows(gp))
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+def _grad_tables(prob):
+    import torch
+    dA = [torch.full((int(r), prob.h_in), float("nan"), dtype=torch.float32, device="cuda")
+          for r in prob.ranks]
+    dB = [torch.full((prob.h_out, int(r)), float("nan"), dtype=torch.float32, device="cuda")
+          for r in prob.ranks]
+    pa = torch.tensor([t.data_ptr() if t.numel() else 0 for t in dA], dtype=torch.int64, device="cuda")
+    pb = torch.tensor([t.data_ptr() if t.numel() else 0 for t in dB], dtype=torch.int64, device="cuda")
+    return dA, dB, pa, pb
+
+
+def _run_backward(gp, u=None, with_dx=True, flags=0, dA=None, dB=None):
+    L = _L()
+    import torch
+    prob = gp.prob
+    if dA is None:
+        dA, dB, pa, pb = _grad_tables(prob)
+    else:
+        pa = torch.tensor([t.data_ptr() if t.numel() else 0 for t in dA], dtype=torch.int64, device="cuda")
+        pb = torch.tensor([t.data_ptr() if t.numel() else 0 for t in dB], dtype=torch.int64, device="cuda")
+    dx = torch.zeros((prob.T, prob.h_in), dtype=torch.bfloat16, device="cuda") if with_dx else None
+    ws = L.new_workspace(L.OP_BACKWARD, gp.adapters, gp.segments)
+    L.packed_backward(gp.x, gp.dy, u, gp.adapters, gp.segments, dx, pa, pb, flags, ws)
+    torch.cuda.synchronize()
+    return dx, dA, dB
+
+
+def _check_backward(gp, ob, dx, dA, dB, adapters=None, dA0=None, dB0=None):
+    prob = gp.prob
+    if adapters is None:
+        du_ref, dx_ref, dA_ref, dB_ref = ob.backward()
+        rows = np.arange(prob.T)
+        check = [i for i in range(prob.N) if prob.ranks[i] > 0]
+    else:
+        rows, du_ref, dx_ref, dA_ref, dB_ref = ob.backward_adapters(adapters)
+        check = list(adapters)
+    if dx is not None:
+        e = rel_err(gp.sorted_rows(dx)[rows], dx_ref)
+        assert e <= BF16_TOL, f"dx rel err {e:.3e}"
+    for i in check:
+        ga, gb = to_f64(dA[i]), to_f64(dB[i])
+        ra = dA_ref[i] + (dA0[i] if dA0 is not None else 0.0)
+        rb = dB_ref[i] + (dB0[i] if dB0 is not None else 0.0)
+        ea, eb = rel_err(ga, ra), rel_err(gb, rb)
+        assert ea <= FP32_TOL, f"dA[{i}] rel err {ea:.3e}"
+        assert eb <= FP32_TOL, f"dB[{i}] rel err {eb:.3e}"
+
+
+@pytest.mark.parametrize("mode", ["u_given", "u_recompute", "no_dx", "token_rows"])
+def test_backward_mixed(mode):
+    import torch
+    rng = np.random.default_rng(3)
+    ranks = [8, 24, 12, 0, 64, 16, 128, 40]
+    T = 260
+    ids = rng.integers(-1, len(ranks), size=T).astype(np.int32)
+    ids[ids == 7] = 2  # adapter 7 has no tokens: its gradients must be zero
+    prob = make_custom(11, 136, 200, ranks, scales="random", ids=ids, with_dy=True)
+    gp = GpuProblem(prob, use_token_rows=(mode == "token_rows"))
+    ob = oracle_batch(prob)
+    u = None
+    if mode != "u_recompute":
+        _say(f"backward {mode}: forward for u")
+        _, u = _run_fused(gp)
+    _say(f"backward {mode}")
+    dx, dA, dB = _run_backward(gp, u=u, with_dx=(mode != "no_dx"))
+    _check_backward(gp, ob, dx, dA, dB)
+    assert float(dA[7].abs().max()) == 0.0 and float(dB[7].abs().max()) == 0.0
+
+
+def test_backward_accumulate():
+    import torch
+    rng = np.random.default_rng(4)
+    ranks = [16, 32, 8]
+    ids = rng.integers(0, 2, size=90).astype(np.int32)  # adapter 2 without tokens
+    prob = make_custom(12, 96, 72, ranks, scales="random", ids=ids, with_dy=True)
+    gp = GpuProblem(prob)
+    ob = oracle_batch(prob)
+    dA0 = [np.random.default_rng(i).standard_normal((r, prob.h_in)) for i, r in enumerate(ranks)]
+    dB0 = [np.random.default_rng(9 + i).standard_normal((prob.h_out, r)) for i, r in enumerate(ranks)]
+    dA = [torch.tensor(a, dtype=torch.float32, device="cuda") for a in dA0]
+    dB = [torch.tensor(b, dtype=torch.float32, device="cuda") for b in dB0]
+    dA0 = [to_f64(t) for t in dA]
+    dB0 = [to_f64(t) for t in dB]
+    _say("backward accumulate")
+    L = _L()
+    dx, dA, dB = _run_backward(gp, u=None, flags=L.GRAD_ACCUMULATE, dA=dA, dB=dB)
+    _check_backward(gp, ob, dx, dA, dB, dA0=dA0, dB0=dB0)
+    assert np.array_equal(to_f64(dA[2]), dA0[2]) and np.array_equal(to_f64(dB[2]), dB0[2])
+
+
+def test_train_qwen2p5_7b_full_size():
+    """Packed training workload: forward on sampled rows, backward with the
+    complete token reductions of four adapters (smallest and largest ranks)."""
+    prob = make_config("train")
+    gp = GpuProblem(prob)
+    ob = oracle_batch(prob)
+    _say("train forward 65536 tok 3584->3584")
+    y, u = _run_fused(gp)
+    _check_forward(gp, ob, y, u, rows=_sample_rows(gp, n=64))
+    _say("train backward")
+    dx, dA, dB = _run_backward(gp, u=u)
+    ranks = prob.ranks
+    pick = [int(np.argmin(ranks)), int(np.argmax(ranks)), 5, 17]
+    _check_backward(gp, ob, dx, dA, dB, adapters=sorted(set(pick)))

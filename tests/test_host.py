@@ -1,0 +1,162 @@
+"""Host-side checks that need no GPU: the C ABI exports, token bookkeeping
+(bit-exact), host validation of every error path, and workspace sizing."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import lora_adapter_batching_amd as L
+from lora_adapter_batching_amd import binding as B
+from oracle import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "lora_sgmv.h")).read()
+    declared = set(re.findall(r"^\s*(?:int|const char\*)\s+(lora_\w+)\s*\(", hdr, flags=re.M))
+    assert {"lora_sgmv_shrink", "lora_sgmv_expand", "lora_sgmv_fused",
+            "lora_packed_backward", "lora_segments_from_ids", "lora_workspace_size"} <= declared
+    lib = L.load()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared <= set(B.EXPORTS) | {"lora_version"}
+    assert L.version() >= 100
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_segments_from_ids_bit_exact(seed):
+    rng = np.random.default_rng(seed)
+    N = int(rng.integers(1, 70))
+    T = int(rng.integers(0, 5000))
+    ids = rng.integers(-1, N, size=T).astype(np.int32)
+    if seed % 3 == 0:
+        ids[ids == N // 2] = 0  # force an empty segment
+    perm, st, ad = L.segments_from_ids(ids, N)
+    operm, ost, oad = oracle.segments_from_ids(ids, N)
+    assert np.array_equal(perm, operm)
+    assert np.array_equal(st, ost)
+    assert np.array_equal(ad, oad)
+    key = np.where(ids < 0, N, ids)
+    assert np.array_equal(perm, np.argsort(key, kind="stable"))
+
+
+def test_segments_from_ids_rejects_bad_ids():
+    for bad in ([0, 5], [-2], [3, 0, 4]):
+        with pytest.raises(B.LoraError) as e:
+            L.segments_from_ids(np.array(bad, np.int32), 4)
+        assert e.value.status == B.LORA_INVALID_ARGUMENT
+    with pytest.raises(B.LoraError):
+        L.segments_from_ids(np.array([0], np.int32), 0)
+
+
+# ---------------------------------------------------------------------------
+# Validation (host mirrors only; the calls below never reach the GPU)
+# ---------------------------------------------------------------------------
+FAKE = 1 << 20  # a 16-byte aligned non-null "device" address, never dereferenced
+
+
+def _adapters(ranks=(8, 16), scales=None, h_in=64, h_out=32, A=FAKE, Bp=FAKE):
+    ranks = np.ascontiguousarray(ranks, np.int32)
+    scales = np.ascontiguousarray(scales if scales is not None else [1.0] * len(ranks), np.float32)
+    c = B.CAdapters(len(ranks), h_in, h_out, A, Bp, ranks.ctypes.data, scales.ctypes.data)
+    return c, (ranks, scales)
+
+
+def _segments(starts, adapter, T=None):
+    starts = np.ascontiguousarray(starts, np.int32)
+    adapter = np.ascontiguousarray(adapter, np.int32)
+    T = int(starts[-1]) if T is None else T
+    c = B.CSegments(T, len(adapter), starts.ctypes.data, adapter.ctypes.data if len(adapter) else 0, 0)
+    return c, (starts, adapter)
+
+
+def _fused(ad, sg, x=FAKE, ldx=64, y=FAKE, ldy=32, u=0, ldu=0, ws=FAKE, wsb=1 << 30):
+    lib = L.load()
+    return lib.lora_sgmv_fused(x, ldx, ctypes.byref(ad), ctypes.byref(sg), y, ldy, u, ldu, ws, wsb, 0)
+
+
+def test_validation_error_codes():
+    lib = L.load()
+    ad, keep_a = _adapters()
+    sg, keep_s = _segments([0, 3, 5], [0, 1])
+    cases = []
+    # segment metadata (the tuples keep the host arrays alive)
+    cases.append((_segments([1, 3, 5], [0, 1]), "seg_starts[0]"))
+    cases.append((_segments([0, 4, 3], [0, 1], T=3), "decreases"))
+    cases.append((_segments([0, 3, 5], [0, 2]), "outside"))
+    cases.append((_segments([0, 3, 5], [-2, 0]), "outside"))
+    cases.append((_segments([0, 3, 5], [0, 1], T=6), "differs"))
+    for (seg, _keep), msg in cases:
+        st = _fused(ad, seg)
+        assert st == B.LORA_INVALID_ARGUMENT, msg
+        assert msg in lib.lora_last_error().decode()
+    # adapters
+    a_bad, k1 = _adapters(ranks=(8, 129))
+    assert _fused(a_bad, sg) == B.LORA_UNSUPPORTED
+    a_bad, k2 = _adapters(ranks=(8, -1))
+    assert _fused(a_bad, sg) == B.LORA_INVALID_ARGUMENT
+    a_bad, k3 = _adapters(scales=[1.0, float("nan")])
+    assert _fused(a_bad, sg) == B.LORA_INVALID_ARGUMENT
+    a_bad, k4 = _adapters(h_in=60)
+    assert _fused(a_bad, sg) == B.LORA_INVALID_ARGUMENT
+    a_bad, k5 = _adapters(A=0)
+    assert _fused(a_bad, sg) == B.LORA_INVALID_ARGUMENT
+    # rows, strides, alignment
+    assert _fused(ad, sg, x=0) == B.LORA_INVALID_ARGUMENT
+    assert _fused(ad, sg, x=FAKE + 2) == B.LORA_INVALID_ARGUMENT
+    assert _fused(ad, sg, ldx=60) == B.LORA_INVALID_ARGUMENT
+    assert _fused(ad, sg, ldx=68) == B.LORA_INVALID_ARGUMENT
+    assert _fused(ad, sg, ldy=16) == B.LORA_INVALID_ARGUMENT
+    assert _fused(ad, sg, u=FAKE, ldu=8) == B.LORA_INVALID_ARGUMENT  # below rank 16
+    assert _fused(ad, sg, u=FAKE + 2, ldu=16) == B.LORA_INVALID_ARGUMENT
+    # workspace
+    need = ctypes.c_size_t(0)
+    assert lib.lora_workspace_size(B.OP_FUSED, ctypes.byref(ad), ctypes.byref(sg), ctypes.byref(need)) == 0
+    assert need.value > 0
+    assert _fused(ad, sg, wsb=need.value - 1) == B.LORA_WORKSPACE_TOO_SMALL
+    assert _fused(ad, sg, ws=0) == B.LORA_INVALID_ARGUMENT
+    assert _fused(ad, sg, ws=FAKE + 16) == B.LORA_INVALID_ARGUMENT
+    # nothing to do: every segment skipped -> OK without touching the GPU
+    sg_skip, k6 = _segments([0, 3, 5], [-1, -1])
+    assert _fused(ad, sg_skip, x=0, y=0) == B.LORA_OK
+    a_r0, k7 = _adapters(ranks=(0, 0))
+    assert _fused(a_r0, sg, x=0, y=0) == B.LORA_OK
+
+
+def test_backward_validation():
+    lib = L.load()
+    ad, ka = _adapters()
+    sg, ks = _segments([0, 3, 5], [0, 1])
+    n = ctypes.c_size_t(0)
+    assert lib.lora_workspace_size(B.OP_BACKWARD, ctypes.byref(ad), ctypes.byref(sg), ctypes.byref(n)) == 0
+
+    def bwd(flags=0, dA=FAKE, dB=FAKE, x=FAKE, dy=FAKE, dx=FAKE, wsb=n.value):
+        return lib.lora_packed_backward(x, 64, dy, 32, 0, 0, ctypes.byref(ad), ctypes.byref(sg), dx, 64,
+                                        dA, dB, flags, FAKE, wsb, 0)
+
+    assert bwd(flags=2) == B.LORA_INVALID_ARGUMENT
+    assert bwd(dA=0) == B.LORA_INVALID_ARGUMENT
+    assert bwd(dy=0) == B.LORA_INVALID_ARGUMENT
+    assert bwd(dx=FAKE + 8) == B.LORA_INVALID_ARGUMENT
+    assert bwd(wsb=n.value - 1) == B.LORA_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_size_bounds():
+    lib = L.load()
+    sizes = {}
+    for T in (16, 4096, 65536):
+        ad, ka = _adapters(ranks=(8, 64, 32), h_in=3584, h_out=3584)
+        sg, ks = _segments([0, T], [1])
+        for op in (B.OP_SHRINK, B.OP_EXPAND, B.OP_FUSED, B.OP_BACKWARD):
+            n = ctypes.c_size_t(0)
+            assert lib.lora_workspace_size(op, ctypes.byref(ad), ctypes.byref(sg), ctypes.byref(n)) == 0
+            sizes[(T, op)] = n.value
+    assert sizes[(16, B.OP_EXPAND)] == 0
+    # forward workspaces do not grow with the token count
+    assert sizes[(16, B.OP_FUSED)] == sizes[(65536, B.OP_FUSED)] < 16 << 20
+    assert sizes[(16, B.OP_BACKWARD)] < sizes[(65536, B.OP_BACKWARD)]
+    n = ctypes.c_size_t(0)
+    assert lib.lora_workspace_size(7, ctypes.byref(ad), ctypes.byref(sg), ctypes.byref(n)) != 0

@@ -1,0 +1,391 @@
+"""Benchmark of the multi-adapter LoRA (SGMV) hot path on one MI355X.
+
+Headline step: one mixed-adapter decode step on Qwen3-4B-like projections --
+256 tokens with adapter ids drawn uniformly from 8 resident rank-32 adapters
+(scale 2), grouped into segments by the library's host bookkeeping, then one
+fused shrink+expand launch per LoRA-wrapped projection: q (2560->2560),
+o (2560->2560) and gate_up (2560->19456). Inputs are synthetic (seeded) and
+resident in HBM; 16 copies of every tensor are rotated so that the 256 MB
+Infinity Cache cannot serve a step from the previous one.
+
+value = algorithmic bytes of the step / wall time per step (GB/s). Secondary
+entries time the prefill, heterogeneous-rank and packed-training workloads
+with HIP events (GB/s, TFLOP/s, fractions of the MI355X peaks).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+METRIC = "SGMV decode HBM GB/s (% peak) + prefill/backward TFLOP/s (% MFMA peak)"
+KERNEL = "sgmv_fwd_kernel"
+WORKLOAD = "decode_qwen3_4b_q_o_gate_up_256tok_8x_r32"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work (what the method must move / compute; no padding)
+# ---------------------------------------------------------------------------
+def active_token_ranks(ranks, seg_starts, seg_adapter):
+    """Per active token its rank (tokens of skipped segments excluded)."""
+    out = []
+    for g in range(len(seg_adapter)):
+        a = int(seg_adapter[g])
+        n = int(seg_starts[g + 1] - seg_starts[g])
+        if a < 0 or n == 0 or ranks[a] == 0:
+            continue
+        out.append(np.full(n, int(ranks[a])))
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+def used_adapters(ranks, seg_starts, seg_adapter):
+    s = set()
+    for g in range(len(seg_adapter)):
+        a = int(seg_adapter[g])
+        if a >= 0 and seg_starts[g + 1] > seg_starts[g] and ranks[a] > 0:
+            s.add(a)
+    return sorted(s)
+
+
+def fwd_work(h_in, h_out, ranks, seg_starts, seg_adapter, save_u=False):
+    tr = active_token_ranks(ranks, seg_starts, seg_adapter)
+    T = len(tr)
+    w = sum(int(ranks[a]) * (h_in + h_out) for a in used_adapters(ranks, seg_starts, seg_adapter))
+    bytes_ = 2 * T * h_in + 4 * T * h_out + 2 * w + (4 * int(tr.sum()) if save_u else 0)
+    flops = 2 * (h_in + h_out) * int(tr.sum())
+    return bytes_, flops
+
+
+def bwd_work(h_in, h_out, ranks, seg_starts, seg_adapter):
+    tr = active_token_ranks(ranks, seg_starts, seg_adapter)
+    T = len(tr)
+    w = sum(int(ranks[a]) * (h_in + h_out) for a in used_adapters(ranks, seg_starts, seg_adapter))
+    # dy, x read; dx read+write; u read; weights read; fp32 dA/dB written
+    bytes_ = 2 * T * h_out + 2 * T * h_in + 4 * T * h_in + 4 * int(tr.sum()) + 2 * w + 4 * w
+    flops = 4 * (h_in + h_out) * int(tr.sum())
+    return bytes_, flops
+
+
+# ---------------------------------------------------------------------------
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lora_adapter_batching_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{KERNEL}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def dev_bf16(bits):
+    import torch
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+# ---------------------------------------------------------------------------
+# Headline: decode step
+# ---------------------------------------------------------------------------
+class DecodeStep:
+    """Pre-marshalled C-ABI calls for one decode step over a rotation set."""
+
+    def __init__(self, projs, nsets):
+        import torch
+        import lora_adapter_batching_amd as L
+        from lora_adapter_batching_amd import binding as Bd
+        self.lib = L.load()
+        self.Bd = Bd
+        p0 = projs["q"]
+        self.ids = np.ascontiguousarray(p0.token_ids, np.int32)
+        self.T, self.N = int(p0.T), int(p0.N)
+        self.perm = np.zeros(self.T, np.int32)
+        self.starts = np.zeros(self.N + 2, np.int32)
+        self.adap = np.zeros(self.N + 1, np.int32)
+        # bookkeeping once to size the workspace and to order the inputs
+        perm, starts, adap = L.segments_from_ids(self.ids, self.N)
+        self.seg = L.Segments(starts, adap)
+        self.cseg = Bd.CSegments(self.T, self.N + 1, self.starts.ctypes.data, self.adap.ctypes.data, 0)
+        self.names = ["q", "o", "gate_up"]
+        self.sets = []
+        self.keep = []
+        dev_inputs = {}
+        for name in self.names:
+            p = projs[name]
+            dev_inputs[name] = (dev_bf16(p.x[perm]), [dev_bf16(a) for a in p.A], [dev_bf16(b) for b in p.B])
+        for s in range(nsets):
+            calls = []
+            for name in self.names:
+                p = projs[name]
+                x0, A0, B0 = dev_inputs[name]
+                x = x0.clone()
+                A = [a.clone() for a in A0]
+                B = [b.clone() for b in B0]
+                ad = L.Adapters(A, B, p.ranks, p.scales, p.h_in, p.h_out)
+                y = torch.zeros((self.T, p.h_out), dtype=torch.bfloat16, device="cuda")
+                ws = L.new_workspace(L.OP_FUSED, ad, self.seg)
+                self.keep.append((x, A, B, ad, y, ws))
+                calls.append((x.data_ptr(), x.stride(0), ad.c, y.data_ptr(), y.stride(0),
+                              ws.data_ptr(), ws.numel()))
+            self.sets.append(calls)
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.work = []
+        for name in self.names:
+            p = projs[name]
+            self.work.append(fwd_work(p.h_in, p.h_out, p.ranks, starts, adap))
+        self.bytes_per_step = sum(b for b, _ in self.work)
+        self.flops_per_step = sum(f for _, f in self.work)
+
+    def step(self, i, events=None):
+        lib = self.lib
+        st = lib.lora_segments_from_ids(self.ids.ctypes.data, self.T, self.N, self.perm.ctypes.data,
+                                        self.starts.ctypes.data, self.adap.ctypes.data)
+        if st:
+            raise RuntimeError(lib.lora_last_error().decode())
+        calls = self.sets[i % len(self.sets)]
+        segp = ctypes.byref(self.cseg)
+        for j, (xp, ldx, adc, yp, ldy, wsp, wsb) in enumerate(calls):
+            if events is not None:
+                events[j][0].record()
+            st = lib.lora_sgmv_fused(xp, ldx, adc, segp, yp, ldy, None, 0, wsp, wsb, self.stream)
+            if events is not None:
+                events[j][1].record()
+            if st:
+                raise RuntimeError(lib.lora_last_error().decode())
+
+
+def bench_decode(steps, warmup, nsets=16):
+    import torch
+    from workloads import make_c2_projections
+    projs = make_c2_projections(1)
+    ds = DecodeStep(projs, nsets)
+    for i in range(warmup):
+        ds.step(i)
+    torch.cuda.synchronize()
+    # timed region: wall clock for value, HIP events around every fused launch
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(3)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ds.step(warmup + i, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per_launch = np.array([[ev[i][j][0].elapsed_time(ev[i][j][1]) for j in range(3)] for i in range(steps)])
+    return ds, (t1 - t0) / steps, per_launch * 1e-3  # seconds
+
+
+# ---------------------------------------------------------------------------
+# Secondary workloads (HIP events around each call)
+# ---------------------------------------------------------------------------
+def _upload(prob, L):
+    import torch
+    if prob.segmented:
+        perm = np.arange(prob.T, dtype=np.int32)
+        starts = np.concatenate([[0], np.cumsum(prob.seg_lens)]).astype(np.int32)
+        adap = np.asarray(prob.seg_adapter, np.int32)
+    else:
+        perm, starts, adap = L.segments_from_ids(prob.token_ids, prob.N)
+    x = dev_bf16(prob.x[perm])
+    A = [dev_bf16(a) for a in prob.A]
+    B = [dev_bf16(b) for b in prob.B]
+    ad = L.Adapters(A, B, prob.ranks, prob.scales, prob.h_in, prob.h_out)
+    sg = L.Segments(starts, adap)
+    y = torch.zeros((prob.T, prob.h_out), dtype=torch.bfloat16, device="cuda")
+    return dict(x=x, A=A, B=B, ad=ad, sg=sg, y=y, starts=starts, adap=adap, perm=perm)
+
+
+def _time_calls(fn, reps, warm=3):
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    ts = []
+    for i in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i)
+        b.record()
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ts]) * 1e-3
+
+
+def _entry(name, seconds, bytes_, flops, extra=None):
+    med = float(np.median(seconds))
+    gbs = bytes_ / med / 1e9
+    tfl = flops / med / 1e12
+    d = {"workload": name, "us": round(med * 1e6, 2), "GB/s": round(gbs, 1),
+         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "TFLOP/s": round(tfl, 2),
+         "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 5), "bytes": int(bytes_), "flops": int(flops)}
+    if extra:
+        d.update(extra)
+    return d
+
+
+def bench_secondary(reps=20):
+    import torch
+    import lora_adapter_batching_amd as L
+    from workloads import make_config
+    out = []
+    for cfg, nsets in (("prefill", 3), ("hetero", 2)):
+        prob = make_config(cfg)
+        sets = [_upload(prob, L) for _ in range(nsets)]
+        ws = L.new_workspace(L.OP_FUSED, sets[0]["ad"], sets[0]["sg"])
+        b, f = fwd_work(prob.h_in, prob.h_out, prob.ranks, sets[0]["starts"], sets[0]["adap"])
+
+        def fn(i, sets=sets, ws=ws):
+            s = sets[i % len(sets)]
+            L.sgmv_fused(s["x"], s["ad"], s["sg"], s["y"], None, ws)
+        sec = _time_calls(fn, reps)
+        name = {"prefill": "prefill_llama3_8b_8192tok_4096x4096_8x_r16",
+                "hetero": "hetero_mlp_up_4096tok_4096x14336_32x_r8-128"}[cfg]
+        out.append(_entry(name, sec, b, f))
+        del sets
+        torch.cuda.empty_cache()
+    # packed training: fused forward (saving u) + packed backward
+    prob = make_config("train")
+    s = _upload(prob, L)
+    dy = dev_bf16(prob.dy)
+    rmax = int(prob.ranks.max())
+    u = torch.zeros((prob.T, rmax), dtype=torch.float32, device="cuda")
+    dx = torch.zeros((prob.T, prob.h_in), dtype=torch.bfloat16, device="cuda")
+    dA = [torch.zeros((int(r), prob.h_in), dtype=torch.float32, device="cuda") for r in prob.ranks]
+    dB = [torch.zeros((prob.h_out, int(r)), dtype=torch.float32, device="cuda") for r in prob.ranks]
+    pa = torch.tensor([t.data_ptr() for t in dA], dtype=torch.int64, device="cuda")
+    pb = torch.tensor([t.data_ptr() for t in dB], dtype=torch.int64, device="cuda")
+    wsf = L.new_workspace(L.OP_FUSED, s["ad"], s["sg"])
+    wsb = L.new_workspace(L.OP_BACKWARD, s["ad"], s["sg"])
+    bf, ff = fwd_work(prob.h_in, prob.h_out, prob.ranks, s["starts"], s["adap"], save_u=True)
+    bb, fb = bwd_work(prob.h_in, prob.h_out, prob.ranks, s["starts"], s["adap"])
+    sf = _time_calls(lambda i: L.sgmv_fused(s["x"], s["ad"], s["sg"], s["y"], u, wsf), reps // 2)
+    sb = _time_calls(lambda i: L.packed_backward(s["x"], dy, u, s["ad"], s["sg"], dx, pa, pb, 0, wsb),
+                     reps // 2)
+    out.append(_entry("train_fwd_qwen2p5_7b_65536tok_3584x3584_32x_r8-64", sf, bf, ff))
+    out.append(_entry("train_bwd_qwen2p5_7b_65536tok_3584x3584_32x_r8-64", sb, bb, fb))
+    out.append(_entry("train_fwd_bwd_qwen2p5_7b", np.array([np.median(sf) + np.median(sb)]), bf + bb,
+                      ff + fb))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on the host cores
+# ---------------------------------------------------------------------------
+def bench_cpu(bytes_per_step, budget_s=10.0):
+    from oracle import oracle
+    from workloads import make_c2_projections
+    projs = make_c2_projections(1)
+    batches = {k: oracle.Batch(p) for k, p in projs.items()}
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for k in ("q", "o", "gate_up"):
+            p = projs[k]
+            oracle.segments_from_ids(p.token_ids, p.N)
+            batches[k].forward()
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return {"value": round(bytes_per_step / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} full decode steps (grouping + q, o, gate_up forward, 256 tokens) in fp64, "
+                      f"{dt * 1e3:.1f} ms per step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        a = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": a.numel()}))
+        return
+    import lora_adapter_batching_amd as L
+    L.load()
+    log("decode step")
+    ds, sec_per_step, per_launch = bench_decode(args.steps, args.warmup)
+    value = ds.bytes_per_step / sec_per_step / 1e9
+    # dominant kernel: the fused launch (sgmv_fwd_kernel), 3 launches per step
+    avg_launch = float(per_launch.mean())
+    bytes_per_launch = ds.bytes_per_step / 3.0
+    achieved = bytes_per_launch / avg_launch / 1e9
+    traffic = load_traffic(WORKLOAD)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": KERNEL, "avg_launch_us": round(avg_launch * 1e6, 3),
+            "launch_us": {n: round(float(np.median(per_launch[:, j])) * 1e6, 3)
+                          for j, n in enumerate(ds.names)},
+            "algorithmic_bytes_per_launch": round(bytes_per_launch)}
+    gate = ds.work[2][0] / float(np.median(per_launch[:, 2])) / 1e9
+    roof["gate_up_GBs"] = round(gate, 1)
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec_per_step * 1e3, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": WORKLOAD, "tokens": ds.T, "adapters": ds.N, "rank": 32,
+                      "projections": {"q": [2560, 2560], "o": [2560, 2560], "gate_up": [2560, 19456]},
+                      "bytes_per_step": int(ds.bytes_per_step), "flops_per_step": int(ds.flops_per_step),
+                      "rotation_sets": len(ds.sets)},
+           "roofline": roof}
+    if not args.no_secondary:
+        log("secondary workloads")
+        del ds
+        torch.cuda.empty_cache()
+        out["secondary"] = bench_secondary()
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = bench_cpu(out["config"]["bytes_per_step"])
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

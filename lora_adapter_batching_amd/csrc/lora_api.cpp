@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -17,7 +18,7 @@
 #include "lora_plan.h"
 
 namespace lora {
-hipError_t launch_fwd(const FwdPlan& P, hipStream_t stream);
+hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream);
 hipError_t launch_transpose(const TransposePlan& P, hipStream_t stream);
 hipError_t launch_wgrad(const WgradPlan& P, int grid, hipStream_t stream);
 int wgrad_items_for_rank(int rank, int h_in, int h_out);
@@ -249,6 +250,25 @@ struct FwdCall {
   int rmax;  // largest rank of the adapters (partials row length)
 };
 
+// Optional planner override for tuning, read once from LORA_SGMV_FORCE:
+// "tile:NC" forces the on-chip fused mode with NC column chunks per tile,
+// "dep:KS:NC" the split-shrink mode. Applies to fused calls only.
+struct ForcePlan {
+  int mode = -1, ks = 0, nc = 0;
+};
+ForcePlan force_plan() {
+  static ForcePlan f = [] {
+    ForcePlan r;
+    const char* e = std::getenv("LORA_SGMV_FORCE");
+    if (!e) return r;
+    int a = 0, b = 0;
+    if (std::sscanf(e, "tile:%d", &a) == 1 && a > 0) { r.mode = kModeFusedTile; r.nc = a; }
+    else if (std::sscanf(e, "dep:%d:%d", &a, &b) == 2 && a > 0 && b > 0) { r.mode = kModeFusedDep; r.ks = a; r.nc = b; }
+    return r;
+  }();
+  return f;
+}
+
 int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int>& slot_of,
             hipStream_t stream) {
   if (segs.empty()) return LORA_OK;
@@ -311,7 +331,25 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
       P.n_items_a = tiles * P.nc;
       P.grid = P.n_items_a;
     } else {
-      if (tiles >= cus / 2 || tiles > kMaxDepTiles) {
+      const ForcePlan fp = force_plan();
+      if (fp.mode == kModeFusedTile) {
+        P.mode = kModeFusedTile;
+        P.ks = 1;
+        P.kchunk = round_up(c.K, 64);
+        P.nblk = cdiv(nblocks, std::min(fp.nc, nblocks));
+        P.nc = cdiv(nblocks, P.nblk);
+        P.n_items_a = tiles * P.nc;
+        P.grid = P.n_items_a;
+      } else if (fp.mode == kModeFusedDep && tiles <= kMaxDepTiles && tiles * fp.ks <= kMaxPartials) {
+        P.mode = kModeFusedDep;
+        P.kchunk = round_up(cdiv(c.K, fp.ks), 64);
+        P.ks = cdiv(c.K, P.kchunk);
+        P.nblk = cdiv(nblocks, std::min(fp.nc, nblocks));
+        P.nc = cdiv(nblocks, P.nblk);
+        P.n_items_a = tiles * P.ks;
+        P.n_items_b = tiles * P.nc;
+        P.grid = P.n_items_a + P.n_items_b;
+      } else if (tiles >= cus / 2 || tiles > kMaxDepTiles) {
         P.mode = kModeFusedTile;
         P.ks = 1;
         P.kchunk = round_up(c.K, 64);
@@ -331,7 +369,10 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
       }
     }
     if (P.grid <= 0) continue;
-    const hipError_t e = launch_fwd(P, stream);
+    int rmax_launch = 0;
+    for (int i = 0; i < ns; ++i) rmax_launch = std::max(rmax_launch, (int)P.seg_rank[i]);
+    const int rbmax = rmax_launch <= 32 ? 1 : (rmax_launch <= 64 ? 2 : 4);
+    const hipError_t e = launch_fwd(P, rbmax, stream);
     if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
   }
   return LORA_OK;

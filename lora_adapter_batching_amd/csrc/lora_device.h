@@ -17,6 +17,35 @@ __device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// ---------------------------------------------------------------------------
+// Buffer-resource access. A raw buffer resource covers [base, base + bytes);
+// an access whose byte offset is at or beyond `bytes` reads zeros and a store
+// there is dropped, without a branch. Lanes with nothing to load or store use
+// kOff (outside every resource: spans stay below 2 GiB).
+// ---------------------------------------------------------------------------
+constexpr uint32_t kOff = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer, 32-bit data format
+
+// Both arguments must be wave-uniform (they are moved to scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mk_rsrc(const void* base, int64_t bytes) {
+  const int64_t cap = 0x7ffffff0;
+  const int n = __builtin_amdgcn_readfirstlane((int)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)));
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
 // bf16 bit pattern -> float (exact).
 __device__ __forceinline__ float bf2f(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);

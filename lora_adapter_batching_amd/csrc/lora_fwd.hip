@@ -33,21 +33,40 @@ struct TileInfo {
   float scale;
 };
 
-__device__ __forceinline__ TileInfo tile_info(const FwdPlan& P, int g) {
-  int lo = 0, hi = P.n_seg;
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (P.seg_tile0[mid] <= g) lo = mid; else hi = mid;
+// Finds the segment that holds tile g with one parallel read of the segment
+// table: thread i checks segment i and the matching thread publishes the
+// tile's description in LDS (a binary search would chain several dependent
+// loads of the kernel-argument table).
+__device__ __forceinline__ TileInfo tile_info(const FwdPlan& P, int g, TileInfo* lds) {
+  const int i = threadIdx.x;
+  if (i < P.n_seg) {
+    const int t0 = P.seg_tile0[i];
+    const int t1 = (i + 1 < P.n_seg) ? P.seg_tile0[i + 1] : P.n_tiles;
+    const int tok0 = P.seg_tok0[i], ntok = P.seg_ntok[i];
+    const int adapter = P.seg_adapter[i], rank = P.seg_rank[i], slot = P.seg_slot[i];
+    const float scale = P.seg_scale[i];
+    if (g >= t0 && g < t1) {
+      const int tt = g - t0;
+      TileInfo t;
+      t.g = g;
+      t.p0 = tok0 + tt * kTileM;
+      t.cnt = min(kTileM, ntok - tt * kTileM);
+      t.adapter = adapter;
+      t.rank = rank;
+      t.slot = slot;
+      t.scale = scale;
+      *lds = t;
+    }
   }
-  TileInfo t;
-  t.g = g;
-  const int tt = g - P.seg_tile0[lo];
-  t.p0 = P.seg_tok0[lo] + tt * kTileM;
-  t.cnt = min(kTileM, P.seg_ntok[lo] - tt * kTileM);
-  t.adapter = P.seg_adapter[lo];
-  t.rank = P.seg_rank[lo];
-  t.slot = P.seg_slot[lo];
-  t.scale = P.seg_scale[lo];
+  __syncthreads();
+  TileInfo t = *lds;
+  t.g = __builtin_amdgcn_readfirstlane(t.g);
+  t.p0 = __builtin_amdgcn_readfirstlane(t.p0);
+  t.cnt = __builtin_amdgcn_readfirstlane(t.cnt);
+  t.adapter = __builtin_amdgcn_readfirstlane(t.adapter);
+  t.rank = __builtin_amdgcn_readfirstlane(t.rank);
+  t.slot = __builtin_amdgcn_readfirstlane(t.slot);
+  t.scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t.scale)));
   return t;
 }
 
@@ -68,34 +87,53 @@ __device__ __forceinline__ int64_t token_row(const FwdPlan& P, int p) {
 // ---------------------------------------------------------------------------
 // Shrink: acc[b] (rows = rank 32b.., cols = this lane's token) over k in [kb, ke)
 // ---------------------------------------------------------------------------
-template <int RB, int UNR>
-__device__ __forceinline__ void shrink_acc(const uint16_t* xrow, bool xvalid, const uint16_t* W,
+// Ring depth of the shrink loop (k-steps of 16 whose loads are in flight).
+template <int RB>
+struct ShrinkDepth {
+  static constexpr int v = RB == 1 ? 8 : (RB == 2 ? 6 : 4);
+};
+// xr: resource over the tile's X rows; xoff: byte offset of this lane's token
+// row (kOff if the token is not valid). W rows of rank >= rank fall outside
+// the W resource and read as zero.
+template <int RB>
+__device__ __forceinline__ void shrink_acc(__amdgpu_buffer_rsrc_t xr, uint32_t xoff, const uint16_t* W,
                                            int64_t ldw, int rank, int kb, int ke, int wave,
                                            int lane, f32x16 (&acc)[RB]) {
+  constexpr int DS = ShrinkDepth<RB>::v;
   const int h = lane >> 5, m = lane & 31;
-  const uint16_t* wrow[RB];
-  bool wv[RB];
+  const __amdgpu_buffer_rsrc_t wr = mk_rsrc(W, (int64_t)rank * ldw * 2);
+  uint32_t woff[RB];
 #pragma unroll
-  for (int b = 0; b < RB; ++b) {
-    const int row = 32 * b + m;
-    wv[b] = row < rank;
-    wrow[b] = W + (int64_t)(wv[b] ? row : 0) * ldw;
+  for (int b = 0; b < RB; ++b) woff[b] = (uint32_t)((int64_t)(32 * b + m) * ldw * 2);
+  // each wave takes a contiguous quarter of [kb, ke) (multiple of 16 long)
+  const int q = ((ke - kb + 63) >> 6) << 4;
+  const int kw0 = __builtin_amdgcn_readfirstlane(kb + wave * q);
+  const int kw1 = __builtin_amdgcn_readfirstlane(min(ke, kw0 + q));
+  const int nsteps = __builtin_amdgcn_readfirstlane(kw1 > kw0 ? (kw1 - kw0 + 15) >> 4 : 0);
+  u32x4 xf[DS], wf[RB][DS];
+  auto load = [&](int j, int s) {
+    const int k = kw0 + 16 * j + 8 * h;
+    const bool kv = j < nsteps && k < kw1;
+    xf[s] = bld16(xr, kv ? xoff + 2u * (uint32_t)k : kOff);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) wf[b][s] = bld16(wr, kv ? woff[b] + 2u * (uint32_t)k : kOff);
+  };
+  // ring: DS k-steps of loads stay in flight while earlier ones are consumed
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    load(s, s);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  constexpr int kUnit = 16 * UNR;
-  for (int k0 = kb + wave * kUnit; k0 < ke; k0 += 4 * kUnit) {
-    u32x4 xf[UNR], wf[RB][UNR];
+  for (int j0 = 0; j0 < nsteps; j0 += DS) {
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int k = k0 + 16 * u + 8 * h;
-      const bool kv = k < ke;
-      xf[u] = (xvalid && kv) ? ld16(xrow + k) : zero16();
+    for (int s = 0; s < DS; ++s) {
 #pragma unroll
-      for (int b = 0; b < RB; ++b) wf[b][u] = (wv[b] && kv) ? ld16(wrow[b] + k) : zero16();
+      for (int b = 0; b < RB; ++b) acc[b] = mfma32(as_bf16x8(wf[b][s]), as_bf16x8(xf[s]), acc[b]);
+      load(j0 + s + DS, s);
+      // keep slot order: the refill of slot s is issued before slot s+1 is
+      // consumed, so only slot s+1's own loads need to have arrived
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u)
-#pragma unroll
-      for (int b = 0; b < RB; ++b) acc[b] = mfma32(as_bf16x8(wf[b][u]), as_bf16x8(xf[u]), acc[b]);
   }
 }
 
@@ -164,55 +202,194 @@ __device__ __forceinline__ u32x4 ld_partial(const uint16_t* row, int k, int rank
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// y[token][col] += oscale * sum_k V[col][k] P[token][k] for column blocks
-// [cb_begin, cb_end) handled round-robin by the 4 waves.
+// One 32-column block of the expand as held in registers by a lane: the
+// A-operand rows of V and the two 16-byte runs of this lane's y row.
 template <int RB>
-__device__ __forceinline__ void expand_run(const PFrags<RB>& F, const uint16_t* V, int64_t ldv,
-                                           int rank, bool vec16, int ncols, uint16_t* yrow,
-                                           bool yvalid, int cb_begin, int cb_end, float oscale,
-                                           int wave, int lane) {
+struct ExpBlock {
+  u32x4 vf[2 * RB];
+  u32x4 y0, y1;
+  int cb;  // block index, -1 if none
+};
+
+struct ExpArgs {
+  __amdgpu_buffer_rsrc_t vr;  // V [ncols, ldv] bf16
+  int64_t ldv;
+  int rank;
+  bool vec16;
+  int ncols;
+  __amdgpu_buffer_rsrc_t yr;  // y rows of the tile
+  uint32_t yoff;              // this lane's y row (kOff if invalid)
+  float oscale;
+};
+
+template <int RB>
+__device__ __forceinline__ void exp_load(const ExpArgs& a, int cb, int lane, ExpBlock<RB>& B) {
   const int m = lane & 31, h = lane >> 5;
-  const int kbn = (rank + 15) >> 4;
-  for (int cb = cb_begin + wave; cb < cb_end; cb += 4) {
-    const int col0 = cb * 32;
-    const int vcol = col0 + colmap(m);
-    const bool vok = vcol < ncols;
-    const uint16_t* vrow = V + (int64_t)(vok ? vcol : 0) * ldv;
-    u32x4 vf[2 * RB];
+  B.cb = cb;
+  const int col0 = cb * 32;
+  const uint32_t vrow = (uint32_t)((int64_t)(col0 + colmap(m)) * a.ldv * 2);  // rows >= ncols: outside
 #pragma unroll
-    for (int kb = 0; kb < 2 * RB; ++kb) {
-      const int k = 16 * kb + 8 * h;
-      if (kb < kbn && vok && k < rank)
-        vf[kb] = vec16 ? ld16(vrow + k) : ld_partial(vrow, k, rank);
-      else
-        vf[kb] = zero16();
-    }
-    const int c0 = col0 + 8 * h, c1 = col0 + 16 + 8 * h;
-    const bool ok0 = yvalid && c0 < ncols, ok1 = yvalid && c1 < ncols;
-    const u32x4 y0 = ok0 ? ld16(yrow + c0) : zero16();
-    const u32x4 y1 = ok1 ? ld16(yrow + c1) : zero16();
-    f32x16 acc = zero_acc16();
+  for (int kb = 0; kb < 2 * RB; ++kb) {
+    const int k = 16 * kb + 8 * h;
+    if (a.vec16) {
+      B.vf[kb] = bld16(a.vr, k < a.rank ? vrow + 2u * k : kOff);
+    } else {
+      uint32_t w[4];
 #pragma unroll
-    for (int kb = 0; kb < 2 * RB; ++kb) {
-      if (kb < kbn) {
-        acc = mfma32(as_bf16x8(vf[kb]), F.hi[kb], acc);
-        acc = mfma32(as_bf16x8(vf[kb]), F.lo[kb], acc);
+      for (int q = 0; q < 4; ++q) {
+        const int k0 = k + 2 * q;
+        const uint32_t lo = bld2(a.vr, k0 < a.rank ? vrow + 2u * k0 : kOff);
+        const uint32_t hi = bld2(a.vr, k0 + 1 < a.rank ? vrow + 2u * (k0 + 1) : kOff);
+        w[q] = (lo & 0xffffu) | (hi << 16);
       }
-    }
-    float f[8];
-    if (ok0) {
-      unpack8(y0, f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = f[i] + oscale * acc[i];
-      st16(yrow + c0, pack8(f));
-    }
-    if (ok1) {
-      unpack8(y1, f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = f[i] + oscale * acc[8 + i];
-      st16(yrow + c1, pack8(f));
+      B.vf[kb] = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
+  const int c0 = col0 + 8 * h, c1 = col0 + 16 + 8 * h;
+  B.y0 = bld16(a.yr, c0 < a.ncols ? a.yoff + 2u * c0 : kOff);
+  B.y1 = bld16(a.yr, c1 < a.ncols ? a.yoff + 2u * c1 : kOff);
+}
+
+template <int RB>
+__device__ __forceinline__ void exp_finish(const ExpArgs& a, const PFrags<RB>& F, int lane,
+                                           const ExpBlock<RB>& B) {
+  const int h = lane >> 5;
+  const int kbn = (a.rank + 15) >> 4;
+  f32x16 acc = zero_acc16();
+#pragma unroll
+  for (int kb = 0; kb < 2 * RB; ++kb) {
+    if (kb < kbn) {
+      acc = mfma32(as_bf16x8(B.vf[kb]), F.hi[kb], acc);
+      acc = mfma32(as_bf16x8(B.vf[kb]), F.lo[kb], acc);
+    }
+  }
+  const int col0 = B.cb * 32;
+  const int c0 = col0 + 8 * h, c1 = col0 + 16 + 8 * h;
+  float f[8];
+  unpack8(B.y0, f);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = f[i] + a.oscale * acc[i];
+  bst16(a.yr, c0 < a.ncols ? a.yoff + 2u * c0 : kOff, pack8(f));
+  unpack8(B.y1, f);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = f[i] + a.oscale * acc[8 + i];
+  bst16(a.yr, c1 < a.ncols ? a.yoff + 2u * c1 : kOff, pack8(f));
+}
+
+// Blocks per round of the expand loop (32-column blocks whose loads a wave
+// issues together). Stores share the memory counter with loads on this chip
+// family, so a pending y store would force every later wait to drain all
+// loads; the expand therefore runs in rounds: issue a round's loads, wait
+// once, then compute and store the round.
+template <int RB>
+struct ExpandDepth {
+  static constexpr int v = RB == 1 ? 8 : (RB == 2 ? 4 : 2);
+};
+
+template <int RB>
+struct ExpRing {
+  ExpBlock<RB> b[ExpandDepth<RB>::v];
+};
+
+// Loads the round of blocks cb_first, cb_first + 4, ... (< cb_end).
+template <int RB>
+__device__ __forceinline__ void exp_ring_load(const ExpArgs& a, int cb_first, int cb_end, int lane,
+                                              ExpRing<RB>& R) {
+  constexpr int DE = ExpandDepth<RB>::v;
+#pragma unroll
+  for (int s = 0; s < DE; ++s) {
+    const int cb = cb_first + 4 * s;
+    if (cb < cb_end) {
+      exp_load<RB>(a, cb, lane, R.b[s]);
+    } else {
+      R.b[s].cb = -1;
+#pragma unroll
+      for (int kb = 0; kb < 2 * RB; ++kb) R.b[s].vf[kb] = zero16();
+      R.b[s].y0 = zero16();
+      R.b[s].y1 = zero16();
+    }
+  }
+}
+
+// y[token][col] += oscale * sum_k V[col][k] P[token][k] over the wave's
+// blocks; R holds the first round (already issued by the caller).
+template <int RB>
+__device__ __forceinline__ void exp_ring_run(const ExpArgs& a, const PFrags<RB>& F, int cb_first,
+                                             int cb_end, int lane, ExpRing<RB>& R) {
+  constexpr int DE = ExpandDepth<RB>::v;
+  int cb = cb_first;
+  while (true) {
+#pragma unroll
+    for (int s = 0; s < DE; ++s)
+      if (R.b[s].cb >= 0) exp_finish<RB>(a, F, lane, R.b[s]);
+    cb += 4 * DE;
+    if (cb >= cb_end) break;
+    exp_ring_load<RB>(a, cb, cb_end, lane, R);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup hand-off of split-K partial sums (see item_shrink and
+// item_expand_wait). LORA_XWG selects the protocol:
+//  1: every thread fences at agent scope (release before, acquire after).
+//  2: one thread per workgroup fences, ordered with the others by barriers.
+//  3: partials move with agent-scope (cache-coherent) accesses and the
+//     counters with atomics; no cache-wide writeback or invalidate.
+// ---------------------------------------------------------------------------
+#ifndef LORA_XWG
+#define LORA_XWG 3
+#endif
+
+// Returns a value that depends on the store having been performed (protocol
+// 3 uses a returning atomic swap; the caller folds the results into LDS so
+// the wave waits for every swap before it reaches the barrier).
+__device__ __forceinline__ float xwg_store(float* p, float v) {
+#if LORA_XWG == 3
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  *p = v;
+  return 0.f;
+#endif
+}
+__device__ __forceinline__ float xwg_load(const float* p) {
+#if LORA_XWG == 3
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  return *p;
+#endif
+}
+// Called by every thread after its partial stores; thread 0 increments *ctr
+// and gets the previous value (other threads get 0).
+__device__ __forceinline__ int xwg_signal(int* ctr) {
+  int old = 0;
+#if LORA_XWG == 1
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+#elif LORA_XWG == 2
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#else
+  __syncthreads();
+  if (threadIdx.x == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#endif
+  return old;
+}
+// Thread 0 has seen the counter complete; make the partials visible to the
+// whole workgroup (ends with a barrier).
+__device__ __forceinline__ void xwg_acquire() {
+#if LORA_XWG == 2
+  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __syncthreads();
+#elif LORA_XWG == 1
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#else
+  __syncthreads();
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -221,24 +398,34 @@ __device__ __forceinline__ void expand_run(const PFrags<RB>& F, const uint16_t* 
 struct Smem {
   float red[4 * 16 * 64];
   float Pl[kTileM * kLdp];
+  TileInfo ti;
   int flag;
 };
 
-template <int RB>
-__device__ __forceinline__ int unroll_for() {
-  return RB == 1 ? 8 : (RB == 2 ? 4 : 2);
+// X rows of the tile as a buffer resource: based at the tile's first row when
+// rows are contiguous, at X itself for a token_rows gather.
+__device__ __forceinline__ void tile_rows(const uint16_t* base, int64_t ld, int width, const FwdPlan& P,
+                                          const TileInfo& t, __amdgpu_buffer_rsrc_t& r, uint32_t& off) {
+  const int n = threadIdx.x & 31;
+  const bool valid = n < t.cnt;
+  if (P.token_rows) {
+    r = mk_rsrc(base, (int64_t)0x7ffffff0);
+    off = valid ? (uint32_t)((int64_t)P.token_rows[t.p0 + n] * ld * 2) : kOff;
+  } else {
+    r = mk_rsrc(base + (int64_t)t.p0 * ld, ((int64_t)(t.cnt - 1) * ld + width) * 2);
+    off = valid ? (uint32_t)((int64_t)n * ld * 2) : kOff;
+  }
 }
 
 template <int RB>
 __device__ __forceinline__ void shrink_range(const FwdPlan& P, const TileInfo& t, int kb, int ke,
                                              int wave, int lane, f32x16 (&acc)[RB]) {
-  const int n = lane & 31;
-  const bool xvalid = n < t.cnt;
-  const uint16_t* xrow = P.X + (xvalid ? token_row(P, t.p0 + n) : 0) * P.ldx;
+  __amdgpu_buffer_rsrc_t xr;
+  uint32_t xoff;
+  tile_rows(P.X, P.ldx, P.K, P, t, xr, xoff);
 #pragma unroll
   for (int b = 0; b < RB; ++b) acc[b] = zero_acc16();
-  constexpr int UNR = RB == 1 ? 8 : (RB == 2 ? 4 : 2);
-  shrink_acc<RB, UNR>(xrow, xvalid, w_ptr(P, t), P.K, t.rank, kb, ke, wave, lane, acc);
+  shrink_acc<RB>(xr, xoff, w_ptr(P, t), P.K, t.rank, kb, ke, wave, lane, acc);
 }
 
 // Writes Pl rows 0..31, columns < 32*RB (zero where rank/token invalid) to U.
@@ -250,22 +437,36 @@ __device__ __forceinline__ void store_u_from_lds(const FwdPlan& P, const TileInf
   }
 }
 
+__device__ __forceinline__ ExpArgs exp_args(const FwdPlan& P, const TileInfo& t) {
+  ExpArgs a;
+  tile_rows(P.Y, P.ldy, P.N, P, t, a.yr, a.yoff);
+  a.ldv = ((t.rank + P.v_round - 1) / P.v_round) * P.v_round;
+  a.vec16 = (a.ldv & 7) == 0;
+  a.vr = mk_rsrc(v_ptr(P, t), (int64_t)P.N * a.ldv * 2);
+  a.rank = t.rank;
+  a.ncols = P.N;
+  a.oscale = P.scale_in_shrink ? 1.f : t.scale;
+  return a;
+}
+
+// Column-block range of n-chunk c: this wave starts at cb0 + wave.
+__device__ __forceinline__ void chunk_blocks(const FwdPlan& P, int c, int& cb0, int& cb_end) {
+  const int nblocks = (P.N + 31) >> 5;
+  cb0 = c * P.nblk;
+  cb_end = min(nblocks, cb0 + P.nblk);
+}
+
 template <int RB>
 __device__ __forceinline__ void expand_tile_from_lds(const FwdPlan& P, const TileInfo& t, int c,
                                                      const float* Pl, int wave, int lane) {
+  const ExpArgs a = exp_args(P, t);
+  int cb0, cb_end;
+  chunk_blocks(P, c, cb0, cb_end);
+  ExpRing<RB> R;
+  exp_ring_load<RB>(a, cb0 + wave, cb_end, lane, R);
   PFrags<RB> F;
   build_pfrags<RB>(Pl, t.rank, lane, F);
-  const int n = lane & 31;
-  const bool yvalid = n < t.cnt;
-  uint16_t* yrow = P.Y + (yvalid ? token_row(P, t.p0 + n) : 0) * P.ldy;
-  const int nblocks = (P.N + 31) >> 5;
-  const int cb0 = c * P.nblk;
-  const int cb1 = min(nblocks, cb0 + P.nblk);
-  const int ldv = ((t.rank + P.v_round - 1) / P.v_round) * P.v_round;
-  const bool vec16 = (ldv & 7) == 0;
-  const float oscale = P.scale_in_shrink ? 1.f : t.scale;
-  expand_run<RB>(F, v_ptr(P, t), ldv, t.rank, vec16, P.N, yrow, yvalid, cb0, cb1, oscale, wave,
-                 lane);
+  exp_ring_run<RB>(a, F, cb0 + wave, cb_end, lane, R);
 }
 
 // kModeFusedTile: full shrink of one tile on chip, then its n-chunk c.
@@ -315,28 +516,29 @@ __device__ __forceinline__ void item_shrink(const FwdPlan& P, Smem& S, const Til
   }
   float* part = partial_ptr(P, t.g, c);
   const int rpad = P.rpad;
-  reduce_waves<RB>(S.red, acc, wave, lane, [&](int k, int n, float v) { part[n * rpad + k] = v; });
-  // publish the partial: every thread's stores, then one counter increment
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
+  float sink = 0.f;
+  reduce_waves<RB>(S.red, acc, wave, lane,
+                   [&](int k, int n, float v) { sink += xwg_store(part + n * rpad + k, v); });
+#if LORA_XWG == 3
+  S.red[threadIdx.x] = sink;  // waits for every swap of this thread
+#else
+  (void)sink;
+#endif
   int* ctr = P.counters + kCtrTiles + t.g;
-  if (P.mode == kModeFusedDep) {
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    return;
-  }
+  const int old = xwg_signal(ctr);
+  // storing the returned count makes thread 0 wait for its increment to be
+  // performed before anything later (e.g. the done count) is issued
+  if (threadIdx.x == 0) S.flag = old;
+  if (P.mode == kModeFusedDep) return;
   // kModeShrink, ks > 1: the last arriving chunk sums all chunks in order
-  if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    S.flag = (old == P.ks - 1);
-  }
   __syncthreads();
-  if (!S.flag) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (S.flag != P.ks - 1) return;
+  xwg_acquire();
   for (int e = threadIdx.x; e < kTileM * t.rank; e += kThreads) {
     const int n = e / t.rank, k = e - n * t.rank;
     if (n >= t.cnt) continue;
-    float s = partial_ptr(P, t.g, 0)[n * rpad + k];
-    for (int q = 1; q < P.ks; ++q) s += partial_ptr(P, t.g, q)[n * rpad + k];
+    float s = xwg_load(partial_ptr(P, t.g, 0) + n * rpad + k);
+    for (int q = 1; q < P.ks; ++q) s += xwg_load(partial_ptr(P, t.g, q) + n * rpad + k);
     P.U[(int64_t)(t.p0 + n) * P.ldu + k] = s * ps;
   }
   if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -350,6 +552,13 @@ template <int RB>
 __device__ __forceinline__ void item_expand_wait(const FwdPlan& P, Smem& S, const TileInfo& t, int c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int* ctr = P.counters + kCtrTiles + t.g;
+  // the y rows and expand weights do not depend on the shrink: load the
+  // first block before waiting
+  const ExpArgs ea = exp_args(P, t);
+  int cb0, cb_end;
+  chunk_blocks(P, c, cb0, cb_end);
+  ExpRing<RB> R;
+  exp_ring_load<RB>(ea, cb0 + wave, cb_end, lane, R);
   if (threadIdx.x == 0) {
     const uint64_t t0 = wall_clock64();
     int ready = 0;
@@ -360,20 +569,21 @@ __device__ __forceinline__ void item_expand_wait(const FwdPlan& P, Smem& S, cons
     }
     S.flag = ready;
   }
-  __syncthreads();
+  xwg_acquire();
   const float ps = P.scale_in_shrink ? t.scale : 1.f;
   float* Pl = S.Pl;
   const int rcols = 32 * RB;
   if (S.flag) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int rpad = P.rpad;
     for (int e = threadIdx.x; e < kTileM * rcols; e += kThreads) {
       const int n = e / rcols, k = e - n * rcols;
-      float s = partial_ptr(P, t.g, 0)[n * rpad + k];
-      for (int q = 1; q < P.ks; ++q) s += partial_ptr(P, t.g, q)[n * rpad + k];
+      float s = xwg_load(partial_ptr(P, t.g, 0) + n * rpad + k);
+      for (int q = 1; q < P.ks; ++q) s += xwg_load(partial_ptr(P, t.g, q) + n * rpad + k);
       Pl[n * kLdp + k] = s * ps;
     }
   } else {
+    // the prefetched blocks are dropped while the shrink is recomputed
+    // (keeps both register sets from being live at once) and loaded again
     for (int q = 0; q < P.ks; ++q) {
       const int kb = q * P.kchunk;
       const int ke = min(P.K, kb + P.kchunk);
@@ -387,10 +597,13 @@ __device__ __forceinline__ void item_expand_wait(const FwdPlan& P, Smem& S, cons
       const int n = e / rcols, k = e - n * rcols;
       Pl[n * kLdp + k] *= ps;
     }
+    exp_ring_load<RB>(ea, cb0 + wave, cb_end, lane, R);
   }
   __syncthreads();
   if (P.write_u && c == 0) store_u_from_lds(P, t, Pl);
-  expand_tile_from_lds<RB>(P, t, c, Pl, wave, lane);
+  PFrags<RB> F;
+  build_pfrags<RB>(Pl, t.rank, lane, F);
+  exp_ring_run<RB>(ea, F, cb0 + wave, cb_end, lane, R);
 }
 
 template <int RB>
@@ -403,6 +616,7 @@ __device__ __forceinline__ void run_item(const FwdPlan& P, Smem& S, const TileIn
   }
 }
 
+template <int RBMAX>
 __global__ __launch_bounds__(kThreads) void sgmv_fwd_kernel(FwdPlan P) {
   __shared__ Smem S;
   const int b = blockIdx.x;
@@ -422,28 +636,35 @@ __global__ __launch_bounds__(kThreads) void sgmv_fwd_kernel(FwdPlan P) {
   }
   if (item >= 0) {
     const int g = item / per, c = item - g * per;
-    const TileInfo t = tile_info(P, g);
-    if (t.rank <= 32) run_item<1>(P, S, t, kind, c);
-    else if (t.rank <= 64) run_item<2>(P, S, t, kind, c);
-    else run_item<4>(P, S, t, kind, c);
+    const TileInfo t = tile_info(P, g, &S.ti);
+    if (RBMAX == 1 || t.rank <= 32) run_item<1>(P, S, t, kind, c);
+    else if (RBMAX == 2 || t.rank <= 64) run_item<(RBMAX >= 2 ? 2 : 1)>(P, S, t, kind, c);
+    else run_item<RBMAX>(P, S, t, kind, c);
   }
   if (P.mode == kModeFusedDep) {
-    // the last workgroup to finish returns every counter of this launch to zero
+    // the last workgroup to finish returns every counter of this launch to
+    // zero (thread 0's earlier counter atomics have returned before this one
+    // is issued, so every tile increment lands before the done count does)
     __syncthreads();
     if (threadIdx.x == 0) {
-      const int old = __hip_atomic_fetch_add(P.counters + kCtrDone, 1, __ATOMIC_ACQ_REL,
+      const int old = __hip_atomic_fetch_add(P.counters + kCtrDone, 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
       if (old == P.grid - 1) {
         for (int g = 0; g < P.n_tiles; ++g)
           __hip_atomic_store(P.counters + kCtrTiles + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(P.counters + kCtrDone, 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(P.counters + kCtrDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
 }
 
-hipError_t launch_fwd(const FwdPlan& P, hipStream_t stream) {
-  hipLaunchKernelGGL(sgmv_fwd_kernel, dim3(P.grid), dim3(kThreads), 0, stream, P);
+hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream) {
+  if (rbmax <= 1)
+    hipLaunchKernelGGL(sgmv_fwd_kernel<1>, dim3(P.grid), dim3(kThreads), 0, stream, P);
+  else if (rbmax == 2)
+    hipLaunchKernelGGL(sgmv_fwd_kernel<2>, dim3(P.grid), dim3(kThreads), 0, stream, P);
+  else
+    hipLaunchKernelGGL(sgmv_fwd_kernel<4>, dim3(P.grid), dim3(kThreads), 0, stream, P);
   return hipGetLastError();
 }
 

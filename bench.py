@@ -85,27 +85,38 @@ def bwd_work(h_in, h_out, ranks, seg_starts, seg_adapter):
 
 # ---------------------------------------------------------------------------
 def kernel_source_hash():
+    """Hash of the library sources with comments and whitespace removed, so
+    that counter summaries stay tied to the code they measured."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "lora_adapter_batching_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            src = open(os.path.join(csrc, f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            src = re.sub(r"//[^\n]*", "", src)
+            h.update(re.sub(r"\s+", "", src).encode())
     return h.hexdigest()[:16]
 
 
 def load_traffic(workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic_<kernel>_<workload>.txt, 'key: value' lines), if it was
     taken on the current kernel sources (else None)."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{KERNEL}_{workload}.json")
+    p = os.path.join(ROOT, "profiles", f"traffic_{KERNEL}_{workload}.txt")
     if not os.path.exists(p):
         return None
+    kv = {}
+    for line in open(p):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_hash():
+        return None
     try:
-        d = json.load(open(p))
-    except Exception:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
         return None
-    if d.get("kernel_source_sha") != kernel_source_hash():
-        return None
-    return d.get("traffic_bytes_per_launch")
 
 
 def dev_bf16(bits):

@@ -7,10 +7,10 @@
  *     u_t = A_i x_t            "shrink" to rank r_i        A_i: [r_i, h_in]
  *     y_t = y_t + s_i B_i u_t  "expand" back to h_out      B_i: [h_out, r_i]
  *
- * for all adapters of the batch in one kernel launch (C-LoRA announcement,
+ * for all adapters of the batch in one kernel launch ("Trajectory presenta C-LoRA" (vivodigitale.it),
  * "Come funziona l'architettura": a decode batch mixes tokens of different
  * resident adapters and the per-adapter matrix-vector work is fused into a
- * single launch). The packed-training backward (PLoRA summary, "LoRA
+ * single launch). The packed-training backward ("Technische Samenvatting: PLoRA" (gist.science), "LoRA
  * Execution Engine", packed kernels over concatenated adapter tensors, tiled
  * along the sequence or hidden dimension rather than the small rank) gives
  *
@@ -81,7 +81,7 @@ enum { LORA_OP_SHRINK = 0, LORA_OP_EXPAND = 1, LORA_OP_FUSED = 2, LORA_OP_BACKWA
 
 /*
  * The adapters resident on the GPU (all of them reachable from one launch:
- * C-LoRA announcement, "Come funziona l'architettura", every adapter loaded
+ * "Trajectory presenta C-LoRA" (vivodigitale.it), "Come funziona l'architettura", every adapter loaded
  * in GPU memory). Pointer tables are read on the device at every call, so
  * weights can be updated in place, or re-pointed, between calls without any
  * other call (same rank).
@@ -100,7 +100,7 @@ typedef struct lora_adapters_t {
  * A token batch in sorted-position order, cut into segments that each use
  * one adapter (a segment is a run of positions [seg_starts[g],
  * seg_starts[g+1])). Several segments may use the same adapter (packed
- * sequences, PLoRA summary "Kernelontwerp"); their tokens are summed
+ * sequences, "Technische Samenvatting: PLoRA" (gist.science) "Kernelontwerp"); their tokens are summed
  * together in dA_i / dB_i.
  */
 typedef struct lora_segments_t {
@@ -109,7 +109,9 @@ typedef struct lora_segments_t {
   const int32_t* seg_starts;  /* HOST [S+1]: [0] = 0, non-decreasing, [S] = T */
   const int32_t* seg_adapter; /* HOST [S]: -1 (no adapter) or 0..N-1 */
   const int32_t* token_rows;  /* DEVICE [T] or NULL: row of x/y/dx/dy used by position p.
-                                 Rows must be distinct for the writing calls. */
+                                 Rows must be distinct for the writing calls, and
+                                 row * ld * 2 bytes must stay below 2 GiB (rows past
+                                 that read as zero and are not written). */
 } lora_segments_t;
 
 /*
@@ -152,7 +154,7 @@ int lora_sgmv_expand(const float* u, int64_t ldu, const lora_adapters_t* adapter
 
 /*
  * Fused shrink + expand in ONE kernel launch for all adapters of the batch
- * (C-LoRA announcement, "Come funziona l'architettura"):
+ * ("Trajectory presenta C-LoRA" (vivodigitale.it), "Come funziona l'architettura"):
  * y[row(p)] += s_i B_i (A_i x[row(p)]). If u_save is not NULL the fp32
  * intermediate u is also written there (for a later backward), ldu >= max
  * rank used. x and y must not overlap.
@@ -162,7 +164,7 @@ int lora_sgmv_fused(const void* x, int64_t ldx, const lora_adapters_t* adapters,
                     int64_t ldu, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Packed backward over all adapters of the batch (PLoRA summary, "LoRA
+ * Packed backward over all adapters of the batch ("Technische Samenvatting: PLoRA" (gist.science), "LoRA
  * Execution Engine": forward and backward cases tiled along the sequence or
  * hidden dimension):
  *   du[p]  = s_i B_i^T dy[row(p)]                          (kept in the workspace)

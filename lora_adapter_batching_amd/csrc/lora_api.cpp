@@ -47,7 +47,7 @@ constexpr int kMaxKs = 16;            // largest split of the shrink reduction
 constexpr int kMaxPartials = 512;     // tiles * ks in split modes (bounds the workspace)
 constexpr int kMaxDepTiles = 1024 - kCtrTiles;  // counter slots
 constexpr size_t kCounterBytes = 4096;
-constexpr int kMinKChunk = 256;       // smallest k-chunk of a split shrink
+constexpr int kShrinkChunk = 1280;    // k elements per item of a split shrink
 constexpr int kMaxSlots = kMaxJobs;   // adapters per backward group
 
 struct DeviceInfo {
@@ -269,6 +269,16 @@ ForcePlan force_plan() {
   return f;
 }
 
+// XCD-aware item order for the on-chip fused mode (LORA_SGMV_XCD=1 enables;
+// measured slower on the packed-training shapes, so off by default).
+bool xcd_remap_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("LORA_SGMV_XCD");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
 int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int>& slot_of,
             hipStream_t stream) {
   if (segs.empty()) return LORA_OK;
@@ -302,26 +312,29 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
     P.n_seg = ns;
     P.n_tiles = tiles;
     const int nblocks = cdiv(c.N, 32);
-    const int target = 2 * cus;
-    auto choose_ks = [&]() {
+    const int slots = 2 * cus;  // resident workgroups at the kernels' occupancy
+    // split of the shrink reduction: none when the tiles alone fill the GPU,
+    // otherwise chunks of about kShrinkChunk elements
+    auto choose_ks = [&](bool for_fused) {
       int ks = 1;
-      if (tiles < cus) ks = cdiv(target, tiles);
-      ks = std::min({ks, kMaxKs, std::max(1, c.K / kMinKChunk), std::max(1, kMaxPartials / tiles)});
+      if (tiles < (for_fused ? cus / 4 : cus)) ks = cdiv(c.K, kShrinkChunk);
+      ks = std::min({ks, kMaxKs, std::max(1, kMaxPartials / tiles)});
       ks = std::max(ks, 1);
-      const int kchunk = round_up(cdiv(c.K, ks), 64);
-      P.kchunk = kchunk;
-      P.ks = cdiv(c.K, kchunk);
+      P.kchunk = round_up(cdiv(c.K, ks), 64);
+      P.ks = cdiv(c.K, P.kchunk);
     };
+    // column chunks per tile: enough items for about two per resident slot,
+    // at least one 32-column block per wave
     auto choose_nc = [&]() {
-      int nc = std::max(1, cdiv(target, tiles));
-      nc = std::min(nc, std::max(1, nblocks / 4));  // at least one block per wave
+      int nc = std::max(1, cdiv(2 * slots, tiles));
+      nc = std::min(nc, std::max(1, nblocks / 4));
       P.nblk = cdiv(nblocks, nc);
       P.nc = cdiv(nblocks, P.nblk);
     };
     P.spin_ticks = (int)std::min<int64_t>((int64_t)dev.wall_khz * 1000 / 5000, 1 << 30);  // 200 us
     if (c.mode_op == LORA_OP_SHRINK) {
       P.mode = kModeShrink;
-      choose_ks();
+      choose_ks(false);
       if (P.ks > 1 && tiles > kMaxDepTiles) { P.ks = 1; P.kchunk = round_up(c.K, 64); }
       P.n_items_a = tiles * P.ks;
       P.grid = P.n_items_a;
@@ -349,19 +362,23 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
         P.n_items_a = tiles * P.ks;
         P.n_items_b = tiles * P.nc;
         P.grid = P.n_items_a + P.n_items_b;
-      } else if (tiles >= cus / 2 || tiles > kMaxDepTiles) {
+      } else if (tiles >= slots || tiles > std::min(kMaxDepTiles, kMaxPartials)) {
+        // the tiles alone fill every resident slot: keep u on chip. Workgroup
+        // b runs on XCD b % 8; consecutive tiles (one adapter's) are mapped to
+        // the same XCD so that its weights stay in that XCD's L2
         P.mode = kModeFusedTile;
         P.ks = 1;
         P.kchunk = round_up(c.K, 64);
-        int nc = std::max(1, cus / tiles);
-        nc = std::min(nc, std::max(1, nblocks / 4));
-        P.nblk = cdiv(nblocks, nc);
-        P.nc = cdiv(nblocks, P.nblk);
-        P.n_items_a = tiles * P.nc;
-        P.grid = P.n_items_a;
+        P.nc = 1;
+        P.nblk = nblocks;
+        P.n_items_a = tiles;
+        P.xcd_remap = xcd_remap_enabled() ? 1 : 0;
+        P.grid = P.xcd_remap ? round_up(tiles, 8) : tiles;
       } else {
+        // fewer tiles than slots: shrink items (split along k when few) and
+        // finer expand items that wait for their tile, so all CUs stay busy
         P.mode = kModeFusedDep;
-        choose_ks();
+        choose_ks(true);
         choose_nc();
         P.n_items_a = tiles * P.ks;
         P.n_items_b = tiles * P.nc;

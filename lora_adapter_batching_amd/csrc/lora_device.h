@@ -36,11 +36,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mk_rsrc(const void* base, int6
   void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
   return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, kRsrcWord3);
 }
-__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+// kNT marks an access non-temporal (data streamed once: activations and
+// outputs), so that it does not displace reused adapter weights from L2.
+constexpr int kNT = 2;
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off, int aux = 0) {
+  return aux ? __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNT)
+             : __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
-__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v, int aux = 0) {
+  if (aux)
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kNT);
+  else
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
 }
 __device__ __forceinline__ uint32_t bld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);

@@ -37,7 +37,8 @@ struct TileInfo {
 // table: thread i checks segment i and the matching thread publishes the
 // tile's description in LDS (a binary search would chain several dependent
 // loads of the kernel-argument table).
-__device__ __forceinline__ TileInfo tile_info(const FwdPlan& P, int g, TileInfo* lds) {
+template <typename PT>
+__device__ __forceinline__ TileInfo tile_info(const PT& P, int g, TileInfo* lds) {
   const int i = threadIdx.x;
   if (i < P.n_seg) {
     const int t0 = P.seg_tile0[i];
@@ -70,17 +71,20 @@ __device__ __forceinline__ TileInfo tile_info(const FwdPlan& P, int g, TileInfo*
   return t;
 }
 
-__device__ __forceinline__ const uint16_t* w_ptr(const FwdPlan& P, const TileInfo& t) {
+template <typename PT>
+__device__ __forceinline__ const uint16_t* w_ptr(const PT& P, const TileInfo& t) {
   if (P.Wtab) return reinterpret_cast<const uint16_t*>(P.Wtab[t.adapter]);
   return P.Wslots + (int64_t)t.slot * P.w_slot_elems;
 }
-__device__ __forceinline__ const uint16_t* v_ptr(const FwdPlan& P, const TileInfo& t) {
+template <typename PT>
+__device__ __forceinline__ const uint16_t* v_ptr(const PT& P, const TileInfo& t) {
   if (P.Vtab) return reinterpret_cast<const uint16_t*>(P.Vtab[t.adapter]);
   return P.Vslots + (int64_t)t.slot * P.v_slot_elems;
 }
 
 // Row of X / Y used by sorted position p.
-__device__ __forceinline__ int64_t token_row(const FwdPlan& P, int p) {
+template <typename PT>
+__device__ __forceinline__ int64_t token_row(const PT& P, int p) {
   return P.token_rows ? (int64_t)P.token_rows[p] : (int64_t)p;
 }
 
@@ -228,10 +232,13 @@ __device__ __forceinline__ void exp_load(const ExpArgs& a, int cb, int lane, Exp
   B.cb = cb;
   const int col0 = cb * 32;
   const uint32_t vrow = (uint32_t)((int64_t)(col0 + colmap(m)) * a.ldv * 2);  // rows >= ncols: outside
+  const int kbn = (a.rank + 15) >> 4;  // k-steps of 16 that hold rank columns (uniform)
 #pragma unroll
   for (int kb = 0; kb < 2 * RB; ++kb) {
     const int k = 16 * kb + 8 * h;
-    if (a.vec16) {
+    if (kb >= kbn) {
+      B.vf[kb] = zero16();  // never used by the MFMAs: no load issued
+    } else if (a.vec16) {
       B.vf[kb] = bld16(a.vr, k < a.rank ? vrow + 2u * k : kOff);
     } else {
       uint32_t w[4];
@@ -404,7 +411,8 @@ struct Smem {
 
 // X rows of the tile as a buffer resource: based at the tile's first row when
 // rows are contiguous, at X itself for a token_rows gather.
-__device__ __forceinline__ void tile_rows(const uint16_t* base, int64_t ld, int width, const FwdPlan& P,
+template <typename PT>
+__device__ __forceinline__ void tile_rows(const uint16_t* base, int64_t ld, int width, const PT& P,
                                           const TileInfo& t, __amdgpu_buffer_rsrc_t& r, uint32_t& off) {
   const int n = threadIdx.x & 31;
   const bool valid = n < t.cnt;
@@ -417,8 +425,8 @@ __device__ __forceinline__ void tile_rows(const uint16_t* base, int64_t ld, int 
   }
 }
 
-template <int RB>
-__device__ __forceinline__ void shrink_range(const FwdPlan& P, const TileInfo& t, int kb, int ke,
+template <int RB, typename PT>
+__device__ __forceinline__ void shrink_range(const PT& P, const TileInfo& t, int kb, int ke,
                                              int wave, int lane, f32x16 (&acc)[RB]) {
   __amdgpu_buffer_rsrc_t xr;
   uint32_t xoff;
@@ -429,7 +437,8 @@ __device__ __forceinline__ void shrink_range(const FwdPlan& P, const TileInfo& t
 }
 
 // Writes Pl rows 0..31, columns < 32*RB (zero where rank/token invalid) to U.
-__device__ __forceinline__ void store_u_from_lds(const FwdPlan& P, const TileInfo& t,
+template <typename PT>
+__device__ __forceinline__ void store_u_from_lds(const PT& P, const TileInfo& t,
                                                  const float* Pl) {
   for (int e = threadIdx.x; e < kTileM * t.rank; e += kThreads) {
     const int n = e / t.rank, k = e - n * t.rank;
@@ -437,7 +446,8 @@ __device__ __forceinline__ void store_u_from_lds(const FwdPlan& P, const TileInf
   }
 }
 
-__device__ __forceinline__ ExpArgs exp_args(const FwdPlan& P, const TileInfo& t) {
+template <typename PT>
+__device__ __forceinline__ ExpArgs exp_args(const PT& P, const TileInfo& t) {
   ExpArgs a;
   tile_rows(P.Y, P.ldy, P.N, P, t, a.yr, a.yoff);
   a.ldv = ((t.rank + P.v_round - 1) / P.v_round) * P.v_round;
@@ -450,14 +460,15 @@ __device__ __forceinline__ ExpArgs exp_args(const FwdPlan& P, const TileInfo& t)
 }
 
 // Column-block range of n-chunk c: this wave starts at cb0 + wave.
-__device__ __forceinline__ void chunk_blocks(const FwdPlan& P, int c, int& cb0, int& cb_end) {
+template <typename PT>
+__device__ __forceinline__ void chunk_blocks(const PT& P, int c, int& cb0, int& cb_end) {
   const int nblocks = (P.N + 31) >> 5;
   cb0 = c * P.nblk;
   cb_end = min(nblocks, cb0 + P.nblk);
 }
 
-template <int RB>
-__device__ __forceinline__ void expand_tile_from_lds(const FwdPlan& P, const TileInfo& t, int c,
+template <int RB, typename PT>
+__device__ __forceinline__ void expand_tile_from_lds(const PT& P, const TileInfo& t, int c,
                                                      const float* Pl, int wave, int lane) {
   const ExpArgs a = exp_args(P, t);
   int cb0, cb_end;
@@ -470,8 +481,8 @@ __device__ __forceinline__ void expand_tile_from_lds(const FwdPlan& P, const Til
 }
 
 // kModeFusedTile: full shrink of one tile on chip, then its n-chunk c.
-template <int RB>
-__device__ __forceinline__ void item_fused_tile(const FwdPlan& P, Smem& S, const TileInfo& t, int c) {
+template <int RB, typename PT>
+__device__ __forceinline__ void item_fused_tile(const PT& P, Smem& S, const TileInfo& t, int c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   f32x16 acc[RB];
   shrink_range<RB>(P, t, 0, P.K, wave, lane, acc);
@@ -483,8 +494,8 @@ __device__ __forceinline__ void item_fused_tile(const FwdPlan& P, Smem& S, const
 }
 
 // kModeExpand: U from memory, expand n-chunk c.
-template <int RB>
-__device__ __forceinline__ void item_expand(const FwdPlan& P, Smem& S, const TileInfo& t, int c) {
+template <int RB, typename PT>
+__device__ __forceinline__ void item_expand(const PT& P, Smem& S, const TileInfo& t, int c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float* Pl = S.Pl;
   for (int e = threadIdx.x; e < kTileM * 32 * RB; e += kThreads) {
@@ -495,13 +506,14 @@ __device__ __forceinline__ void item_expand(const FwdPlan& P, Smem& S, const Til
   expand_tile_from_lds<RB>(P, t, c, Pl, wave, lane);
 }
 
-__device__ __forceinline__ float* partial_ptr(const FwdPlan& P, int g, int c) {
+template <typename PT>
+__device__ __forceinline__ float* partial_ptr(const PT& P, int g, int c) {
   return P.partials + ((int64_t)g * P.ks + c) * kTileM * P.rpad;
 }
 
 // kModeShrink / kModeFusedDep phase A: shrink over k-chunk c.
-template <int RB>
-__device__ __forceinline__ void item_shrink(const FwdPlan& P, Smem& S, const TileInfo& t, int c) {
+template <int RB, typename PT>
+__device__ __forceinline__ void item_shrink(const PT& P, Smem& S, const TileInfo& t, int c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kb = c * P.kchunk;
   const int ke = min(P.K, kb + P.kchunk);
@@ -548,8 +560,8 @@ __device__ __forceinline__ void item_shrink(const FwdPlan& P, Smem& S, const Til
 // If the chunks do not arrive within spin_ticks (e.g. their workgroups are
 // not resident), the item computes the same chunks itself in the same order,
 // so the result is identical and no wait is unbounded.
-template <int RB>
-__device__ __forceinline__ void item_expand_wait(const FwdPlan& P, Smem& S, const TileInfo& t, int c) {
+template <int RB, typename PT>
+__device__ __forceinline__ void item_expand_wait(const PT& P, Smem& S, const TileInfo& t, int c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int* ctr = P.counters + kCtrTiles + t.g;
   // the y rows and expand weights do not depend on the shrink: load the
@@ -606,8 +618,8 @@ __device__ __forceinline__ void item_expand_wait(const FwdPlan& P, Smem& S, cons
   exp_ring_run<RB>(ea, F, cb0 + wave, cb_end, lane, R);
 }
 
-template <int RB>
-__device__ __forceinline__ void run_item(const FwdPlan& P, Smem& S, const TileInfo& t, int kind, int c) {
+template <int RB, typename PT>
+__device__ __forceinline__ void run_item(const PT& P, Smem& S, const TileInfo& t, int kind, int c) {
   switch (kind) {
     case 0: item_shrink<RB>(P, S, t, c); break;
     case 1: item_expand<RB>(P, S, t, c); break;
@@ -616,8 +628,8 @@ __device__ __forceinline__ void run_item(const FwdPlan& P, Smem& S, const TileIn
   }
 }
 
-template <int RBMAX>
-__global__ __launch_bounds__(kThreads) void sgmv_fwd_kernel(FwdPlan P) {
+template <int RBMAX, typename PT>
+__global__ __launch_bounds__(kThreads) void sgmv_fwd_kernel(PT P) {
   __shared__ Smem S;
   const int b = blockIdx.x;
   int item = -1, kind = 0, per = 1;
@@ -658,14 +670,35 @@ __global__ __launch_bounds__(kThreads) void sgmv_fwd_kernel(FwdPlan P) {
   }
 }
 
-hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream) {
+template <typename PT>
+static hipError_t launch_fwd_t(const PT& P, int rbmax, hipStream_t stream) {
   if (rbmax <= 1)
-    hipLaunchKernelGGL(sgmv_fwd_kernel<1>, dim3(P.grid), dim3(kThreads), 0, stream, P);
+    hipLaunchKernelGGL((sgmv_fwd_kernel<1, PT>), dim3(P.grid), dim3(kThreads), 0, stream, P);
   else if (rbmax == 2)
-    hipLaunchKernelGGL(sgmv_fwd_kernel<2>, dim3(P.grid), dim3(kThreads), 0, stream, P);
+    hipLaunchKernelGGL((sgmv_fwd_kernel<2, PT>), dim3(P.grid), dim3(kThreads), 0, stream, P);
   else
-    hipLaunchKernelGGL(sgmv_fwd_kernel<4>, dim3(P.grid), dim3(kThreads), 0, stream, P);
+    hipLaunchKernelGGL((sgmv_fwd_kernel<4, PT>), dim3(P.grid), dim3(kThreads), 0, stream, P);
   return hipGetLastError();
+}
+
+// Launches with the smallest plan type that holds the segments: the plan is
+// the kernel argument, and its size is part of every launch's host cost.
+hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream) {
+  if (P.n_seg <= kSmallSeg) {
+    FwdPlanT<kSmallSeg> Q;
+    static_cast<FwdHeader&>(Q) = static_cast<const FwdHeader&>(P);
+    for (int i = 0; i < P.n_seg; ++i) {
+      Q.seg_tok0[i] = P.seg_tok0[i];
+      Q.seg_ntok[i] = P.seg_ntok[i];
+      Q.seg_tile0[i] = P.seg_tile0[i];
+      Q.seg_adapter[i] = P.seg_adapter[i];
+      Q.seg_scale[i] = P.seg_scale[i];
+      Q.seg_rank[i] = P.seg_rank[i];
+      Q.seg_slot[i] = P.seg_slot[i];
+    }
+    return launch_fwd_t(Q, rbmax, stream);
+  }
+  return launch_fwd_t(P, rbmax, stream);
 }
 
 }  // namespace lora

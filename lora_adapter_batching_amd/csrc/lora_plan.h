@@ -28,7 +28,7 @@ enum FwdMode : int32_t {
 constexpr int kCtrDone = 0;      // workgroups finished (kModeFusedDep)
 constexpr int kCtrTiles = 64;    // per-tile arrival counters start here
 
-struct FwdPlan {
+struct FwdHeader {
   const uint16_t* X;  // shrink input rows, bf16 (x forward, dy backward)
   int64_t ldx;
   uint16_t* Y;  // expand in/out rows, bf16 (y forward, dx backward)
@@ -62,14 +62,21 @@ struct FwdPlan {
   int32_t xcd_remap;    // 1: map consecutive items of phase A to the same XCD
   int32_t grid;         // launched workgroups
   int32_t spin_ticks;   // wall-clock ticks an expand waits before computing the shrink itself
-  int32_t seg_tok0[kMaxSeg];
-  int32_t seg_ntok[kMaxSeg];
-  int32_t seg_tile0[kMaxSeg];
-  int32_t seg_adapter[kMaxSeg];
-  float seg_scale[kMaxSeg];
-  uint8_t seg_rank[kMaxSeg];
-  uint8_t seg_slot[kMaxSeg];
 };
+
+// Segment table of a launch (struct of arrays), CAP entries.
+template <int CAP>
+struct FwdPlanT : FwdHeader {
+  int32_t seg_tok0[CAP];
+  int32_t seg_ntok[CAP];
+  int32_t seg_tile0[CAP];
+  int32_t seg_adapter[CAP];
+  float seg_scale[CAP];
+  uint8_t seg_rank[CAP];
+  uint8_t seg_slot[CAP];
+};
+constexpr int kSmallSeg = 16;  // capacity of the small plan (decode batches)
+using FwdPlan = FwdPlanT<kMaxSeg>;
 
 // Weight-gradient launch: items are (job, kind, column chunk); a job is one
 // adapter (or part of its segments) whose token reduction the item owns.

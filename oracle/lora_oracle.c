@@ -18,16 +18,16 @@
  *             dA_i =       sum_{t: a(t)=i} du_t x_t^T
  *
  * Sources. LoRA keeps the base model frozen and trains small adapter weights
- * with a rank and a scaling factor (C-LoRA announcement, "Cos'e C-LoRA e
- * perche serve"; PLoRA summary, "Resultaten", search space of rank and scaling
+ * with a rank and a scaling factor ("Trajectory presenta C-LoRA" (vivodigitale.it), "Cos'e C-LoRA e
+ * perche serve"; "Technische Samenvatting: PLoRA" (gist.science), "Resultaten", search space of rank and scaling
  * factor). A decode batch mixes tokens of many resident adapters and one
  * kernel launch covers the per-adapter matrix-vector work of the whole batch
- * (C-LoRA announcement, "Come funziona l'architettura"). Packed training runs
+ * ("Trajectory presenta C-LoRA" (vivodigitale.it), "Come funziona l'architettura"). Packed training runs
  * the forward and backward of many adapters together over concatenated LoRA
- * tensors (PLoRA summary, "LoRA Execution Engine", "Packed LoRA Kernels" and
+ * tensors ("Technische Samenvatting: PLoRA" (gist.science), "LoRA Execution Engine", "Packed LoRA Kernels" and
  * "Kernelontwerp"). The pages print no formula; the forward above is the
  * standard low-rank update written per token, and the backward is its chain
- * rule. Gradients are fp32 buffers on the GPU side (C-LoRA announcement,
+ * rule. Gradients are fp32 buffers on the GPU side ("Trajectory presenta C-LoRA" (vivodigitale.it),
  * "Come funziona l'architettura": gradient buffers in the AdapterStore); here
  * everything is fp64.
  *

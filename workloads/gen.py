@@ -6,8 +6,8 @@ Nothing here computes the LoRA product: this module only decides shapes,
 adapter ids, segment lengths, ranks, scales and random values.
 
 Workload shapes follow the multi-adapter serving and packed-training settings
-described in the C-LoRA announcement ("Come funziona l'architettura": decode
-batches that mix tokens of many resident adapters) and the PLoRA summary
+described in the "Trajectory presenta C-LoRA" (vivodigitale.it) ("Come funziona l'architettura": decode
+batches that mix tokens of many resident adapters) and the "Technische Samenvatting: PLoRA" (gist.science)
 ("LoRA Execution Engine": many heterogeneous adapters fine-tuned in one packed
 job, up to 32 adapters per job, ranks and scaling factors varied across a
 hyper-parameter search).

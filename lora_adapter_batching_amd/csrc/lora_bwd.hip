@@ -5,8 +5,8 @@
 //   dB_i[j][k] = s_i sum_t dy[t][j] u[t][k],   dA_i[k][d] = sum_t du[t][k] x[t][d].
 // Each workgroup owns a block of hidden columns of one adapter's gradient and
 // walks all of that adapter's tokens, so the reduction is deterministic and
-// needs no atomics; tiles follow the hidden dimension, not the rank (PLoRA
-// summary, "Kernelontwerp").
+// needs no atomics; tiles follow the hidden dimension, not the rank
+// ("Technische Samenvatting: PLoRA" (gist.science), "Kernelontwerp").
 #include "lora_device.h"
 #include "lora_plan.h"
 

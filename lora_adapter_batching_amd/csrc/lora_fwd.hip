@@ -1,21 +1,22 @@
 // lora_fwd.hip -- shrink / expand / fused multi-adapter LoRA kernels for gfx950.
 //
 // Method: every token of a batch carries an adapter; the batch is cut into
-// segments of one adapter each and a single launch covers all of them (C-LoRA
-// announcement, "Come funziona l'architettura"). Work is tiled along the
-// token (sequence) and hidden dimensions, never along the small rank (PLoRA
-// summary, "Kernelontwerp"). The same kernel serves the backward du/dx pass
-// with dy in place of x, B^T in place of A and A^T in place of B.
+// segments of one adapter each and a single launch covers all of them
+// ("Trajectory presenta C-LoRA" (vivodigitale.it), "Come funziona
+// l'architettura"). Work is tiled along the token (sequence) and hidden
+// dimensions, never along the small rank ("Technische Samenvatting: PLoRA"
+// (gist.science), "Kernelontwerp"). The same kernel serves the backward du/dx
+// pass with dy in place of x, B^T in place of A and A^T in place of B.
 //
-// Shapes handled by one workgroup (4 wave64):
-//  shrink  P^T[rank 32b..32b+31][token 0..31] += W[rank][k] * X[token][k]
-//          32x32x16 bf16 MFMA; both operands are read straight from global
-//          memory with 16-byte loads (8 consecutive k per lane); the 4 waves
-//          split k and are summed in LDS in a fixed order.
-//  expand  Y^T[col][token] += V[col][rank] * P^T[rank][token]
-//          32x32x16 bf16 MFMA; P (fp32) enters as a bf16 hi + lo pair; rows
-//          of each 32-column block are permuted (colmap) so that every lane
-//          owns two runs of 8 contiguous bf16 of one token row of Y.
+// One workgroup (4 wave64) owns a tile of 32 tokens of one segment:
+//  shrink  P^T[rank][token] += W[rank][k] * X[token][k]
+//  expand  Y^T[col][token]  += V[col][rank] * P^T[rank][token]
+// both on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; fp32 P enters the
+// expand as a bf16 hi + lo pair. Global memory is touched only with
+// row-contiguous 16-byte accesses (consecutive lanes take consecutive 16
+// bytes of a row): chunks of X, W, y and V are staged through padded LDS rows
+// and the MFMA operands are read from LDS. The next chunk's global loads are
+// issued before the current chunk is computed.
 #include "lora_device.h"
 #include "lora_plan.h"
 
@@ -82,62 +83,190 @@ __device__ __forceinline__ const uint16_t* v_ptr(const PT& P, const TileInfo& t)
   return P.Vslots + (int64_t)t.slot * P.v_slot_elems;
 }
 
-// Row of X / Y used by sorted position p.
+// Workgroup barrier for LDS hand-offs between waves. Global loads that are in
+// flight across it belong to the calling wave only and are waited for where
+// their registers are used.
+__device__ __forceinline__ void lds_sync() { __syncthreads(); }
+
+// ---------------------------------------------------------------------------
+// Chunk geometry for RB 32-row rank blocks (rank <= 32 * RB).
+// ---------------------------------------------------------------------------
+template <int RB>
+struct Geo {
+  static constexpr int KC = RB == 1 ? 256 : 128;           // shrink k-chunk (elements)
+  static constexpr int KCP = KC + 8;                       // LDS row of X / W (elements)
+  static constexpr int CW = RB == 1 ? 256 : 128;           // expand column chunk
+  static constexpr int CWP = CW + 8;                       // LDS row of y (elements)
+  static constexpr int RP = 32 * RB + 8;                   // LDS row of V (elements)
+  static constexpr int XV = (32 * KC / 8) / kThreads;      // X vectors per thread
+  static constexpr int WV = (32 * RB * KC / 8) / kThreads; // W vectors per thread
+  static constexpr int YV = (32 * CW / 8) / kThreads;      // y vectors per thread
+  static constexpr int VV = (CW * 4 * RB) / kThreads;      // V vectors per thread (at most)
+  static constexpr int SHRINK_BYTES = (32 + 32 * RB) * KCP * 2;
+  static constexpr int EXPAND_BYTES = 32 * CWP * 2 + CW * RP * 2;
+  static constexpr int STAGE_BYTES = SHRINK_BYTES > EXPAND_BYTES ? SHRINK_BYTES : EXPAND_BYTES;
+};
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int kRedBytes = 4 * 16 * 64 * 4;  // wave-reduction buffer
+template <int RBMAX>
+struct StageBytes {
+  static constexpr int v = cmax(cmax(Geo<1>::STAGE_BYTES, RBMAX >= 2 ? Geo<2>::STAGE_BYTES : 0),
+                                cmax(RBMAX >= 4 ? Geo<4>::STAGE_BYTES : 0, kRedBytes));
+};
+
+template <int RBMAX>
+struct Smem {
+  alignas(16) uint8_t stage[StageBytes<RBMAX>::v];  // staged chunks, or the reduction buffer
+  alignas(16) float Pl[kTileM * kLdp];              // the tile's P (fp32)
+  TileInfo ti;
+  int flag;
+};
+
+// Rows of a tile as a buffer resource: based at the tile's first row when
+// rows are contiguous, at the matrix itself for a token_rows gather.
+struct TileRows {
+  __amdgpu_buffer_rsrc_t r;
+  int64_t ld2;  // row stride in bytes
+  bool gather;
+};
 template <typename PT>
-__device__ __forceinline__ int64_t token_row(const PT& P, int p) {
-  return P.token_rows ? (int64_t)P.token_rows[p] : (int64_t)p;
+__device__ __forceinline__ TileRows tile_rows(const uint16_t* base, int64_t ld, int width, const PT& P,
+                                              const TileInfo& t) {
+  TileRows tr;
+  tr.gather = P.token_rows != nullptr;
+  tr.ld2 = ld * 2;
+  if (tr.gather)
+    tr.r = mk_rsrc(base, (int64_t)0x7ffffff0);
+  else
+    tr.r = mk_rsrc(base + (int64_t)t.p0 * ld, ((int64_t)(t.cnt - 1) * ld + width) * 2);
+  return tr;
+}
+// Byte offset of tile row n in the resource (kOff if not a valid token).
+template <typename PT>
+__device__ __forceinline__ uint32_t row_off(const PT& P, const TileInfo& t, const TileRows& tr, int n) {
+  if (n >= t.cnt) return kOff;
+  const int64_t row = tr.gather ? (int64_t)P.token_rows[t.p0 + n] : (int64_t)n;
+  return (uint32_t)(row * tr.ld2);
 }
 
 // ---------------------------------------------------------------------------
-// Shrink: acc[b] (rows = rank 32b.., cols = this lane's token) over k in [kb, ke)
+// Shrink over k in [kb, ke). Chunk j of the loop covers KC columns of the 32
+// X rows of the tile and of the 32*RB W rows; thread t moves the 16-byte
+// vectors t, t + 256, ... of the chunk (row-major), so a wave reads whole row
+// runs. Rows past the tile or the rank read as zero. The 4 waves split each
+// chunk's k-steps; acc[b] holds P^T rows 32b.. of the wave's partial sum.
 // ---------------------------------------------------------------------------
-// Ring depth of the shrink loop (k-steps of 16 whose loads are in flight).
 template <int RB>
-struct ShrinkDepth {
-  static constexpr int v = RB == 1 ? 8 : (RB == 2 ? 6 : 4);
+struct ShrinkRegs {
+  u32x4 x[Geo<RB>::XV];
+  u32x4 w[Geo<RB>::WV];
 };
-// xr: resource over the tile's X rows; xoff: byte offset of this lane's token
-// row (kOff if the token is not valid). W rows of rank >= rank fall outside
-// the W resource and read as zero.
+
 template <int RB>
-__device__ __forceinline__ void shrink_acc(__amdgpu_buffer_rsrc_t xr, uint32_t xoff, const uint16_t* W,
-                                           int64_t ldw, int rank, int kb, int ke, int wave,
-                                           int lane, f32x16 (&acc)[RB]) {
-  constexpr int DS = ShrinkDepth<RB>::v;
+struct ShrinkCtx {
+  __amdgpu_buffer_rsrc_t xr, wr;
+  uint32_t xoff[Geo<RB>::XV];  // byte offset of this thread's X rows
+  uint32_t woff[Geo<RB>::WV];  // byte offset of this thread's W rows
+  int kb, ke;
+};
+
+template <int RB>
+__device__ __forceinline__ void shrink_load(const ShrinkCtx<RB>& C, int chunk, ShrinkRegs<RB>& R) {
+  using G = Geo<RB>;
+  constexpr int VPR = G::KC / 8;  // vectors per row of a chunk
+  const int k = C.kb + chunk * G::KC + 8 * (threadIdx.x % VPR);  // same column for every j
+  const bool kv = k < C.ke;
+  const uint32_t kbytes = 2u * (uint32_t)k;
+#pragma unroll
+  for (int j = 0; j < G::XV; ++j) R.x[j] = bld16(C.xr, kv ? C.xoff[j] + kbytes : kOff);
+#pragma unroll
+  for (int j = 0; j < G::WV; ++j) R.w[j] = bld16(C.wr, kv ? C.woff[j] + kbytes : kOff);
+}
+
+template <int RB>
+__device__ __forceinline__ void shrink_to_lds(const ShrinkRegs<RB>& R, uint16_t* xs, uint16_t* ws) {
+  using G = Geo<RB>;
+  constexpr int VPR = G::KC / 8;
+  constexpr int RPJ = kThreads / VPR;  // rows per j
+  const int r0 = threadIdx.x / VPR, c = 8 * (threadIdx.x % VPR);
+#pragma unroll
+  for (int j = 0; j < G::XV; ++j) st16(xs + (r0 + RPJ * j) * G::KCP + c, R.x[j]);
+#pragma unroll
+  for (int j = 0; j < G::WV; ++j) st16(ws + (r0 + RPJ * j) * G::KCP + c, R.w[j]);
+}
+
+template <int RB>
+__device__ __forceinline__ void shrink_mfma(const uint16_t* xs, const uint16_t* ws, int wave, int lane,
+                                            f32x16 (&acc)[RB]) {
+  using G = Geo<RB>;
+  constexpr int SPW = G::KC / 64;  // k-steps of 16 per wave per chunk
   const int h = lane >> 5, m = lane & 31;
-  const __amdgpu_buffer_rsrc_t wr = mk_rsrc(W, (int64_t)rank * ldw * 2);
-  uint32_t woff[RB];
 #pragma unroll
-  for (int b = 0; b < RB; ++b) woff[b] = (uint32_t)((int64_t)(32 * b + m) * ldw * 2);
-  // each wave takes a contiguous quarter of [kb, ke) (multiple of 16 long)
-  const int q = ((ke - kb + 63) >> 6) << 4;
-  const int kw0 = __builtin_amdgcn_readfirstlane(kb + wave * q);
-  const int kw1 = __builtin_amdgcn_readfirstlane(min(ke, kw0 + q));
-  const int nsteps = __builtin_amdgcn_readfirstlane(kw1 > kw0 ? (kw1 - kw0 + 15) >> 4 : 0);
-  u32x4 xf[DS], wf[RB][DS];
-  auto load = [&](int j, int s) {
-    const int k = kw0 + 16 * j + 8 * h;
-    const bool kv = j < nsteps && k < kw1;
-    xf[s] = bld16(xr, kv ? xoff + 2u * (uint32_t)k : kOff);
+  for (int s = 0; s < SPW; ++s) {
+    const int k = 16 * (wave * SPW + s) + 8 * h;
+    const u32x4 xf = ld16(xs + m * G::KCP + k);
 #pragma unroll
-    for (int b = 0; b < RB; ++b) wf[b][s] = bld16(wr, kv ? woff[b] + 2u * (uint32_t)k : kOff);
-  };
-  // ring: DS k-steps of loads stay in flight while earlier ones are consumed
-#pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    load(s, s);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int j0 = 0; j0 < nsteps; j0 += DS) {
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-#pragma unroll
-      for (int b = 0; b < RB; ++b) acc[b] = mfma32(as_bf16x8(wf[b][s]), as_bf16x8(xf[s]), acc[b]);
-      load(j0 + s + DS, s);
-      // keep slot order: the refill of slot s is issued before slot s+1 is
-      // consumed, so only slot s+1's own loads need to have arrived
-      __builtin_amdgcn_sched_barrier(0);
+    for (int b = 0; b < RB; ++b) {
+      const u32x4 wf = ld16(ws + (32 * b + m) * G::KCP + k);
+      acc[b] = mfma32(as_bf16x8(wf), as_bf16x8(xf), acc[b]);
     }
+  }
+}
+
+template <int RB, typename PT>
+__device__ __forceinline__ void shrink_lds(const PT& P, const TileInfo& t, int kb, int ke, uint8_t* stage,
+                                           f32x16 (&acc)[RB]) {
+  using G = Geo<RB>;
+  constexpr int VPR = G::KC / 8;
+  constexpr int RPJ = kThreads / VPR;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = threadIdx.x / VPR;
+  ShrinkCtx<RB> C;
+  const TileRows xt = tile_rows(P.X, P.ldx, P.K, P, t);
+  C.xr = xt.r;
+#pragma unroll
+  for (int j = 0; j < G::XV; ++j) C.xoff[j] = row_off(P, t, xt, r0 + RPJ * j);
+  const uint32_t ldw2 = 2u * (uint32_t)P.K;
+  C.wr = mk_rsrc(w_ptr(P, t), (int64_t)t.rank * ldw2);  // rows >= rank fall outside
+#pragma unroll
+  for (int j = 0; j < G::WV; ++j) C.woff[j] = (uint32_t)(r0 + RPJ * j) * ldw2;
+  C.kb = kb;
+  C.ke = ke;
+#pragma unroll
+  for (int b = 0; b < RB; ++b) acc[b] = zero_acc16();
+  uint16_t* xs = reinterpret_cast<uint16_t*>(stage);
+  uint16_t* ws = xs + 32 * G::KCP;
+  const int nch = __builtin_amdgcn_readfirstlane((ke - kb + G::KC - 1) / G::KC);
+  if (nch <= 0) return;
+  // Two register sets alternate: while chunk c is computed from LDS, the
+  // loads of chunks c+1 and c+2 are in flight. Loads past the last chunk
+  // fall outside the k range and read nothing.
+  ShrinkRegs<RB> R0, R1;
+  shrink_load<RB>(C, 0, R0);
+  shrink_load<RB>(C, 1, R1);
+  int c = 0;
+  for (; c + 2 < nch; c += 2) {
+    shrink_to_lds<RB>(R0, xs, ws);
+    lds_sync();
+    shrink_load<RB>(C, c + 2, R0);
+    shrink_mfma<RB>(xs, ws, wave, lane, acc);
+    lds_sync();
+    shrink_to_lds<RB>(R1, xs, ws);
+    lds_sync();
+    shrink_load<RB>(C, c + 3, R1);
+    shrink_mfma<RB>(xs, ws, wave, lane, acc);
+    lds_sync();
+  }
+  shrink_to_lds<RB>(R0, xs, ws);
+  lds_sync();
+  shrink_mfma<RB>(xs, ws, wave, lane, acc);
+  lds_sync();
+  if (c + 1 < nch) {
+    shrink_to_lds<RB>(R1, xs, ws);
+    lds_sync();
+    shrink_mfma<RB>(xs, ws, wave, lane, acc);
+    lds_sync();
   }
 }
 
@@ -151,7 +280,7 @@ __device__ __forceinline__ void reduce_waves(float* red, const f32x16 (&acc)[RB]
   for (int b = 0; b < RB; ++b) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) red[(wave * 16 + i) * 64 + lane] = acc[b][i];
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = tid + 256 * j;
@@ -163,7 +292,7 @@ __device__ __forceinline__ void reduce_waves(float* red, const f32x16 (&acc)[RB]
       const int mm = 8 * (i >> 2) + 4 * (ln >> 5) + (i & 3);
       out(32 * b + mm, ln & 31, s);
     }
-    __syncthreads();
+    lds_sync();
   }
 }
 
@@ -177,7 +306,7 @@ struct PFrags {
 };
 
 // B-operand fragments of P^T from the LDS tile Pl[token][k]: lane supplies
-// P[token = lane%32][16kb + 8(lane/32) + e].
+// P[token = lane%32][16kb + 8(lane/32) + e], zero for k >= rank.
 template <int RB>
 __device__ __forceinline__ void build_pfrags(const float* Pl, int rank, int lane, PFrags<RB>& F) {
   const int n = lane & 31, h = lane >> 5;
@@ -193,146 +322,186 @@ __device__ __forceinline__ void build_pfrags(const float* Pl, int rank, int lane
   }
 }
 
-// 8 bf16 of row `row` starting at k, zero beyond `rank`, for rows whose
-// stride is not a multiple of 8 elements.
-__device__ __forceinline__ u32x4 ld_partial(const uint16_t* row, int k, int rank) {
-  uint32_t w[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t a = (k + 2 * q < rank) ? row[k + 2 * q] : 0u;
-    const uint32_t b = (k + 2 * q + 1 < rank) ? row[k + 2 * q + 1] : 0u;
-    w[q] = a | (b << 16);
-  }
-  return u32x4{w[0], w[1], w[2], w[3]};
-}
-
-// One 32-column block of the expand as held in registers by a lane: the
-// A-operand rows of V and the two 16-byte runs of this lane's y row.
+// Expand of the item's columns [c0, c1) in chunks of CW columns. A chunk's
+// 32 y rows and its CW rows of V (one contiguous span of V) are staged
+// through LDS; every wave computes whole 32-column blocks from LDS, with the
+// rows of a block permuted by colmap so that a lane owns two runs of 8
+// contiguous bf16 of one y row; the results go back into the LDS y tile,
+// which is then stored row-contiguously.
 template <int RB>
-struct ExpBlock {
-  u32x4 vf[2 * RB];
-  u32x4 y0, y1;
-  int cb;  // block index, -1 if none
+struct ExpRegs {
+  u32x4 y[Geo<RB>::YV];
+  u32x4 v[Geo<RB>::VV];
 };
 
-struct ExpArgs {
-  __amdgpu_buffer_rsrc_t vr;  // V [ncols, ldv] bf16
-  int64_t ldv;
-  int rank;
-  bool vec16;
-  int ncols;
-  __amdgpu_buffer_rsrc_t yr;  // y rows of the tile
-  uint32_t yoff;              // this lane's y row (kOff if invalid)
+template <int RB>
+struct ExpCtx {
+  __amdgpu_buffer_rsrc_t yr, vr;
+  uint32_t yoff[Geo<RB>::YV];  // byte offset of this thread's y rows
+  uint16_t vrow[Geo<RB>::VV];  // V vector f = t + 256j of a chunk: row within the chunk
+  uint16_t vlds[Geo<RB>::VV];  // and its element offset in the LDS V tile
+  int64_t ldv;                 // V row stride (elements)
+  int rank, kbn;               // rank, k-steps of 16 that hold rank columns
+  int nv;                      // 16-byte V vectors per chunk (vec16)
+  bool vec16;                  // V rows are whole 16-byte vectors
+  int c0, c1;                  // column range of the item
   float oscale;
 };
 
 template <int RB>
-__device__ __forceinline__ void exp_load(const ExpArgs& a, int cb, int lane, ExpBlock<RB>& B) {
+__device__ __forceinline__ void exp_load(const ExpCtx<RB>& C, int cs, ExpRegs<RB>& R) {
+  using G = Geo<RB>;
+  constexpr int YPR = G::CW / 8;
+  const int col = cs + 8 * (threadIdx.x % YPR);
+  const bool cv = col < C.c1;
+  const uint32_t cbytes = 2u * (uint32_t)col;
+#pragma unroll
+  for (int j = 0; j < G::YV; ++j) R.y[j] = bld16(C.yr, cv ? C.yoff[j] + cbytes : kOff);
+  if (C.vec16) {
+    // the chunk's V rows [cs, cs + CW) are one contiguous span
+    const uint32_t base = (uint32_t)(cs * C.ldv * 2);
+#pragma unroll
+    for (int j = 0; j < G::VV; ++j) {
+      const int f = threadIdx.x + kThreads * j;
+      const bool ok = f < C.nv && cs + C.vrow[j] < C.c1;
+      R.v[j] = bld16(C.vr, ok ? base + 16u * (uint32_t)f : kOff);
+    }
+  }
+}
+
+template <int RB>
+__device__ __forceinline__ void exp_to_lds(const ExpCtx<RB>& C, int cs, const ExpRegs<RB>& R,
+                                           uint16_t* ys, uint16_t* vs) {
+  using G = Geo<RB>;
+  constexpr int YPR = G::CW / 8;
+  constexpr int RPJ = kThreads / YPR;
+  const int r0 = threadIdx.x / YPR, c = 8 * (threadIdx.x % YPR);
+#pragma unroll
+  for (int j = 0; j < G::YV; ++j) st16(ys + (r0 + RPJ * j) * G::CWP + c, R.y[j]);
+  if (C.vec16) {
+#pragma unroll
+    for (int j = 0; j < G::VV; ++j)
+      if (threadIdx.x + kThreads * j < C.nv) st16(vs + C.vlds[j], R.v[j]);
+  } else {
+    // rows not made of whole 16-byte vectors: element loads straight to LDS
+    const int kw = 16 * C.kbn;
+    for (int e = threadIdx.x; e < G::CW * kw; e += kThreads) {
+      const int row = e / kw, k = e - row * kw;
+      const bool ok = k < C.rank && cs + row < C.c1;
+      vs[row * G::RP + k] = (uint16_t)bld2(C.vr, ok ? (uint32_t)(((cs + row) * C.ldv + k) * 2) : kOff);
+    }
+  }
+}
+
+template <int RB>
+__device__ __forceinline__ void exp_mfma(const ExpCtx<RB>& C, const PFrags<RB>& F, int cs, uint16_t* ys,
+                                         const uint16_t* vs, int wave, int lane) {
+  using G = Geo<RB>;
+  constexpr int NB = G::CW / 32;  // 32-column blocks per chunk
   const int m = lane & 31, h = lane >> 5;
-  B.cb = cb;
-  const int col0 = cb * 32;
-  const uint32_t vrow = (uint32_t)((int64_t)(col0 + colmap(m)) * a.ldv * 2);  // rows >= ncols: outside
-  const int kbn = (a.rank + 15) >> 4;  // k-steps of 16 that hold rank columns (uniform)
 #pragma unroll
-  for (int kb = 0; kb < 2 * RB; ++kb) {
-    const int k = 16 * kb + 8 * h;
-    if (kb >= kbn) {
-      B.vf[kb] = zero16();  // never used by the MFMAs: no load issued
-    } else if (a.vec16) {
-      B.vf[kb] = bld16(a.vr, k < a.rank ? vrow + 2u * k : kOff);
-    } else {
-      uint32_t w[4];
+  for (int q = wave; q < NB; q += 4) {
+    const int col0 = 32 * q;
+    if (cs + col0 >= C.c1) break;  // uniform
+    f32x16 acc = zero_acc16();
+    const uint16_t* vrow = vs + (col0 + colmap(m)) * G::RP + 8 * h;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k0 = k + 2 * q;
-        const uint32_t lo = bld2(a.vr, k0 < a.rank ? vrow + 2u * k0 : kOff);
-        const uint32_t hi = bld2(a.vr, k0 + 1 < a.rank ? vrow + 2u * (k0 + 1) : kOff);
-        w[q] = (lo & 0xffffu) | (hi << 16);
+    for (int kb = 0; kb < 2 * RB; ++kb) {
+      if (kb < C.kbn) {
+        const u32x4 vf = ld16(vrow + 16 * kb);
+        acc = mfma32(as_bf16x8(vf), F.hi[kb], acc);
+        acc = mfma32(as_bf16x8(vf), F.lo[kb], acc);
       }
-      B.vf[kb] = u32x4{w[0], w[1], w[2], w[3]};
     }
+    // token m, columns col0 + 8h + [0, 8) and col0 + 16 + 8h + [0, 8)
+    uint16_t* yr = ys + m * G::CWP + col0 + 8 * h;
+    float f[8];
+    unpack8(ld16(yr), f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = f[i] + C.oscale * acc[i];
+    st16(yr, pack8(f));
+    unpack8(ld16(yr + 16), f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = f[i] + C.oscale * acc[8 + i];
+    st16(yr + 16, pack8(f));
   }
-  const int c0 = col0 + 8 * h, c1 = col0 + 16 + 8 * h;
-  B.y0 = bld16(a.yr, c0 < a.ncols ? a.yoff + 2u * c0 : kOff);
-  B.y1 = bld16(a.yr, c1 < a.ncols ? a.yoff + 2u * c1 : kOff);
 }
 
 template <int RB>
-__device__ __forceinline__ void exp_finish(const ExpArgs& a, const PFrags<RB>& F, int lane,
-                                           const ExpBlock<RB>& B) {
-  const int h = lane >> 5;
-  const int kbn = (a.rank + 15) >> 4;
-  f32x16 acc = zero_acc16();
+__device__ __forceinline__ void exp_store(const ExpCtx<RB>& C, int cs, const uint16_t* ys) {
+  using G = Geo<RB>;
+  constexpr int YPR = G::CW / 8;
+  constexpr int RPJ = kThreads / YPR;
+  const int r0 = threadIdx.x / YPR, c = 8 * (threadIdx.x % YPR);
+  const int col = cs + c;
+  const bool cv = col < C.c1;
+  const uint32_t cbytes = 2u * (uint32_t)col;
 #pragma unroll
-  for (int kb = 0; kb < 2 * RB; ++kb) {
-    if (kb < kbn) {
-      acc = mfma32(as_bf16x8(B.vf[kb]), F.hi[kb], acc);
-      acc = mfma32(as_bf16x8(B.vf[kb]), F.lo[kb], acc);
-    }
-  }
-  const int col0 = B.cb * 32;
-  const int c0 = col0 + 8 * h, c1 = col0 + 16 + 8 * h;
-  float f[8];
-  unpack8(B.y0, f);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = f[i] + a.oscale * acc[i];
-  bst16(a.yr, c0 < a.ncols ? a.yoff + 2u * c0 : kOff, pack8(f));
-  unpack8(B.y1, f);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = f[i] + a.oscale * acc[8 + i];
-  bst16(a.yr, c1 < a.ncols ? a.yoff + 2u * c1 : kOff, pack8(f));
+  for (int j = 0; j < G::YV; ++j)
+    bst16(C.yr, cv ? C.yoff[j] + cbytes : kOff, ld16(ys + (r0 + RPJ * j) * G::CWP + c));
 }
 
-// Blocks per round of the expand loop (32-column blocks whose loads a wave
-// issues together). Stores share the memory counter with loads on this chip
-// family, so a pending y store would force every later wait to drain all
-// loads; the expand therefore runs in rounds: issue a round's loads, wait
-// once, then compute and store the round.
-template <int RB>
-struct ExpandDepth {
-  static constexpr int v = RB == 1 ? 8 : (RB == 2 ? 4 : 2);
-};
-
-template <int RB>
-struct ExpRing {
-  ExpBlock<RB> b[ExpandDepth<RB>::v];
-};
-
-// Loads the round of blocks cb_first, cb_first + 4, ... (< cb_end).
-template <int RB>
-__device__ __forceinline__ void exp_ring_load(const ExpArgs& a, int cb_first, int cb_end, int lane,
-                                              ExpRing<RB>& R) {
-  constexpr int DE = ExpandDepth<RB>::v;
+template <int RB, typename PT>
+__device__ __forceinline__ ExpCtx<RB> exp_ctx(const PT& P, const TileInfo& t, int c) {
+  using G = Geo<RB>;
+  constexpr int YPR = G::CW / 8;
+  constexpr int RPJ = kThreads / YPR;
+  ExpCtx<RB> C;
+  const TileRows yt = tile_rows(P.Y, P.ldy, P.N, P, t);
+  C.yr = yt.r;
+  const int r0 = threadIdx.x / YPR;
 #pragma unroll
-  for (int s = 0; s < DE; ++s) {
-    const int cb = cb_first + 4 * s;
-    if (cb < cb_end) {
-      exp_load<RB>(a, cb, lane, R.b[s]);
-    } else {
-      R.b[s].cb = -1;
+  for (int j = 0; j < G::YV; ++j) C.yoff[j] = row_off(P, t, yt, r0 + RPJ * j);
+  C.ldv = ((t.rank + P.v_round - 1) / P.v_round) * P.v_round;
+  C.vec16 = (C.ldv & 7) == 0;
+  C.vr = mk_rsrc(v_ptr(P, t), (int64_t)P.N * C.ldv * 2);
+  C.rank = t.rank;
+  C.kbn = (t.rank + 15) >> 4;
+  const int rv = (int)(C.ldv >> 3);  // vectors per V row (vec16)
+  C.nv = G::CW * rv;
+  const float inv = 1.0f / (float)max(rv, 1);
 #pragma unroll
-      for (int kb = 0; kb < 2 * RB; ++kb) R.b[s].vf[kb] = zero16();
-      R.b[s].y0 = zero16();
-      R.b[s].y1 = zero16();
-    }
+  for (int j = 0; j < G::VV; ++j) {
+    // row = f / rv exactly: (f + 0.5) / rv is at least 1/(2 rv) away from an integer
+    const int f = threadIdx.x + kThreads * j;
+    const int row = (int)(((float)f + 0.5f) * inv);
+    C.vrow[j] = (uint16_t)row;
+    C.vlds[j] = (uint16_t)(row * G::RP + 8 * (f - row * rv));
   }
+  const int nblocks = (P.N + 31) >> 5;
+  const int cb0 = c * P.nblk;
+  C.c0 = 32 * cb0;
+  C.c1 = min(P.N, 32 * min(nblocks, cb0 + P.nblk));
+  C.oscale = P.scale_in_shrink ? 1.f : t.scale;
+  return C;
 }
 
-// y[token][col] += oscale * sum_k V[col][k] P[token][k] over the wave's
-// blocks; R holds the first round (already issued by the caller).
+// Runs the expand over the item's columns. R holds the first chunk's loads,
+// issued by the caller (so they can be issued before a wait).
 template <int RB>
-__device__ __forceinline__ void exp_ring_run(const ExpArgs& a, const PFrags<RB>& F, int cb_first,
-                                             int cb_end, int lane, ExpRing<RB>& R) {
-  constexpr int DE = ExpandDepth<RB>::v;
-  int cb = cb_first;
-  while (true) {
-#pragma unroll
-    for (int s = 0; s < DE; ++s)
-      if (R.b[s].cb >= 0) exp_finish<RB>(a, F, lane, R.b[s]);
-    cb += 4 * DE;
-    if (cb >= cb_end) break;
-    exp_ring_load<RB>(a, cb, cb_end, lane, R);
-  }
+__device__ __forceinline__ void expand_run(const ExpCtx<RB>& C, const PFrags<RB>& F, ExpRegs<RB>& R,
+                                           uint8_t* stage) {
+  using G = Geo<RB>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint16_t* ys = reinterpret_cast<uint16_t*>(stage);
+  uint16_t* vs = ys + 32 * G::CWP;
+  // a rank that ends half-way through a 16-wide k-step: the other half of
+  // the last step is zero in every V row (written once; chunks never touch it)
+  if (C.vec16 && (C.ldv & 8) && threadIdx.x < G::CW)
+    st16(vs + threadIdx.x * G::RP + C.ldv, zero16());
+  auto chunk = [&](int cs) {
+    exp_to_lds<RB>(C, cs, R, ys, vs);
+    lds_sync();
+    if (cs + G::CW < C.c1) exp_load<RB>(C, cs + G::CW, R);
+    exp_mfma<RB>(C, F, cs, ys, vs, wave, lane);
+    lds_sync();
+    exp_store<RB>(C, cs, ys);
+    lds_sync();
+  };
+  // the first chunk is peeled so that every pass of the loop starts with the
+  // same loads and stores pending (the next chunk's loads, then the stores)
+  if (C.c0 < C.c1) chunk(C.c0);
+  for (int cs = C.c0 + G::CW; cs < C.c1; cs += G::CW) chunk(cs);
 }
 
 // ---------------------------------------------------------------------------
@@ -402,108 +571,50 @@ __device__ __forceinline__ void xwg_acquire() {
 // ---------------------------------------------------------------------------
 // Items
 // ---------------------------------------------------------------------------
-struct Smem {
-  float red[4 * 16 * 64];
-  float Pl[kTileM * kLdp];
-  TileInfo ti;
-  int flag;
-};
-
-// X rows of the tile as a buffer resource: based at the tile's first row when
-// rows are contiguous, at X itself for a token_rows gather.
+// Writes Pl rows 0..cnt-1, columns < rank to U.
 template <typename PT>
-__device__ __forceinline__ void tile_rows(const uint16_t* base, int64_t ld, int width, const PT& P,
-                                          const TileInfo& t, __amdgpu_buffer_rsrc_t& r, uint32_t& off) {
-  const int n = threadIdx.x & 31;
-  const bool valid = n < t.cnt;
-  if (P.token_rows) {
-    r = mk_rsrc(base, (int64_t)0x7ffffff0);
-    off = valid ? (uint32_t)((int64_t)P.token_rows[t.p0 + n] * ld * 2) : kOff;
-  } else {
-    r = mk_rsrc(base + (int64_t)t.p0 * ld, ((int64_t)(t.cnt - 1) * ld + width) * 2);
-    off = valid ? (uint32_t)((int64_t)n * ld * 2) : kOff;
-  }
-}
-
-template <int RB, typename PT>
-__device__ __forceinline__ void shrink_range(const PT& P, const TileInfo& t, int kb, int ke,
-                                             int wave, int lane, f32x16 (&acc)[RB]) {
-  __amdgpu_buffer_rsrc_t xr;
-  uint32_t xoff;
-  tile_rows(P.X, P.ldx, P.K, P, t, xr, xoff);
-#pragma unroll
-  for (int b = 0; b < RB; ++b) acc[b] = zero_acc16();
-  shrink_acc<RB>(xr, xoff, w_ptr(P, t), P.K, t.rank, kb, ke, wave, lane, acc);
-}
-
-// Writes Pl rows 0..31, columns < 32*RB (zero where rank/token invalid) to U.
-template <typename PT>
-__device__ __forceinline__ void store_u_from_lds(const PT& P, const TileInfo& t,
-                                                 const float* Pl) {
+__device__ __forceinline__ void store_u_from_lds(const PT& P, const TileInfo& t, const float* Pl) {
   for (int e = threadIdx.x; e < kTileM * t.rank; e += kThreads) {
     const int n = e / t.rank, k = e - n * t.rank;
     if (n < t.cnt) P.U[(int64_t)(t.p0 + n) * P.ldu + k] = Pl[n * kLdp + k];
   }
 }
 
-template <typename PT>
-__device__ __forceinline__ ExpArgs exp_args(const PT& P, const TileInfo& t) {
-  ExpArgs a;
-  tile_rows(P.Y, P.ldy, P.N, P, t, a.yr, a.yoff);
-  a.ldv = ((t.rank + P.v_round - 1) / P.v_round) * P.v_round;
-  a.vec16 = (a.ldv & 7) == 0;
-  a.vr = mk_rsrc(v_ptr(P, t), (int64_t)P.N * a.ldv * 2);
-  a.rank = t.rank;
-  a.ncols = P.N;
-  a.oscale = P.scale_in_shrink ? 1.f : t.scale;
-  return a;
-}
-
-// Column-block range of n-chunk c: this wave starts at cb0 + wave.
-template <typename PT>
-__device__ __forceinline__ void chunk_blocks(const PT& P, int c, int& cb0, int& cb_end) {
-  const int nblocks = (P.N + 31) >> 5;
-  cb0 = c * P.nblk;
-  cb_end = min(nblocks, cb0 + P.nblk);
-}
-
 template <int RB, typename PT>
-__device__ __forceinline__ void expand_tile_from_lds(const PT& P, const TileInfo& t, int c,
-                                                     const float* Pl, int wave, int lane) {
-  const ExpArgs a = exp_args(P, t);
-  int cb0, cb_end;
-  chunk_blocks(P, c, cb0, cb_end);
-  ExpRing<RB> R;
-  exp_ring_load<RB>(a, cb0 + wave, cb_end, lane, R);
+__device__ __forceinline__ void expand_from_lds(const PT& P, const TileInfo& t, int c, const float* Pl,
+                                                uint8_t* stage) {
+  const ExpCtx<RB> C = exp_ctx<RB>(P, t, c);
+  ExpRegs<RB> R;
+  if (C.c0 < C.c1) exp_load<RB>(C, C.c0, R);
   PFrags<RB> F;
-  build_pfrags<RB>(Pl, t.rank, lane, F);
-  exp_ring_run<RB>(a, F, cb0 + wave, cb_end, lane, R);
+  build_pfrags<RB>(Pl, t.rank, threadIdx.x & 63, F);
+  expand_run<RB>(C, F, R, stage);
 }
 
 // kModeFusedTile: full shrink of one tile on chip, then its n-chunk c.
-template <int RB, typename PT>
-__device__ __forceinline__ void item_fused_tile(const PT& P, Smem& S, const TileInfo& t, int c) {
+template <int RB, typename PT, typename SM>
+__device__ __forceinline__ void item_fused_tile(const PT& P, SM& S, const TileInfo& t, int c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   f32x16 acc[RB];
-  shrink_range<RB>(P, t, 0, P.K, wave, lane, acc);
+  shrink_lds<RB>(P, t, 0, P.K, S.stage, acc);
   const float ps = P.scale_in_shrink ? t.scale : 1.f;
   float* Pl = S.Pl;
-  reduce_waves<RB>(S.red, acc, wave, lane, [&](int k, int n, float v) { Pl[n * kLdp + k] = v * ps; });
+  reduce_waves<RB>(reinterpret_cast<float*>(S.stage), acc, wave, lane,
+                   [&](int k, int n, float v) { Pl[n * kLdp + k] = v * ps; });
   if (P.write_u && c == 0) store_u_from_lds(P, t, Pl);
-  expand_tile_from_lds<RB>(P, t, c, Pl, wave, lane);
+  expand_from_lds<RB>(P, t, c, Pl, S.stage);
 }
 
 // kModeExpand: U from memory, expand n-chunk c.
-template <int RB, typename PT>
-__device__ __forceinline__ void item_expand(const PT& P, Smem& S, const TileInfo& t, int c) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+template <int RB, typename PT, typename SM>
+__device__ __forceinline__ void item_expand(const PT& P, SM& S, const TileInfo& t, int c) {
   float* Pl = S.Pl;
   for (int e = threadIdx.x; e < kTileM * 32 * RB; e += kThreads) {
     const int n = e / (32 * RB), k = e - n * (32 * RB);
     Pl[n * kLdp + k] = (n < t.cnt && k < t.rank) ? P.U[(int64_t)(t.p0 + n) * P.ldu + k] : 0.f;
   }
-  __syncthreads();
-  expand_tile_from_lds<RB>(P, t, c, Pl, wave, lane);
+  lds_sync();
+  expand_from_lds<RB>(P, t, c, Pl, S.stage);
 }
 
 template <typename PT>
@@ -512,16 +623,17 @@ __device__ __forceinline__ float* partial_ptr(const PT& P, int g, int c) {
 }
 
 // kModeShrink / kModeFusedDep phase A: shrink over k-chunk c.
-template <int RB, typename PT>
-__device__ __forceinline__ void item_shrink(const PT& P, Smem& S, const TileInfo& t, int c) {
+template <int RB, typename PT, typename SM>
+__device__ __forceinline__ void item_shrink(const PT& P, SM& S, const TileInfo& t, int c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kb = c * P.kchunk;
   const int ke = min(P.K, kb + P.kchunk);
   f32x16 acc[RB];
-  shrink_range<RB>(P, t, kb, ke, wave, lane, acc);
+  shrink_lds<RB>(P, t, kb, ke, S.stage, acc);
+  float* red = reinterpret_cast<float*>(S.stage);
   const float ps = P.scale_in_shrink ? t.scale : 1.f;
   if (P.mode == kModeShrink && P.ks == 1) {
-    reduce_waves<RB>(S.red, acc, wave, lane, [&](int k, int n, float v) {
+    reduce_waves<RB>(red, acc, wave, lane, [&](int k, int n, float v) {
       if (n < t.cnt && k < t.rank) P.U[(int64_t)(t.p0 + n) * P.ldu + k] = v * ps;
     });
     return;
@@ -529,10 +641,10 @@ __device__ __forceinline__ void item_shrink(const PT& P, Smem& S, const TileInfo
   float* part = partial_ptr(P, t.g, c);
   const int rpad = P.rpad;
   float sink = 0.f;
-  reduce_waves<RB>(S.red, acc, wave, lane,
+  reduce_waves<RB>(red, acc, wave, lane,
                    [&](int k, int n, float v) { sink += xwg_store(part + n * rpad + k, v); });
 #if LORA_XWG == 3
-  S.red[threadIdx.x] = sink;  // waits for every swap of this thread
+  red[threadIdx.x] = sink;  // waits for every swap of this thread
 #else
   (void)sink;
 #endif
@@ -560,17 +672,15 @@ __device__ __forceinline__ void item_shrink(const PT& P, Smem& S, const TileInfo
 // If the chunks do not arrive within spin_ticks (e.g. their workgroups are
 // not resident), the item computes the same chunks itself in the same order,
 // so the result is identical and no wait is unbounded.
-template <int RB, typename PT>
-__device__ __forceinline__ void item_expand_wait(const PT& P, Smem& S, const TileInfo& t, int c) {
+template <int RB, typename PT, typename SM>
+__device__ __forceinline__ void item_expand_wait(const PT& P, SM& S, const TileInfo& t, int c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int* ctr = P.counters + kCtrTiles + t.g;
-  // the y rows and expand weights do not depend on the shrink: load the
-  // first block before waiting
-  const ExpArgs ea = exp_args(P, t);
-  int cb0, cb_end;
-  chunk_blocks(P, c, cb0, cb_end);
-  ExpRing<RB> R;
-  exp_ring_load<RB>(ea, cb0 + wave, cb_end, lane, R);
+  // y rows and expand weights do not depend on the shrink: issue the first
+  // chunk's loads before waiting
+  const ExpCtx<RB> C = exp_ctx<RB>(P, t, c);
+  ExpRegs<RB> R;
+  exp_load<RB>(C, C.c0, R);  // an empty column range reads nothing
   if (threadIdx.x == 0) {
     const uint64_t t0 = wall_clock64();
     int ready = 0;
@@ -593,33 +703,35 @@ __device__ __forceinline__ void item_expand_wait(const PT& P, Smem& S, const Til
       for (int q = 1; q < P.ks; ++q) s += xwg_load(partial_ptr(P, t.g, q) + n * rpad + k);
       Pl[n * kLdp + k] = s * ps;
     }
-  } else {
-    // the prefetched blocks are dropped while the shrink is recomputed
-    // (keeps both register sets from being live at once) and loaded again
-    for (int q = 0; q < P.ks; ++q) {
-      const int kb = q * P.kchunk;
-      const int ke = min(P.K, kb + P.kchunk);
-      f32x16 acc[RB];
-      shrink_range<RB>(P, t, kb, ke, wave, lane, acc);
-      reduce_waves<RB>(S.red, acc, wave, lane, [&](int k, int n, float v) {
-        Pl[n * kLdp + k] = (q == 0) ? v : Pl[n * kLdp + k] + v;
-      });
-    }
-    for (int e = threadIdx.x; e < kTileM * rcols; e += kThreads) {
-      const int n = e / rcols, k = e - n * rcols;
-      Pl[n * kLdp + k] *= ps;
-    }
-    exp_ring_load<RB>(ea, cb0 + wave, cb_end, lane, R);
+    lds_sync();
+    if (P.write_u && c == 0) store_u_from_lds(P, t, Pl);
+    PFrags<RB> F;
+    build_pfrags<RB>(Pl, t.rank, lane, F);
+    expand_run<RB>(C, F, R, S.stage);
+    return;
   }
-  __syncthreads();
+  // Fallback. The early loads are dropped and issued again after the shrink
+  // (a separate expand, so that they are not held in registers through it).
+  for (int q = 0; q < P.ks; ++q) {
+    const int kb = q * P.kchunk;
+    const int ke = min(P.K, kb + P.kchunk);
+    f32x16 acc[RB];
+    shrink_lds<RB>(P, t, kb, ke, S.stage, acc);
+    reduce_waves<RB>(reinterpret_cast<float*>(S.stage), acc, wave, lane, [&](int k, int n, float v) {
+      Pl[n * kLdp + k] = (q == 0) ? v : Pl[n * kLdp + k] + v;
+    });
+  }
+  for (int e = threadIdx.x; e < kTileM * rcols; e += kThreads) {
+    const int n = e / rcols, k = e - n * rcols;
+    Pl[n * kLdp + k] *= ps;
+  }
+  lds_sync();
   if (P.write_u && c == 0) store_u_from_lds(P, t, Pl);
-  PFrags<RB> F;
-  build_pfrags<RB>(Pl, t.rank, lane, F);
-  exp_ring_run<RB>(ea, F, cb0 + wave, cb_end, lane, R);
+  expand_from_lds<RB>(P, t, c, Pl, S.stage);
 }
 
-template <int RB, typename PT>
-__device__ __forceinline__ void run_item(const PT& P, Smem& S, const TileInfo& t, int kind, int c) {
+template <int RB, typename PT, typename SM>
+__device__ __forceinline__ void run_item(const PT& P, SM& S, const TileInfo& t, int kind, int c) {
   switch (kind) {
     case 0: item_shrink<RB>(P, S, t, c); break;
     case 1: item_expand<RB>(P, S, t, c); break;
@@ -629,8 +741,8 @@ __device__ __forceinline__ void run_item(const PT& P, Smem& S, const TileInfo& t
 }
 
 template <int RBMAX, typename PT>
-__global__ __launch_bounds__(kThreads) void sgmv_fwd_kernel(PT P) {
-  __shared__ Smem S;
+__global__ __launch_bounds__(kThreads, 2) void sgmv_fwd_kernel(PT P) {
+  __shared__ Smem<RBMAX> S;
   const int b = blockIdx.x;
   int item = -1, kind = 0, per = 1;
   if (P.mode == kModeFusedDep) {

@@ -313,11 +313,11 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
     P.n_tiles = tiles;
     const int nblocks = cdiv(c.N, 32);
     const int slots = 2 * cus;  // resident workgroups at the kernels' occupancy
-    // split of the shrink reduction: none when the tiles alone fill the GPU,
-    // otherwise chunks of about kShrinkChunk elements
-    auto choose_ks = [&](bool for_fused) {
+    // split of a shrink-only call's reduction: none when the tiles alone fill
+    // the GPU, otherwise chunks of about kShrinkChunk elements
+    auto choose_ks = [&]() {
       int ks = 1;
-      if (tiles < (for_fused ? cus / 4 : cus)) ks = cdiv(c.K, kShrinkChunk);
+      if (tiles < cus) ks = cdiv(c.K, kShrinkChunk);
       ks = std::min({ks, kMaxKs, std::max(1, kMaxPartials / tiles)});
       ks = std::max(ks, 1);
       P.kchunk = round_up(cdiv(c.K, ks), 64);
@@ -334,7 +334,7 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
     P.spin_ticks = (int)std::min<int64_t>((int64_t)dev.wall_khz * 1000 / 5000, 1 << 30);  // 200 us
     if (c.mode_op == LORA_OP_SHRINK) {
       P.mode = kModeShrink;
-      choose_ks(false);
+      choose_ks();
       if (P.ks > 1 && tiles > kMaxDepTiles) { P.ks = 1; P.kchunk = round_up(c.K, 64); }
       P.n_items_a = tiles * P.ks;
       P.grid = P.n_items_a;
@@ -362,10 +362,21 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
         P.n_items_a = tiles * P.ks;
         P.n_items_b = tiles * P.nc;
         P.grid = P.n_items_a + P.n_items_b;
-      } else if (tiles >= slots || tiles > std::min(kMaxDepTiles, kMaxPartials)) {
-        // the tiles alone fill every resident slot: keep u on chip. Workgroup
-        // b runs on XCD b % 8; consecutive tiles (one adapter's) are mapped to
-        // the same XCD so that its weights stay in that XCD's L2
+      } else if (4 * tiles <= cus) {
+        // small batch: at most one workgroup per CU. Each computes its tile's
+        // full shrink on chip and one column chunk of the expand: a split
+        // shrink would hand partial sums between XCDs, which costs more than
+        // the repeated shrink reads
+        P.mode = kModeFusedTile;
+        P.ks = 1;
+        P.kchunk = round_up(c.K, 64);
+        P.nblk = cdiv(nblocks, std::max(1, std::min(nblocks, cus / tiles)));
+        P.nc = cdiv(nblocks, P.nblk);
+        P.n_items_a = tiles * P.nc;
+        P.xcd_remap = xcd_remap_enabled() ? 1 : 0;
+        P.grid = P.xcd_remap ? round_up(P.n_items_a, 8) : P.n_items_a;
+      } else if (tiles >= cus || tiles > std::min(kMaxDepTiles, kMaxPartials)) {
+        // the tiles alone give every CU work: keep u on chip, one item per tile
         P.mode = kModeFusedTile;
         P.ks = 1;
         P.kchunk = round_up(c.K, 64);
@@ -375,12 +386,16 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
         P.xcd_remap = xcd_remap_enabled() ? 1 : 0;
         P.grid = P.xcd_remap ? round_up(tiles, 8) : tiles;
       } else {
-        // fewer tiles than slots: shrink items (split along k when few) and
-        // finer expand items that wait for their tile, so all CUs stay busy
+        // medium batch: one shrink item per tile and a few expand items per
+        // tile that wait for it (about three workgroups per CU in all), so
+        // every CU has work without repeating the shrink
         P.mode = kModeFusedDep;
-        choose_ks(true);
-        choose_nc();
-        P.n_items_a = tiles * P.ks;
+        P.ks = 1;
+        P.kchunk = round_up(c.K, 64);
+        const int nc = std::max(2, std::min(nblocks, 3 * cus / tiles - 1));
+        P.nblk = cdiv(nblocks, nc);
+        P.nc = cdiv(nblocks, P.nblk);
+        P.n_items_a = tiles;
         P.n_items_b = tiles * P.nc;
         P.grid = P.n_items_a + P.n_items_b;
       }

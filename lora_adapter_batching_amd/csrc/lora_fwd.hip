@@ -39,14 +39,24 @@ struct TileInfo {
 // tile's description in LDS (a binary search would chain several dependent
 // loads of the kernel-argument table).
 template <typename PT>
+struct PlanCap;
+template <int CAP>
+struct PlanCap<FwdPlanT<CAP>> {
+  static constexpr int v = CAP;  // segment capacity of a plan type
+};
+
+template <typename PT>
 __device__ __forceinline__ TileInfo tile_info(const PT& P, int g, TileInfo* lds) {
-  const int i = threadIdx.x;
-  if (i < P.n_seg) {
-    const int t0 = P.seg_tile0[i];
-    const int t1 = (i + 1 < P.n_seg) ? P.seg_tile0[i + 1] : P.n_tiles;
-    const int tok0 = P.seg_tok0[i], ntok = P.seg_ntok[i];
-    const int adapter = P.seg_adapter[i], rank = P.seg_rank[i], slot = P.seg_slot[i];
-    const float scale = P.seg_scale[i];
+  // the table reads do not wait for n_seg: entries past it are in the plan
+  // too, and only the comparison uses n_seg
+  const int i = min((int)threadIdx.x, PlanCap<PT>::v - 1);
+  const int t0 = P.seg_tile0[i];
+  const int t1n = P.seg_tile0[min(i + 1, PlanCap<PT>::v - 1)];
+  const int tok0 = P.seg_tok0[i], ntok = P.seg_ntok[i];
+  const int adapter = P.seg_adapter[i], rank = P.seg_rank[i], slot = P.seg_slot[i];
+  const float scale = P.seg_scale[i];
+  if (threadIdx.x < P.n_seg) {
+    const int t1 = (i + 1 < P.n_seg) ? t1n : P.n_tiles;
     if (g >= t0 && g < t1) {
       const int tt = g - t0;
       TileInfo t;
@@ -741,7 +751,7 @@ __device__ __forceinline__ void run_item(const PT& P, SM& S, const TileInfo& t, 
 }
 
 template <int RBMAX, typename PT>
-__global__ __launch_bounds__(kThreads, 2) void sgmv_fwd_kernel(PT P) {
+__global__ __launch_bounds__(kThreads, RBMAX <= 2 ? 3 : 2) void sgmv_fwd_kernel(PT P) {
   __shared__ Smem<RBMAX> S;
   const int b = blockIdx.x;
   int item = -1, kind = 0, per = 1;
@@ -797,7 +807,7 @@ static hipError_t launch_fwd_t(const PT& P, int rbmax, hipStream_t stream) {
 // the kernel argument, and its size is part of every launch's host cost.
 hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream) {
   if (P.n_seg <= kSmallSeg) {
-    FwdPlanT<kSmallSeg> Q;
+    FwdPlanT<kSmallSeg> Q{};
     static_cast<FwdHeader&>(Q) = static_cast<const FwdHeader&>(P);
     for (int i = 0; i < P.n_seg; ++i) {
       Q.seg_tok0[i] = P.seg_tok0[i];

@@ -64,33 +64,142 @@ hipError_t launch_transpose(const TransposePlan& P, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 // Weight gradients
 // ---------------------------------------------------------------------------
-// Columns per lane QN and rank blocks of 16 (KB) for a rank: QN * KB = 16
-// keeps 64 fp32 accumulators per lane for every rank.
-__host__ __device__ constexpr int wgrad_qn(int kb) { return kb <= 2 ? 8 : (kb == 4 ? 4 : 2); }
+// Both gradients have the form O[j][k] = s * sum_t Z[t][j] Q[t][k] over the
+// adapter's tokens t: Z = dy, Q = u for dB (O = dB_i[j][k]); Z = x, Q = du for
+// dA (O = dA_i^T, stored as dA_i[k][j]). An item owns 64*QN columns j of one
+// adapter's O and reduces over all of the adapter's tokens in steps of 32.
+// v_mfma_f32_16x16x32_bf16 takes A = Z^T (16 columns x 32 tokens; each lane
+// loads 8 token rows of QN columns and transposes them in registers) and
+// B = Q (32 tokens x 16 ranks, fp32 split into bf16 hi + lo, staged through
+// LDS transposed). The loads of the next kWgDepth-1 steps are in flight while
+// a step is computed.
+// Columns per lane QN and rank blocks of 16 (KB) for a rank.
+__host__ __device__ constexpr int wgrad_qn(int kb) { return kb <= 4 ? 4 : 2; }
 __host__ __device__ inline int wgrad_kb(int rank) {
   const int k = (rank + 15) >> 4;
   return k <= 1 ? 1 : (k <= 2 ? 2 : (k <= 4 ? 4 : 8));
 }
 __host__ __device__ inline int wgrad_cw(int rank) { return 4 * 16 * wgrad_qn(wgrad_kb(rank)); }
 
-constexpr int kQtLd = 36;  // LDS row length (floats) of the transposed u/du tile
+constexpr int kQtLd = 36;    // LDS row length (floats) of the transposed Q tile
+constexpr int kWgDepth = 3;  // steps whose loads are in flight (and LDS Q buffers)
 
-template <int QN>
-__device__ __forceinline__ void load_row_cols(const uint16_t* p, bool ok, uint32_t (&w)[QN / 2]) {
-  if constexpr (QN == 8) {
-    const u32x4 v = ok ? ld16(p) : zero16();
-    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-  } else if constexpr (QN == 4) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 v = ok ? *reinterpret_cast<const u32x2*>(p) : u32x2{0u, 0u};
-    w[0] = v[0]; w[1] = v[1];
+// One 32-token step of an item: the token range and how to address it.
+struct WgCursor {
+  int seg;   // segment index in the plan (>= seg_end: past the item's tokens)
+  int t0;    // first sorted position of the step
+  int tend;  // end of the segment
+};
+
+template <int KB, int QN>
+struct WgRegs {
+  uint32_t z[8][QN / 2];  // Z rows 8g + e, this lane's QN columns (bf16 pairs)
+  float q[2 * KB];        // this thread's share of the step's Q tile
+};
+
+__device__ __forceinline__ void wg_advance(const WgradPlan& P, int seg_end, WgCursor& c) {
+  c.t0 += 32;
+  while (c.t0 >= c.tend && c.seg < seg_end) {
+    ++c.seg;
+    if (c.seg < seg_end) {
+      c.t0 = P.seg_tok0[c.seg];
+      c.tend = c.t0 + P.seg_ntok[c.seg];
+    }
+  }
+}
+
+template <int KB, int QN, bool GATHER>
+__device__ __forceinline__ void wg_load(const WgradPlan& P, const uint16_t* Z, int64_t ldz, int ncols,
+                                        const float* Q, int64_t ldq, int rank, int ccol, bool col_ok,
+                                        int seg_end, const WgCursor& c, WgRegs<KB, QN>& R) {
+  const int lane = threadIdx.x & 63, g = lane >> 4;
+  const bool live = c.seg < seg_end;
+  const int cnt = live ? min(32, c.tend - c.t0) : 0;  // valid tokens of the step (uniform)
+  // Z: a resource over the step's rows (contiguous positions) or over the
+  // whole matrix (token_rows gather; row * ldz * 2 < 2 GiB)
+  __amdgpu_buffer_rsrc_t zr, rr;
+  if constexpr (GATHER) {
+    zr = mk_rsrc(Z, cnt > 0 ? (int64_t)0x7ffffff0 : 0);
+    rr = mk_rsrc(P.token_rows + (live ? c.t0 : 0), (int64_t)cnt * 4);
   } else {
-    w[0] = ok ? *reinterpret_cast<const uint32_t*>(p) : 0u;
+    zr = mk_rsrc(Z + (int64_t)(live ? c.t0 : 0) * ldz, cnt > 0 ? ((int64_t)(cnt - 1) * ldz + ncols) * 2 : 0);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = 8 * g + e;
+    const bool ok = col_ok && r < cnt;
+    int64_t row = r;
+    if constexpr (GATHER) row = (int64_t)__builtin_amdgcn_raw_buffer_load_b32(rr, ok ? 4 * r : (int)kOff, 0, 0);
+    const uint32_t off = ok ? (uint32_t)(row * ldz * 2 + (int64_t)ccol * 2) : kOff;
+    if constexpr (QN == 4) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(zr, (int)off, 0, 0);
+      R.z[e][0] = v[0];
+      R.z[e][1] = v[1];
+    } else {
+      R.z[e][0] = __builtin_amdgcn_raw_buffer_load_b32(zr, (int)off, 0, 0);
+    }
+  }
+  // Q (fp32, sorted positions): element (tt, k) = (e2 / 16KB, e2 % 16KB)
+  const __amdgpu_buffer_rsrc_t qr = mk_rsrc(Q + (int64_t)(live ? c.t0 : 0) * ldq, (int64_t)cnt * ldq * 4);
+#pragma unroll
+  for (int j = 0; j < 2 * KB; ++j) {
+    const int e2 = threadIdx.x + kThreads * j;
+    const int tt = e2 / (16 * KB), k = e2 - tt * (16 * KB);
+    const uint32_t off = (tt < cnt && k < rank) ? (uint32_t)(((int64_t)tt * ldq + k) * 4) : kOff;
+    R.q[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (int)off, 0, 0));
   }
 }
 
 template <int KB, int QN>
-__device__ __forceinline__ void wgrad_item(const WgradPlan& P, int job, int kind, int chunk, float (*Qt)[kQtLd]) {
+__device__ __forceinline__ void wg_commit_q(const WgRegs<KB, QN>& R, float (*Qt)[kQtLd]) {
+#pragma unroll
+  for (int j = 0; j < 2 * KB; ++j) {
+    const int e2 = threadIdx.x + kThreads * j;
+    const int tt = e2 / (16 * KB), k = e2 - tt * (16 * KB);
+    Qt[k][tt] = R.q[j];
+  }
+}
+
+template <int KB, int QN>
+__device__ __forceinline__ void wg_compute(const WgRegs<KB, QN>& R, float (*Qt)[kQtLd], f32x4 (&acc)[QN][KB]) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  // A operand: frag q = Z[8g + e][column q], e = 0..7 (register transpose)
+  bf16x8 fa[QN];
+#pragma unroll
+  for (int q = 0; q < QN; ++q) {
+    u32x4 v;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t lo = R.z[2 * d][q >> 1], hi = R.z[2 * d + 1][q >> 1];
+      v[d] = (q & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    fa[q] = as_bf16x8(v);
+  }
+  // B operand: Q[8g + e][16kb + cl] as bf16 hi + lo
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    float f[8];
+    const f32x4 q0 = *reinterpret_cast<const f32x4*>(&Qt[16 * kb + cl][8 * g]);
+    const f32x4 q1 = *reinterpret_cast<const f32x4*>(&Qt[16 * kb + cl][8 * g + 4]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = q0[e];
+      f[4 + e] = q1[e];
+    }
+    bf16x8 qh, ql;
+    split8(f, qh, ql);
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      acc[q][kb] = mfma16(fa[q], qh, acc[q][kb]);
+      acc[q][kb] = mfma16(fa[q], ql, acc[q][kb]);
+    }
+  }
+}
+
+template <int KB, int QN, bool GATHER>
+__device__ __forceinline__ void wgrad_item(const WgradPlan& P, int job, int kind, int chunk,
+                                           float (*Qt)[128][kQtLd]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, cl = lane & 15;
   const int a = P.job_adapter[job];
@@ -114,57 +223,44 @@ __device__ __forceinline__ void wgrad_item(const WgradPlan& P, int job, int kind
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) acc[q][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int seg0 = P.job_seg0[job], nseg = P.job_nseg[job];
-  for (int sgi = 0; sgi < nseg; ++sgi) {
-    const int tok0 = P.seg_tok0[seg0 + sgi];
-    const int tend = tok0 + P.seg_ntok[seg0 + sgi];
-    for (int t0 = tok0; t0 < tend; t0 += 32) {
-      // stage Q[t0 .. t0+31][0 .. 16*KB) transposed into LDS
-      for (int e = threadIdx.x; e < 32 * 16 * KB; e += kThreads) {
-        const int tt = e / (16 * KB), k = e - tt * (16 * KB);
-        Qt[k][tt] = (t0 + tt < tend && k < rank) ? Q[(int64_t)(t0 + tt) * ldq + k] : 0.f;
-      }
-      // Z rows t0 + 8g + e, columns ccol .. ccol+QN-1
-      uint32_t w[8][QN / 2];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = t0 + 8 * g + e;
-        const bool ok = col_ok && t < tend;
-        const int64_t row = ok ? (P.token_rows ? (int64_t)P.token_rows[t] : (int64_t)t) : 0;
-        load_row_cols<QN>(Z + row * ldz + ccol, ok, w[e]);
-      }
-      __syncthreads();
-      // A operand: frag q = Z[t0 + 8g + e][ccol + q], e = 0..7 (register transpose)
-      bf16x8 fa[QN];
-#pragma unroll
-      for (int q = 0; q < QN; ++q) {
-        u32x4 v;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t lo = w[2 * d][q >> 1], hi = w[2 * d + 1][q >> 1];
-          v[d] = (q & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        fa[q] = as_bf16x8(v);
-      }
-      // B operand: Q[t0 + 8g + e][16kb + cl] as bf16 hi + lo
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        float f[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = Qt[16 * kb + cl][8 * g + e];
-        bf16x8 qh, ql;
-        split8(f, qh, ql);
-#pragma unroll
-        for (int q = 0; q < QN; ++q) {
-          acc[q][kb] = mfma16(fa[q], qh, acc[q][kb]);
-          acc[q][kb] = mfma16(fa[q], ql, acc[q][kb]);
-        }
-      }
-      __syncthreads();
+  const int seg0 = P.job_seg0[job];
+  const int seg_end = seg0 + P.job_nseg[job];
+  int nsteps = 0;
+  for (int q = seg0; q < seg_end; ++q) nsteps += (P.seg_ntok[q] + 31) >> 5;
+  WgCursor lc{seg0, 0, 0};
+  if (seg0 < seg_end) {
+    lc.t0 = P.seg_tok0[seg0];
+    lc.tend = lc.t0 + P.seg_ntok[seg0];
+    if (lc.t0 >= lc.tend) {  // skip empty segments
+      lc.t0 -= 32;
+      wg_advance(P, seg_end, lc);
     }
   }
-  // lane holds C[m = 4g + i][n = cl] of block (q, kb): column ccol(m) + q where
-  // the A-operand row m came from lane m's columns c0 + QN*m, rank 16kb + cl
+  // Ring of D register sets; step i uses set i % D and LDS buffer i % D.
+  // The step count is rounded up to a multiple of D: steps past the item's
+  // tokens load nothing (all offsets fall outside their resources) and add
+  // zeros, so every pass of the loop issues the same loads and each wait
+  // covers only the set it needs.
+  // (a gathered batch waits for its row indices anyway: a shallow ring)
+  constexpr int D = GATHER ? 2 : kWgDepth;
+  WgRegs<KB, QN> R[D];
+#pragma unroll
+  for (int s = 0; s < D; ++s) {
+    wg_load<KB, QN, GATHER>(P, Z, ldz, ncols, Q, ldq, rank, ccol, col_ok, seg_end, lc, R[s]);
+    wg_advance(P, seg_end, lc);
+  }
+  for (int i = 0; i < nsteps; i += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      wg_commit_q<KB, QN>(R[s], Qt[s]);
+      __syncthreads();
+      wg_compute<KB, QN>(R[s], Qt[s], acc);
+      wg_load<KB, QN, GATHER>(P, Z, ldz, ncols, Q, ldq, rank, ccol, col_ok, seg_end, lc, R[s]);
+      wg_advance(P, seg_end, lc);
+    }
+  }
+  // lane holds C[m = 4g + i][n = cl] of block (q, kb): column c0 + QN*m + q
+  // (the A-operand row m came from lane m's columns), rank 16kb + cl
   const bool accum = P.job_accum[job] != 0;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
@@ -194,8 +290,9 @@ __device__ __forceinline__ void wgrad_item(const WgradPlan& P, int job, int kind
   }
 }
 
-__global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradPlan P) {
-  __shared__ float Qt[128][kQtLd];
+template <bool GATHER>
+__global__ __launch_bounds__(kThreads, 2) void wgrad_kernel(WgradPlan P) {
+  __shared__ alignas(16) float Qt[kWgDepth][128][kQtLd];
   // locate the job: items are laid out job by job; each job has its own
   // column width (from its rank) and therefore its own item count
   int item = blockIdx.x;
@@ -212,10 +309,10 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradPlan P) {
   const int kind = item < nb_db ? 0 : 1;
   const int chunk = kind == 0 ? item : item - nb_db;
   switch (wgrad_kb(P.job_rank[job])) {
-    case 1: wgrad_item<1, wgrad_qn(1)>(P, job, kind, chunk, Qt); break;
-    case 2: wgrad_item<2, wgrad_qn(2)>(P, job, kind, chunk, Qt); break;
-    case 4: wgrad_item<4, wgrad_qn(4)>(P, job, kind, chunk, Qt); break;
-    default: wgrad_item<8, wgrad_qn(8)>(P, job, kind, chunk, Qt); break;
+    case 1: wgrad_item<1, wgrad_qn(1), GATHER>(P, job, kind, chunk, Qt); break;
+    case 2: wgrad_item<2, wgrad_qn(2), GATHER>(P, job, kind, chunk, Qt); break;
+    case 4: wgrad_item<4, wgrad_qn(4), GATHER>(P, job, kind, chunk, Qt); break;
+    default: wgrad_item<8, wgrad_qn(8), GATHER>(P, job, kind, chunk, Qt); break;
   }
 }
 
@@ -225,7 +322,10 @@ int wgrad_items_for_rank(int rank, int h_in, int h_out) {
 }
 
 hipError_t launch_wgrad(const WgradPlan& P, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(kThreads), 0, stream, P);
+  if (P.token_rows)
+    hipLaunchKernelGGL(wgrad_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, P);
+  else
+    hipLaunchKernelGGL(wgrad_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, P);
   return hipGetLastError();
 }
 

@@ -731,9 +731,12 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
       for (size_t q = 0; q < jobs.size(); ++q)
         if (!done[q] && q != j && jobs[q].adapter == J.adapter && jobs[q].accum < J.accum) earlier_pending = true;
       if (earlier_pending) continue;
+      W.job_item0[nj] = grid;
       W.job_adapter[nj] = J.adapter;
       W.job_seg0[nj] = nseg;
       W.job_nseg[nj] = (int)J.segs.size();
+      W.job_nsteps[nj] = 0;
+      for (auto& p : J.segs) W.job_nsteps[nj] += cdiv(p.second, kTileM);
       W.job_accum[nj] = J.accum;
       W.job_scale[nj] = J.scale;
       W.job_rank[nj] = J.rank;
@@ -746,6 +749,7 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
     }
     if (nj == 0) return fail(LORA_DEVICE_ERROR, "internal planner error (no weight-gradient job placed)");
     W.n_jobs = nj;
+    W.job_item0[nj] = grid;
     const hipError_t e = launch_wgrad(W, grid, strm);
     if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "weight-gradient launch failed: %s", hipGetErrorString(e));
   }

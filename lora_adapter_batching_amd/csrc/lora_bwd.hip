@@ -225,8 +225,7 @@ __device__ __forceinline__ void wgrad_item(const WgradPlan& P, int job, int kind
 
   const int seg0 = P.job_seg0[job];
   const int seg_end = seg0 + P.job_nseg[job];
-  int nsteps = 0;
-  for (int q = seg0; q < seg_end; ++q) nsteps += (P.seg_ntok[q] + 31) >> 5;
+  const int nsteps = P.job_nsteps[job];
   WgCursor lc{seg0, 0, 0};
   if (seg0 < seg_end) {
     lc.t0 = P.seg_tok0[seg0];
@@ -271,19 +270,29 @@ __device__ __forceinline__ void wgrad_item(const WgradPlan& P, int job, int kind
       const int m = 4 * g + i;
       const int cb = c0 + QN * m;
       if (cb >= ncols) continue;
-      if (is_db) {
+      float v[QN];
 #pragma unroll
-        for (int q = 0; q < QN; ++q) {
-          float* o = out + (int64_t)(cb + q) * rank + k;
-          const float v = oscale * acc[q][kb][i];
-          *o = accum ? (*o + v) : v;
+      for (int q = 0; q < QN; ++q) v[q] = oscale * acc[q][kb][i];
+      if (is_db) {
+        // dB_i [h_out][r]: lanes cl write consecutive ranks of one column
+        float* o = out + (int64_t)cb * rank + k;
+        if (accum) {
+#pragma unroll
+          for (int q = 0; q < QN; ++q) o[(int64_t)q * rank] += v[q];
+        } else {
+#pragma unroll
+          for (int q = 0; q < QN; ++q) o[(int64_t)q * rank] = v[q];
         }
       } else {
+        // dA_i [r][h_in]: the lane's QN columns are contiguous
         float* o = out + (int64_t)k * ncols + cb;
+        if constexpr (QN == 4) {
+          f32x4 w = f32x4{v[0], v[1], v[2], v[3]};
+          if (accum) w += *reinterpret_cast<const f32x4*>(o);
+          *reinterpret_cast<f32x4*>(o) = w;
+        } else {
 #pragma unroll
-        for (int q = 0; q < QN; ++q) {
-          const float v = oscale * acc[q][kb][i];
-          o[q] = accum ? (o[q] + v) : v;
+          for (int q = 0; q < QN; ++q) o[q] = accum ? o[q] + v[q] : v[q];
         }
       }
     }
@@ -293,21 +302,22 @@ __device__ __forceinline__ void wgrad_item(const WgradPlan& P, int job, int kind
 template <bool GATHER>
 __global__ __launch_bounds__(kThreads, 2) void wgrad_kernel(WgradPlan P) {
   __shared__ alignas(16) float Qt[kWgDepth][128][kQtLd];
-  // locate the job: items are laid out job by job; each job has its own
-  // column width (from its rank) and therefore its own item count
-  int item = blockIdx.x;
-  int job = 0;
-  int per = 0, nb_db = 0;
-  for (; job < P.n_jobs; ++job) {
-    const int cw = wgrad_cw(P.job_rank[job]);
-    nb_db = (P.h_out + cw - 1) / cw;
-    per = nb_db + (P.h_in + cw - 1) / cw;
-    if (item < per) break;
-    item -= per;
+  __shared__ int job_of_item;
+  // locate the job with one parallel read of the item table (thread j checks
+  // job j); items are laid out job by job, dB chunks before dA chunks
+  const int item = blockIdx.x;
+  {
+    const int j = min((int)threadIdx.x, kMaxJobs - 1);
+    const int i0 = P.job_item0[j], i1 = P.job_item0[j + 1];
+    if ((int)threadIdx.x < P.n_jobs && item >= i0 && item < i1) job_of_item = j;
   }
-  if (job >= P.n_jobs) return;
-  const int kind = item < nb_db ? 0 : 1;
-  const int chunk = kind == 0 ? item : item - nb_db;
+  __syncthreads();
+  const int job = __builtin_amdgcn_readfirstlane(job_of_item);
+  const int cw = wgrad_cw(P.job_rank[job]);
+  const int nb_db = (P.h_out + cw - 1) / cw;
+  const int local = item - P.job_item0[job];
+  const int kind = local < nb_db ? 0 : 1;
+  const int chunk = kind == 0 ? local : local - nb_db;
   switch (wgrad_kb(P.job_rank[job])) {
     case 1: wgrad_item<1, wgrad_qn(1), GATHER>(P, job, kind, chunk, Qt); break;
     case 2: wgrad_item<2, wgrad_qn(2), GATHER>(P, job, kind, chunk, Qt); break;

@@ -36,6 +36,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mk_rsrc(const void* base, int6
   void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
   return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, kRsrcWord3);
 }
+// The same descriptor as four scalar words, for the LDS-destination load
+// below (issued as inline assembly so that the compiler neither reorders it
+// nor inserts its own conservative waits for it: callers wait explicitly).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 mk_rsrc_words(const void* base, int64_t bytes) {
+  const int64_t cap = 0x7ffffff0;
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)));
+  r[3] = kRsrcWord3;
+  return r;
+}
+// Loads 16 bytes per lane from byte offset voff of the buffer straight into
+// LDS: lane l's bytes land at LDS byte address lds_addr + 16 l (lds_addr
+// wave-uniform). Lanes whose offset is outside the buffer write zeros. The
+// load counts in vmcnt like any vector load.
+// M0 (which holds the LDS address) is declared as an output of the
+// statement, so the compiler keeps no value of its own in it across the load.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  int m0_out;
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
+               : "={m0}"(m0_out)
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory");
+  (void)m0_out;
+}
+
 // kNT marks an access non-temporal (data streamed once: activations and
 // outputs), so that it does not displace reused adapter weights from L2.
 constexpr int kNT = 2;

@@ -100,37 +100,57 @@ __device__ __forceinline__ void lds_sync() { __syncthreads(); }
 
 // ---------------------------------------------------------------------------
 // Chunk geometry for RB 32-row rank blocks (rank <= 32 * RB).
+//
+// Shrink chunks are loaded straight into LDS, one 1 KB block per wave
+// instruction (lane l's 16 bytes land at block + 16 l). A block holds R whole
+// rows of the chunk (KC elements each); the block stride is padded by R
+// 16-byte slots, and slot (row q of the block, 16-byte column c) is
+// SR q + (c ^ q): the 32 rows of an MFMA fragment then fall on distinct
+// bank groups, and every instruction still reads whole rows from memory.
 // ---------------------------------------------------------------------------
 template <int RB>
 struct Geo {
-  static constexpr int KC = RB == 1 ? 256 : 128;           // shrink k-chunk (elements)
-  static constexpr int KCP = KC + 8;                       // LDS row of X / W (elements)
-  static constexpr int CW = RB == 1 ? 256 : 128;           // expand column chunk
-  static constexpr int CWP = CW + 8;                       // LDS row of y (elements)
-  static constexpr int RP = 32 * RB + 8;                   // LDS row of V (elements)
-  static constexpr int XV = (32 * KC / 8) / kThreads;      // X vectors per thread
-  static constexpr int WV = (32 * RB * KC / 8) / kThreads; // W vectors per thread
-  static constexpr int YV = (32 * CW / 8) / kThreads;      // y vectors per thread
-  static constexpr int VV = (CW * 4 * RB) / kThreads;      // V vectors per thread (at most)
-  static constexpr int SHRINK_BYTES = (32 + 32 * RB) * KCP * 2;
+  static constexpr int KC = RB == 1 ? 256 : (RB == 2 ? 128 : 64);  // shrink k-chunk (elements)
+  static constexpr int R = 1024 / (2 * KC);                       // rows per LDS block
+  static constexpr int SR = 64 / R;                               // 16-byte slots per row
+  static constexpr int BS = 1024 + 16 * R;                        // LDS block stride (bytes)
+  static constexpr int NBX = 32 / R;                              // blocks of X rows
+  static constexpr int NBW = 32 * RB / R;                         // blocks of W rows
+  static constexpr int BPW = (NBX + NBW) / 4;                     // block loads per wave
+  static constexpr int SHRINK_BYTES = (NBX + NBW) * BS;
+  static constexpr int CW = RB == 1 ? 256 : 128;                  // expand column chunk
+  static constexpr int CWP = CW + 8;                              // LDS row of y (elements)
+  static constexpr int RP = 32 * RB + 8;                          // LDS row of V (elements)
+  static constexpr int YV = (32 * CW / 8) / kThreads;             // y vectors per thread
+  static constexpr int VV = (CW * 4 * RB) / kThreads;             // V vectors per thread (at most)
   static constexpr int EXPAND_BYTES = 32 * CWP * 2 + CW * RP * 2;
-  static constexpr int STAGE_BYTES = SHRINK_BYTES > EXPAND_BYTES ? SHRINK_BYTES : EXPAND_BYTES;
+  static_assert(NBX % 4 == 0 && NBW % 4 == 0, "block loads split evenly over the waves");
 };
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
-constexpr int kRedBytes = 4 * 16 * 64 * 4;  // wave-reduction buffer
+constexpr int kRedBytes = 4 * 16 * 64 * 4;             // wave-reduction buffer
+constexpr int kPlBytes = kTileM * kLdp * 4;             // the tile's P (fp32)
 template <int RBMAX>
-struct StageBytes {
-  static constexpr int v = cmax(cmax(Geo<1>::STAGE_BYTES, RBMAX >= 2 ? Geo<2>::STAGE_BYTES : 0),
-                                cmax(RBMAX >= 4 ? Geo<4>::STAGE_BYTES : 0, kRedBytes));
+struct LdsBytes {
+  static constexpr int shrink = cmax(Geo<1>::SHRINK_BYTES, cmax(RBMAX >= 2 ? Geo<2>::SHRINK_BYTES : 0,
+                                                                RBMAX >= 4 ? Geo<4>::SHRINK_BYTES : 0));
+  static constexpr int expand = cmax(Geo<1>::EXPAND_BYTES, cmax(RBMAX >= 2 ? Geo<2>::EXPAND_BYTES : 0,
+                                                                RBMAX >= 4 ? Geo<4>::EXPAND_BYTES : 0));
+  // buffer 0: shrink chunks, the wave reduction, the expand stage
+  static constexpr int b0 = cmax(shrink, cmax(expand, kRedBytes));
+  // buffer 1: shrink chunks, the tile's P
+  static constexpr int b1 = cmax(shrink, kPlBytes);
 };
 
-template <int RBMAX>
-struct Smem {
-  alignas(16) uint8_t stage[StageBytes<RBMAX>::v];  // staged chunks, or the reduction buffer
-  alignas(16) float Pl[kTileM * kLdp];              // the tile's P (fp32)
-  TileInfo ti;
-  int flag;
+// The workgroup's LDS. The two buffers are separate arrays so that the
+// compiler can tell loads into one from reads of the other.
+struct Lds {
+  uint8_t* b0;
+  uint8_t* b1;
+  TileInfo* ti;
+  int* flag;
+  __device__ float* Pl() const { return reinterpret_cast<float*>(b1); }
+  __device__ float* red() const { return reinterpret_cast<float*>(b0); }
 };
 
 // Rows of a tile as a buffer resource: based at the tile's first row when
@@ -161,122 +181,131 @@ __device__ __forceinline__ uint32_t row_off(const PT& P, const TileInfo& t, cons
 }
 
 // ---------------------------------------------------------------------------
-// Shrink over k in [kb, ke). Chunk j of the loop covers KC columns of the 32
-// X rows of the tile and of the 32*RB W rows; thread t moves the 16-byte
-// vectors t, t + 256, ... of the chunk (row-major), so a wave reads whole row
-// runs. Rows past the tile or the rank read as zero. The 4 waves split each
-// chunk's k-steps; acc[b] holds P^T rows 32b.. of the wave's partial sum.
+// Shrink over k in [kb, ke). Chunk c covers KC columns of the tile's 32 X rows
+// and of the 32*RB W rows; rows past the tile or the rank, and columns past
+// ke, land in LDS as zeros (out-of-range buffer lanes write zeros). Wave w
+// loads blocks w, w+4, ...; the 4 waves then split the chunk's k-steps and
+// read MFMA fragments from LDS; acc[b] holds P^T rows 32b.. of the wave's
+// partial sum. Chunks alternate between the two LDS buffers, so chunk c+1 is
+// in flight while chunk c is computed.
 // ---------------------------------------------------------------------------
-template <int RB>
-struct ShrinkRegs {
-  u32x4 x[Geo<RB>::XV];
-  u32x4 w[Geo<RB>::WV];
-};
+// s_waitcnt immediates (gfx9 encoding): vmcnt(n) alone, lgkmcnt(0) alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier without the memory fence of __syncthreads: the caller
+// waits for exactly the memory operations the other waves depend on.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int RB>
 struct ShrinkCtx {
-  __amdgpu_buffer_rsrc_t xr, wr;
-  uint32_t xoff[Geo<RB>::XV];  // byte offset of this thread's X rows
-  uint32_t woff[Geo<RB>::WV];  // byte offset of this thread's W rows
+  i32x4 xr, wr;
+  uint32_t roff[Geo<RB>::BPW];  // byte offset of this lane's row in each of the wave's blocks
+  uint32_t cbytes;              // this lane's column within a chunk (bytes)
   int kb, ke;
 };
 
+// Issues the wave's block loads of chunk `chunk` into `buf`.
 template <int RB>
-__device__ __forceinline__ void shrink_load(const ShrinkCtx<RB>& C, int chunk, ShrinkRegs<RB>& R) {
+__device__ __forceinline__ void shrink_issue(const ShrinkCtx<RB>& C, int chunk, uint8_t* buf, int wave) {
   using G = Geo<RB>;
-  constexpr int VPR = G::KC / 8;  // vectors per row of a chunk
-  const int k = C.kb + chunk * G::KC + 8 * (threadIdx.x % VPR);  // same column for every j
+  const int k0 = C.kb + chunk * G::KC;
+  const int k = k0 + (int)(C.cbytes >> 1);
   const bool kv = k < C.ke;
-  const uint32_t kbytes = 2u * (uint32_t)k;
+  const uint32_t kbytes = 2u * (uint32_t)k0 + C.cbytes;
+  // block wave + 4 j; NBX is a multiple of 4, so j < NBX / 4 are the X blocks.
+  // The LDS destination must be scalar (it goes to M0).
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)((uint32_t)reinterpret_cast<uintptr_t>(buf) + (uint32_t)wave * G::BS));
 #pragma unroll
-  for (int j = 0; j < G::XV; ++j) R.x[j] = bld16(C.xr, kv ? C.xoff[j] + kbytes : kOff);
+  for (int j = 0; j < G::NBX / 4; ++j) load_lds16(C.xr, base + 4u * j * G::BS, kv ? C.roff[j] + kbytes : kOff);
 #pragma unroll
-  for (int j = 0; j < G::WV; ++j) R.w[j] = bld16(C.wr, kv ? C.woff[j] + kbytes : kOff);
+  for (int j = G::NBX / 4; j < G::BPW; ++j)
+    load_lds16(C.wr, base + 4u * j * G::BS, kv ? C.roff[j] + kbytes : kOff);
 }
 
+// Byte offset in a chunk buffer of 16-byte column c of row `row` of the x
+// (w = false) or W (w = true) rows.
 template <int RB>
-__device__ __forceinline__ void shrink_to_lds(const ShrinkRegs<RB>& R, uint16_t* xs, uint16_t* ws) {
+__device__ __forceinline__ uint32_t slot_off(int row, int c, bool w) {
   using G = Geo<RB>;
-  constexpr int VPR = G::KC / 8;
-  constexpr int RPJ = kThreads / VPR;  // rows per j
-  const int r0 = threadIdx.x / VPR, c = 8 * (threadIdx.x % VPR);
-#pragma unroll
-  for (int j = 0; j < G::XV; ++j) st16(xs + (r0 + RPJ * j) * G::KCP + c, R.x[j]);
-#pragma unroll
-  for (int j = 0; j < G::WV; ++j) st16(ws + (r0 + RPJ * j) * G::KCP + c, R.w[j]);
+  const int q = row % G::R;
+  return (uint32_t)(((w ? G::NBX : 0) + row / G::R) * G::BS + 16 * (G::SR * q + (c ^ q)));
 }
 
 template <int RB>
-__device__ __forceinline__ void shrink_mfma(const uint16_t* xs, const uint16_t* ws, int wave, int lane,
-                                            f32x16 (&acc)[RB]) {
+__device__ __forceinline__ void shrink_mfma(const uint8_t* buf, int wave, int lane, f32x16 (&acc)[RB]) {
   using G = Geo<RB>;
   constexpr int SPW = G::KC / 64;  // k-steps of 16 per wave per chunk
   const int h = lane >> 5, m = lane & 31;
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
-    const int k = 16 * (wave * SPW + s) + 8 * h;
-    const u32x4 xf = ld16(xs + m * G::KCP + k);
+    const int c = 2 * (wave * SPW + s) + h;
+    const u32x4 xf = ld16(buf + slot_off<RB>(m, c, false));
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-      const u32x4 wf = ld16(ws + (32 * b + m) * G::KCP + k);
+      const u32x4 wf = ld16(buf + slot_off<RB>(32 * b + m, c, true));
       acc[b] = mfma32(as_bf16x8(wf), as_bf16x8(xf), acc[b]);
     }
   }
 }
 
 template <int RB, typename PT>
-__device__ __forceinline__ void shrink_lds(const PT& P, const TileInfo& t, int kb, int ke, uint8_t* stage,
+__device__ __forceinline__ void shrink_lds(const PT& P, const TileInfo& t, int kb, int ke, const Lds& L,
                                            f32x16 (&acc)[RB]) {
   using G = Geo<RB>;
-  constexpr int VPR = G::KC / 8;
-  constexpr int RPJ = kThreads / VPR;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r0 = threadIdx.x / VPR;
+  // lane -> (row q of the block, 16-byte column c): slot lane = SR q + (c ^ q)
+  const int q = lane / G::SR;
+  const int c = (lane % G::SR) ^ q;
   ShrinkCtx<RB> C;
   const TileRows xt = tile_rows(P.X, P.ldx, P.K, P, t);
-  C.xr = xt.r;
-#pragma unroll
-  for (int j = 0; j < G::XV; ++j) C.xoff[j] = row_off(P, t, xt, r0 + RPJ * j);
+  if (xt.gather)
+    C.xr = mk_rsrc_words(P.X, (int64_t)0x7ffffff0);
+  else
+    C.xr = mk_rsrc_words(P.X + (int64_t)t.p0 * P.ldx, ((int64_t)(t.cnt - 1) * P.ldx + P.K) * 2);
   const uint32_t ldw2 = 2u * (uint32_t)P.K;
-  C.wr = mk_rsrc(w_ptr(P, t), (int64_t)t.rank * ldw2);  // rows >= rank fall outside
+  C.wr = mk_rsrc_words(w_ptr(P, t), (int64_t)t.rank * ldw2);  // rows >= rank fall outside
 #pragma unroll
-  for (int j = 0; j < G::WV; ++j) C.woff[j] = (uint32_t)(r0 + RPJ * j) * ldw2;
+  for (int j = 0; j < G::BPW; ++j) {
+    const int blk = wave + 4 * j;
+    C.roff[j] = j < G::NBX / 4 ? row_off(P, t, xt, G::R * blk + q) : (uint32_t)(G::R * (blk - G::NBX) + q) * ldw2;
+  }
+  C.cbytes = 16u * (uint32_t)c;
   C.kb = kb;
   C.ke = ke;
 #pragma unroll
   for (int b = 0; b < RB; ++b) acc[b] = zero_acc16();
-  uint16_t* xs = reinterpret_cast<uint16_t*>(stage);
-  uint16_t* ws = xs + 32 * G::KCP;
   const int nch = __builtin_amdgcn_readfirstlane((ke - kb + G::KC - 1) / G::KC);
   if (nch <= 0) return;
-  // Two register sets alternate: while chunk c is computed from LDS, the
-  // loads of chunks c+1 and c+2 are in flight. Loads past the last chunk
-  // fall outside the k range and read nothing.
-  ShrinkRegs<RB> R0, R1;
-  shrink_load<RB>(C, 0, R0);
-  shrink_load<RB>(C, 1, R1);
-  int c = 0;
-  for (; c + 2 < nch; c += 2) {
-    shrink_to_lds<RB>(R0, xs, ws);
-    lds_sync();
-    shrink_load<RB>(C, c + 2, R0);
-    shrink_mfma<RB>(xs, ws, wave, lane, acc);
-    lds_sync();
-    shrink_to_lds<RB>(R1, xs, ws);
-    lds_sync();
-    shrink_load<RB>(C, c + 3, R1);
-    shrink_mfma<RB>(xs, ws, wave, lane, acc);
-    lds_sync();
-  }
-  shrink_to_lds<RB>(R0, xs, ws);
-  lds_sync();
-  shrink_mfma<RB>(xs, ws, wave, lane, acc);
-  lds_sync();
-  if (c + 1 < nch) {
-    shrink_to_lds<RB>(R1, xs, ws);
-    lds_sync();
-    shrink_mfma<RB>(xs, ws, wave, lane, acc);
-    lds_sync();
+  // every wave's loads of a chunk must have landed before any wave reads it:
+  // wait for this wave's loads of the chunk (its later chunk may stay in
+  // flight), then barrier. Before a buffer is loaded again, every wave's
+  // reads of it must be done: wait for LDS reads, then barrier.
+  auto step = [&](uint8_t* buf, int cc) {
+    if (cc + 1 < nch)
+      wait_vmcnt<G::BPW>();
+    else
+      wait_vmcnt<0>();
+    raw_barrier();
+    shrink_mfma<RB>(buf, wave, lane, acc);
+    wait_lgkmcnt0();
+    raw_barrier();
+    if (cc + 2 < nch) shrink_issue<RB>(C, cc + 2, buf, wave);
+  };
+  shrink_issue<RB>(C, 0, L.b0, wave);
+  shrink_issue<RB>(C, 1, L.b1, wave);  // past the range: zeros, waited for below
+  for (int cc = 0; cc < nch; cc += 2) {
+    step(L.b0, cc);
+    if (cc + 1 >= nch) break;
+    step(L.b1, cc + 1);
   }
 }
 
@@ -486,10 +515,16 @@ __device__ __forceinline__ ExpCtx<RB> exp_ctx(const PT& P, const TileInfo& t, in
   return C;
 }
 
-// Runs the expand over the item's columns. R holds the first chunk's loads,
-// issued by the caller (so they can be issued before a wait).
+// Chunks of the expand whose loads are in flight (register sets).
 template <int RB>
-__device__ __forceinline__ void expand_run(const ExpCtx<RB>& C, const PFrags<RB>& F, ExpRegs<RB>& R,
+struct ExpDepth {
+  static constexpr int v = RB <= 2 ? 2 : 1;
+};
+
+// Runs the expand over the item's columns. R holds the loads of the first NE
+// chunks, issued by the caller (so they can be issued before a wait).
+template <int RB, int NE>
+__device__ __forceinline__ void expand_run(const ExpCtx<RB>& C, const PFrags<RB>& F, ExpRegs<RB> (&R)[NE],
                                            uint8_t* stage) {
   using G = Geo<RB>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -499,19 +534,29 @@ __device__ __forceinline__ void expand_run(const ExpCtx<RB>& C, const PFrags<RB>
   // the last step is zero in every V row (written once; chunks never touch it)
   if (C.vec16 && (C.ldv & 8) && threadIdx.x < G::CW)
     st16(vs + threadIdx.x * G::RP + C.ldv, zero16());
-  auto chunk = [&](int cs) {
-    exp_to_lds<RB>(C, cs, R, ys, vs);
+  auto chunk = [&](int cs, ExpRegs<RB>& Rq) {
+    exp_to_lds<RB>(C, cs, Rq, ys, vs);
     lds_sync();
-    if (cs + G::CW < C.c1) exp_load<RB>(C, cs + G::CW, R);
+    exp_load<RB>(C, cs + NE * G::CW, Rq);  // past the range: reads nothing
     exp_mfma<RB>(C, F, cs, ys, vs, wave, lane);
     lds_sync();
     exp_store<RB>(C, cs, ys);
     lds_sync();
   };
-  // the first chunk is peeled so that every pass of the loop starts with the
-  // same loads and stores pending (the next chunk's loads, then the stores)
-  if (C.c0 < C.c1) chunk(C.c0);
-  for (int cs = C.c0 + G::CW; cs < C.c1; cs += G::CW) chunk(cs);
+  // the first chunk is peeled so that the loop is entered with the same
+  // kinds of accesses pending as on its back edge (later loads, then stores)
+  if (C.c0 >= C.c1) return;
+  chunk(C.c0, R[0]);
+  int cs = C.c0 + G::CW;
+  if constexpr (NE == 1) {
+    for (; cs < C.c1; cs += G::CW) chunk(cs, R[0]);
+  } else {
+    for (; cs + G::CW < C.c1; cs += 2 * G::CW) {
+      chunk(cs, R[1]);
+      chunk(cs + G::CW, R[0]);
+    }
+    if (cs < C.c1) chunk(cs, R[1]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -594,37 +639,38 @@ template <int RB, typename PT>
 __device__ __forceinline__ void expand_from_lds(const PT& P, const TileInfo& t, int c, const float* Pl,
                                                 uint8_t* stage) {
   const ExpCtx<RB> C = exp_ctx<RB>(P, t, c);
-  ExpRegs<RB> R;
-  if (C.c0 < C.c1) exp_load<RB>(C, C.c0, R);
+  constexpr int NE = ExpDepth<RB>::v;
+  ExpRegs<RB> R[NE];
+#pragma unroll
+  for (int q = 0; q < NE; ++q) exp_load<RB>(C, C.c0 + q * Geo<RB>::CW, R[q]);  // empty ranges read nothing
   PFrags<RB> F;
   build_pfrags<RB>(Pl, t.rank, threadIdx.x & 63, F);
-  expand_run<RB>(C, F, R, stage);
+  expand_run<RB, NE>(C, F, R, stage);
 }
 
 // kModeFusedTile: full shrink of one tile on chip, then its n-chunk c.
-template <int RB, typename PT, typename SM>
-__device__ __forceinline__ void item_fused_tile(const PT& P, SM& S, const TileInfo& t, int c) {
+template <int RB, typename PT>
+__device__ __forceinline__ void item_fused_tile(const PT& P, const Lds& L, const TileInfo& t, int c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   f32x16 acc[RB];
-  shrink_lds<RB>(P, t, 0, P.K, S.stage, acc);
+  shrink_lds<RB>(P, t, 0, P.K, L, acc);
   const float ps = P.scale_in_shrink ? t.scale : 1.f;
-  float* Pl = S.Pl;
-  reduce_waves<RB>(reinterpret_cast<float*>(S.stage), acc, wave, lane,
-                   [&](int k, int n, float v) { Pl[n * kLdp + k] = v * ps; });
+  float* Pl = L.Pl();
+  reduce_waves<RB>(L.red(), acc, wave, lane, [&](int k, int n, float v) { Pl[n * kLdp + k] = v * ps; });
   if (P.write_u && c == 0) store_u_from_lds(P, t, Pl);
-  expand_from_lds<RB>(P, t, c, Pl, S.stage);
+  expand_from_lds<RB>(P, t, c, Pl, L.b0);
 }
 
 // kModeExpand: U from memory, expand n-chunk c.
-template <int RB, typename PT, typename SM>
-__device__ __forceinline__ void item_expand(const PT& P, SM& S, const TileInfo& t, int c) {
-  float* Pl = S.Pl;
+template <int RB, typename PT>
+__device__ __forceinline__ void item_expand(const PT& P, const Lds& L, const TileInfo& t, int c) {
+  float* Pl = L.Pl();
   for (int e = threadIdx.x; e < kTileM * 32 * RB; e += kThreads) {
     const int n = e / (32 * RB), k = e - n * (32 * RB);
     Pl[n * kLdp + k] = (n < t.cnt && k < t.rank) ? P.U[(int64_t)(t.p0 + n) * P.ldu + k] : 0.f;
   }
   lds_sync();
-  expand_from_lds<RB>(P, t, c, Pl, S.stage);
+  expand_from_lds<RB>(P, t, c, Pl, L.b0);
 }
 
 template <typename PT>
@@ -633,14 +679,14 @@ __device__ __forceinline__ float* partial_ptr(const PT& P, int g, int c) {
 }
 
 // kModeShrink / kModeFusedDep phase A: shrink over k-chunk c.
-template <int RB, typename PT, typename SM>
-__device__ __forceinline__ void item_shrink(const PT& P, SM& S, const TileInfo& t, int c) {
+template <int RB, typename PT>
+__device__ __forceinline__ void item_shrink(const PT& P, const Lds& L, const TileInfo& t, int c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kb = c * P.kchunk;
   const int ke = min(P.K, kb + P.kchunk);
   f32x16 acc[RB];
-  shrink_lds<RB>(P, t, kb, ke, S.stage, acc);
-  float* red = reinterpret_cast<float*>(S.stage);
+  shrink_lds<RB>(P, t, kb, ke, L, acc);
+  float* red = L.red();
   const float ps = P.scale_in_shrink ? t.scale : 1.f;
   if (P.mode == kModeShrink && P.ks == 1) {
     reduce_waves<RB>(red, acc, wave, lane, [&](int k, int n, float v) {
@@ -662,11 +708,11 @@ __device__ __forceinline__ void item_shrink(const PT& P, SM& S, const TileInfo& 
   const int old = xwg_signal(ctr);
   // storing the returned count makes thread 0 wait for its increment to be
   // performed before anything later (e.g. the done count) is issued
-  if (threadIdx.x == 0) S.flag = old;
+  if (threadIdx.x == 0) *L.flag = old;
   if (P.mode == kModeFusedDep) return;
   // kModeShrink, ks > 1: the last arriving chunk sums all chunks in order
   __syncthreads();
-  if (S.flag != P.ks - 1) return;
+  if (*L.flag != P.ks - 1) return;
   xwg_acquire();
   for (int e = threadIdx.x; e < kTileM * t.rank; e += kThreads) {
     const int n = e / t.rank, k = e - n * t.rank;
@@ -682,15 +728,17 @@ __device__ __forceinline__ void item_shrink(const PT& P, SM& S, const TileInfo& 
 // If the chunks do not arrive within spin_ticks (e.g. their workgroups are
 // not resident), the item computes the same chunks itself in the same order,
 // so the result is identical and no wait is unbounded.
-template <int RB, typename PT, typename SM>
-__device__ __forceinline__ void item_expand_wait(const PT& P, SM& S, const TileInfo& t, int c) {
+template <int RB, typename PT>
+__device__ __forceinline__ void item_expand_wait(const PT& P, const Lds& L, const TileInfo& t, int c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int* ctr = P.counters + kCtrTiles + t.g;
   // y rows and expand weights do not depend on the shrink: issue the first
   // chunk's loads before waiting
   const ExpCtx<RB> C = exp_ctx<RB>(P, t, c);
-  ExpRegs<RB> R;
-  exp_load<RB>(C, C.c0, R);  // an empty column range reads nothing
+  constexpr int NE = ExpDepth<RB>::v;
+  ExpRegs<RB> R[NE];
+#pragma unroll
+  for (int q = 0; q < NE; ++q) exp_load<RB>(C, C.c0 + q * Geo<RB>::CW, R[q]);  // empty ranges read nothing
   if (threadIdx.x == 0) {
     const uint64_t t0 = wall_clock64();
     int ready = 0;
@@ -699,13 +747,13 @@ __device__ __forceinline__ void item_expand_wait(const PT& P, SM& S, const TileI
       if (wall_clock64() - t0 > (uint64_t)P.spin_ticks) break;
       __builtin_amdgcn_s_sleep(1);
     }
-    S.flag = ready;
+    *L.flag = ready;
   }
   xwg_acquire();
   const float ps = P.scale_in_shrink ? t.scale : 1.f;
-  float* Pl = S.Pl;
+  float* Pl = L.Pl();
   const int rcols = 32 * RB;
-  if (S.flag) {
+  if (*L.flag) {
     const int rpad = P.rpad;
     for (int e = threadIdx.x; e < kTileM * rcols; e += kThreads) {
       const int n = e / rcols, k = e - n * rcols;
@@ -717,42 +765,51 @@ __device__ __forceinline__ void item_expand_wait(const PT& P, SM& S, const TileI
     if (P.write_u && c == 0) store_u_from_lds(P, t, Pl);
     PFrags<RB> F;
     build_pfrags<RB>(Pl, t.rank, lane, F);
-    expand_run<RB>(C, F, R, S.stage);
+    expand_run<RB, NE>(C, F, R, L.b0);
     return;
   }
   // Fallback. The early loads are dropped and issued again after the shrink
   // (a separate expand, so that they are not held in registers through it).
+  // The chunk sums run in registers (each thread always receives the same
+  // elements from the reduction) because the shrink reuses P's LDS buffer;
+  // the last chunk's pass writes P.
+  float run[4 * RB];
   for (int q = 0; q < P.ks; ++q) {
     const int kb = q * P.kchunk;
     const int ke = min(P.K, kb + P.kchunk);
     f32x16 acc[RB];
-    shrink_lds<RB>(P, t, kb, ke, S.stage, acc);
-    reduce_waves<RB>(reinterpret_cast<float*>(S.stage), acc, wave, lane, [&](int k, int n, float v) {
-      Pl[n * kLdp + k] = (q == 0) ? v : Pl[n * kLdp + k] + v;
+    shrink_lds<RB>(P, t, kb, ke, L, acc);
+    int idx = 0;
+    const bool last = q == P.ks - 1;
+    reduce_waves<RB>(L.red(), acc, wave, lane, [&](int k, int n, float v) {
+      const float sum = (q == 0) ? v : run[idx] + v;
+      run[idx] = sum;
+      if (last) Pl[n * kLdp + k] = sum * ps;
+      ++idx;
     });
-  }
-  for (int e = threadIdx.x; e < kTileM * rcols; e += kThreads) {
-    const int n = e / rcols, k = e - n * rcols;
-    Pl[n * kLdp + k] *= ps;
   }
   lds_sync();
   if (P.write_u && c == 0) store_u_from_lds(P, t, Pl);
-  expand_from_lds<RB>(P, t, c, Pl, S.stage);
+  expand_from_lds<RB>(P, t, c, Pl, L.b0);
 }
 
-template <int RB, typename PT, typename SM>
-__device__ __forceinline__ void run_item(const PT& P, SM& S, const TileInfo& t, int kind, int c) {
+template <int RB, typename PT>
+__device__ __forceinline__ void run_item(const PT& P, const Lds& L, const TileInfo& t, int kind, int c) {
   switch (kind) {
-    case 0: item_shrink<RB>(P, S, t, c); break;
-    case 1: item_expand<RB>(P, S, t, c); break;
-    case 2: item_fused_tile<RB>(P, S, t, c); break;
-    default: item_expand_wait<RB>(P, S, t, c); break;
+    case 0: item_shrink<RB>(P, L, t, c); break;
+    case 1: item_expand<RB>(P, L, t, c); break;
+    case 2: item_fused_tile<RB>(P, L, t, c); break;
+    default: item_expand_wait<RB>(P, L, t, c); break;
   }
 }
 
 template <int RBMAX, typename PT>
-__global__ __launch_bounds__(kThreads, RBMAX <= 2 ? 3 : 2) void sgmv_fwd_kernel(PT P) {
-  __shared__ Smem<RBMAX> S;
+__global__ __launch_bounds__(kThreads, 2) void sgmv_fwd_kernel(PT P) {
+  __shared__ alignas(16) uint8_t lds_b0[LdsBytes<RBMAX>::b0];
+  __shared__ alignas(16) uint8_t lds_b1[LdsBytes<RBMAX>::b1];
+  __shared__ TileInfo lds_ti;
+  __shared__ int lds_flag;
+  const Lds L{lds_b0, lds_b1, &lds_ti, &lds_flag};
   const int b = blockIdx.x;
   int item = -1, kind = 0, per = 1;
   if (P.mode == kModeFusedDep) {
@@ -770,10 +827,10 @@ __global__ __launch_bounds__(kThreads, RBMAX <= 2 ? 3 : 2) void sgmv_fwd_kernel(
   }
   if (item >= 0) {
     const int g = item / per, c = item - g * per;
-    const TileInfo t = tile_info(P, g, &S.ti);
-    if (RBMAX == 1 || t.rank <= 32) run_item<1>(P, S, t, kind, c);
-    else if (RBMAX == 2 || t.rank <= 64) run_item<(RBMAX >= 2 ? 2 : 1)>(P, S, t, kind, c);
-    else run_item<RBMAX>(P, S, t, kind, c);
+    const TileInfo t = tile_info(P, g, L.ti);
+    if (RBMAX == 1 || t.rank <= 32) run_item<1>(P, L, t, kind, c);
+    else if (RBMAX == 2 || t.rank <= 64) run_item<(RBMAX >= 2 ? 2 : 1)>(P, L, t, kind, c);
+    else run_item<RBMAX>(P, L, t, kind, c);
   }
   if (P.mode == kModeFusedDep) {
     // the last workgroup to finish returns every counter of this launch to

@@ -95,9 +95,8 @@ struct WgradPlan {
   int32_t h_in;
   int32_t h_out;
   int32_t n_jobs;
-  int32_t cw;      // columns per item (multiple of 128)
-  int32_t nb_db;   // items per job for dB
-  int32_t nb_da;   // items per job for dA
+  int32_t job_item0[kMaxJobs + 1];  // first item of each job (items: dB chunks, then dA chunks); [n_jobs] = total
+  int32_t job_nsteps[kMaxJobs];     // 32-token steps over the job's segments
   int32_t job_adapter[kMaxJobs];
   int32_t job_seg0[kMaxJobs];
   int32_t job_nseg[kMaxJobs];

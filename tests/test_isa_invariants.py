@@ -1,0 +1,74 @@
+"""Invariants of the compiled gfx950 code that the kernels rely on (CPU only:
+hipcc cross-compiles the device code to assembly; no GPU needed).
+
+- The shrink's LDS-destination loads are inline assembly that sets M0 to the
+  LDS address: every such M0 source and buffer descriptor must be a scalar
+  register, and the compiler must not use M0 anywhere else.
+- No kernel spills to scratch memory (a spill would also add vector memory
+  operations that the explicit load counts of the shrink do not expect).
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "lora_adapter_batching_amd", "csrc")
+HIPCC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+
+
+def _device_asm(src, tmp_path):
+    if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    out = tmp_path / (os.path.basename(src) + ".s")
+    cmd = [HIPCC if os.path.exists(HIPCC) else "hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
+           "--cuda-device-only", "-S", "-o", str(out), src]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def fwd_asm(tmp_path_factory):
+    return _device_asm(os.path.join(CSRC, "lora_fwd.hip"), tmp_path_factory.mktemp("asm"))
+
+
+@pytest.fixture(scope="module")
+def bwd_asm(tmp_path_factory):
+    return _device_asm(os.path.join(CSRC, "lora_bwd.hip"), tmp_path_factory.mktemp("asm"))
+
+
+def test_lds_loads_use_scalar_m0_and_descriptor(fwd_asm):
+    lines = fwd_asm.splitlines()
+    n_loads = 0
+    in_asm = False
+    for i, l in enumerate(lines):
+        s = l.split(";")[0].strip()
+        if "ASMSTART" in l:
+            in_asm = True
+            continue
+        if "ASMEND" in l:
+            in_asm = False
+            continue
+        if not s:
+            continue
+        if in_asm:
+            m = re.match(r"s_mov_b32 m0, (\S+)", s)
+            if m:
+                assert re.fullmatch(r"s\d+", m.group(1)), f"line {i}: M0 from {m.group(1)}"
+            m = re.match(r"buffer_load_dwordx4 v\d+, (\S+), 0 offen lds", s)
+            if m:
+                n_loads += 1
+                assert re.fullmatch(r"s\[\d+:\d+\]", m.group(1)), f"line {i}: descriptor {m.group(1)}"
+        else:
+            assert not re.search(r"\bm0\b", s), f"line {i}: compiler use of M0: {s}"
+    assert n_loads > 0
+
+
+def test_no_scratch(fwd_asm, bwd_asm):
+    for text in (fwd_asm, bwd_asm):
+        sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", text)
+        assert sizes and all(int(v) == 0 for v in sizes), sizes

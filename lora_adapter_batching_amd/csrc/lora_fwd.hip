@@ -34,10 +34,6 @@ struct TileInfo {
   float scale;
 };
 
-// Finds the segment that holds tile g with one parallel read of the segment
-// table: thread i checks segment i and the matching thread publishes the
-// tile's description in LDS (a binary search would chain several dependent
-// loads of the kernel-argument table).
 template <typename PT>
 struct PlanCap;
 template <int CAP>
@@ -45,8 +41,30 @@ struct PlanCap<FwdPlanT<CAP>> {
   static constexpr int v = CAP;  // segment capacity of a plan type
 };
 
+// Finds the segment that holds tile g. Small plans (decode batches): a scalar
+// scan of the whole table, which the compiler reads from the kernel
+// arguments with a few wide scalar loads, with no LDS round trip or barrier.
+// Large plans: one parallel read of the table (thread i checks segment i and
+// the matching thread publishes the tile's description in LDS).
 template <typename PT>
 __device__ __forceinline__ TileInfo tile_info(const PT& P, int g, TileInfo* lds) {
+  constexpr int CAP = PlanCap<PT>::v;
+  if constexpr (CAP <= kSmallSeg) {
+    int sel = 0;
+#pragma unroll
+    for (int i = 1; i < CAP; ++i)
+      if (i < P.n_seg && g >= P.seg_tile0[i]) sel = i;
+    TileInfo t;
+    const int tt = g - P.seg_tile0[sel];
+    t.g = g;
+    t.p0 = P.seg_tok0[sel] + tt * kTileM;
+    t.cnt = min(kTileM, P.seg_ntok[sel] - tt * kTileM);
+    t.adapter = P.seg_adapter[sel];
+    t.rank = P.seg_rank[sel];
+    t.slot = P.seg_slot[sel];
+    t.scale = P.seg_scale[sel];
+    return t;
+  }
   // the table reads do not wait for n_seg: entries past it are in the plan
   // too, and only the comparison uses n_seg
   const int i = min((int)threadIdx.x, PlanCap<PT>::v - 1);

@@ -270,6 +270,26 @@ def _entry(name, seconds, bytes_, flops, extra=None):
     return d
 
 
+def copy_ceiling_gbs(nbytes=1 << 30, reps=10):
+    """Achievable HBM rate of a plain device-to-device copy (read + write
+    bytes per second), timed with HIP events: the practical ceiling next to
+    the 8 TB/s datasheet peak."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    e1.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b
+    return 2.0 * nbytes / sec / 1e9
+
+
 def bench_secondary(reps=20):
     import torch
     import lora_adapter_batching_amd as L
@@ -383,6 +403,7 @@ def main():
             "event_every_steps": EVENT_EVERY}
     gate = ds.work[2][0] / float(np.median(per_launch[:, 2])) / 1e9
     roof["gate_up_GBs"] = round(gate, 1)
+    roof["copy_ceiling_GBs"] = round(copy_ceiling_gbs(), 1)
     out = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec_per_step * 1e3, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

@@ -218,6 +218,27 @@ def test_prefill_llama3_8b_sampled():
     _check_forward(gp, ob, y, u, rows=_sample_rows(gp))
 
 
+def test_prefill_gather_shrink_expand_sampled():
+    """Prefill at full size in request order (token_rows gather/scatter), and
+    the separate shrink and expand entry points at full size."""
+    L = _L()
+    import torch
+    prob = make_config("prefill")
+    gp = GpuProblem(prob, use_token_rows=True)
+    ob = oracle_batch(prob)
+    rows = _sample_rows(gp, n=64, seed=1)
+    _say("prefill fused, token_rows")
+    y, u = _run_fused(gp)
+    _check_forward(gp, ob, y, u, rows=rows)
+    _say("prefill shrink + expand, token_rows")
+    u2 = gp.new_u()
+    L.sgmv_shrink(gp.x, gp.adapters, gp.segments, u2, L.new_workspace(L.OP_SHRINK, gp.adapters, gp.segments))
+    y2 = gp.new_y()
+    L.sgmv_expand(u2, gp.adapters, gp.segments, y2)
+    torch.cuda.synchronize()
+    _check_forward(gp, ob, y2, u2, rows=rows)
+
+
 def test_hetero_mlp_up_sampled():
     prob = make_config("hetero")
     gp = GpuProblem(prob)
@@ -298,6 +319,39 @@ def test_backward_mixed(mode):
     dx, dA, dB = _run_backward(gp, u=u, with_dx=(mode != "no_dx"))
     _check_backward(gp, ob, dx, dA, dB)
     assert float(dA[7].abs().max()) == 0.0 and float(dB[7].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_backward_many_adapters_and_segments(flags):
+    """70 adapters (two transpose groups, two weight-gradient launches) and
+    one adapter spread over 150 segments (its token reduction is split into
+    parts that must run in order)."""
+    import torch
+    L = _L()
+    rng = np.random.default_rng(21)
+    N = 70
+    ranks = [int(r) for r in rng.choice([0, 4, 8, 16], size=N)]
+    ranks[0] = 8
+    lens, ads = [], []
+    for g in range(150):  # adapter 0 in 150 short segments, interleaved with others
+        lens.append(int(rng.integers(1, 4)))
+        ads.append(0)
+        lens.append(int(rng.integers(0, 5)))
+        ads.append(int(rng.integers(-1, N)))
+    prob = make_custom(22, 64, 40, ranks, scales="random", seg_lens=lens, seg_adapter=ads, with_dy=True)
+    gp = GpuProblem(prob)
+    ob = oracle_batch(prob)
+    dA0 = dB0 = None
+    dA = dB = None
+    if flags:
+        g = np.random.default_rng(23)
+        dA = [torch.tensor(g.standard_normal((r, prob.h_in)), dtype=torch.float32, device="cuda") for r in ranks]
+        dB = [torch.tensor(g.standard_normal((prob.h_out, r)), dtype=torch.float32, device="cuda") for r in ranks]
+        dA0 = [to_f64(t) for t in dA]
+        dB0 = [to_f64(t) for t in dB]
+    _say(f"backward 70 adapters, 300 segments, flags={flags}")
+    dx, dA, dB = _run_backward(gp, u=None, flags=flags, dA=dA, dB=dB)
+    _check_backward(gp, ob, dx, dA, dB, dA0=dA0, dB0=dB0)
 
 
 def test_backward_accumulate():

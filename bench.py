@@ -186,16 +186,17 @@ class DecodeStep:
         calls = self.sets[i % len(self.sets)]
         segp = ctypes.byref(self.cseg)
         for j, (xp, ldx, adc, yp, ldy, wsp, wsb) in enumerate(calls):
-            if events is not None:
-                events[j][0].record()
+            ev = events if events is not None and events[0] == j else None
+            if ev is not None:
+                ev[1].record()
             st = lib.lora_sgmv_fused(xp, ldx, adc, segp, yp, ldy, None, 0, wsp, wsb, self.stream)
-            if events is not None:
-                events[j][1].record()
+            if ev is not None:
+                ev[2].record()
             if st:
                 raise RuntimeError(lib.lora_last_error().decode())
 
 
-EVENT_EVERY = 8  # steps between the steps whose launches carry timing events
+EVENT_EVERY = 8  # steps between the steps that carry a pair of timing events
 
 
 def bench_decode(steps, warmup, nsets=16):
@@ -206,20 +207,21 @@ def bench_decode(steps, warmup, nsets=16):
     for i in range(warmup):
         ds.step(i)
     torch.cuda.synchronize()
-    # timed region: wall clock for value; HIP events around every fused launch
-    # of every EVENT_EVERY-th step (a timing event costs a few microseconds of
-    # GPU time, so recording them on every launch would slow the step itself)
+    # timed region: wall clock for value; HIP events around one fused launch
+    # of every EVENT_EVERY-th step, taking the projections in turn (a timing
+    # event costs a few microseconds of GPU time, so recording them around
+    # every launch would slow the step itself)
     sampled = list(range(0, steps, EVENT_EVERY))
-    ev = {i: [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(3)]
-          for i in sampled}
+    ev = {i: (k % 3, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for k, i in enumerate(sampled)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         ds.step(warmup + i, ev.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    per_launch = np.array([[ev[i][j][0].elapsed_time(ev[i][j][1]) for j in range(3)] for i in sampled])
-    return ds, (t1 - t0) / steps, per_launch * 1e-3  # seconds
+    per_launch = [np.array([a.elapsed_time(b) for (j, a, b) in ev.values() if j == jj]) * 1e-3 for jj in range(3)]
+    return ds, (t1 - t0) / steps, per_launch  # seconds, per projection
 
 
 # ---------------------------------------------------------------------------
@@ -390,18 +392,18 @@ def main():
     ds, sec_per_step, per_launch = bench_decode(args.steps, args.warmup)
     value = ds.bytes_per_step / sec_per_step / 1e9
     # dominant kernel: the fused launch (sgmv_fwd_kernel), 3 launches per step
-    avg_launch = float(per_launch.mean())
+    avg_launch = float(np.mean([pl.mean() for pl in per_launch]))
     bytes_per_launch = ds.bytes_per_step / 3.0
     achieved = bytes_per_launch / avg_launch / 1e9
     traffic = load_traffic(WORKLOAD)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": KERNEL, "avg_launch_us": round(avg_launch * 1e6, 3),
-            "launch_us": {n: round(float(np.median(per_launch[:, j])) * 1e6, 3)
+            "launch_us": {n: round(float(np.median(per_launch[j])) * 1e6, 3)
                           for j, n in enumerate(ds.names)},
             "algorithmic_bytes_per_launch": round(bytes_per_launch),
             "event_every_steps": EVENT_EVERY}
-    gate = ds.work[2][0] / float(np.median(per_launch[:, 2])) / 1e9
+    gate = ds.work[2][0] / float(np.median(per_launch[2])) / 1e9
     roof["gate_up_GBs"] = round(gate, 1)
     roof["copy_ceiling_GBs"] = round(copy_ceiling_gbs(), 1)
     out = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,

@@ -85,6 +85,14 @@ enum { LORA_OP_SHRINK = 0, LORA_OP_EXPAND = 1, LORA_OP_FUSED = 2, LORA_OP_BACKWA
  * in GPU memory). Pointer tables are read on the device at every call, so
  * weights can be updated in place, or re-pointed, between calls without any
  * other call (same rank).
+ *
+ * A_ptrs_host / B_ptrs_host are optional HOST copies of the two tables. When
+ * both are given, forward launches of up to 16 segments carry the weight
+ * addresses in their launch arguments instead of reading the device tables
+ * (one dependent memory round trip less at the start of every workgroup,
+ * which matters for decode-sized batches). They must then hold the same
+ * addresses as the device tables at the time of the call; the library only
+ * reads them during the call. NULL (either one): the device tables are used.
  */
 typedef struct lora_adapters_t {
   int32_t num_adapters;   /* N >= 1 */
@@ -94,6 +102,8 @@ typedef struct lora_adapters_t {
   const uint64_t* B_ptrs; /* DEVICE [N]: address of bf16 B_i [h_out, r_i]; may be 0 if r_i == 0 */
   const int32_t* ranks;   /* HOST [N]: r_i in [0, 128] */
   const float* scales;    /* HOST [N]: s_i, finite */
+  const uint64_t* A_ptrs_host; /* HOST [N] or NULL: same entries as A_ptrs */
+  const uint64_t* B_ptrs_host; /* HOST [N] or NULL: same entries as B_ptrs */
 } lora_adapters_t;
 
 /*

@@ -36,7 +36,8 @@ class CAdapters(ctypes.Structure):
     _fields_ = [("num_adapters", ctypes.c_int32), ("h_in", ctypes.c_int32),
                 ("h_out", ctypes.c_int32), ("A_ptrs", ctypes.c_void_p),
                 ("B_ptrs", ctypes.c_void_p), ("ranks", ctypes.c_void_p),
-                ("scales", ctypes.c_void_p)]
+                ("scales", ctypes.c_void_p), ("A_ptrs_host", ctypes.c_void_p),
+                ("B_ptrs_host", ctypes.c_void_p)]
 
 
 class CSegments(ctypes.Structure):
@@ -116,11 +117,15 @@ class Adapters:
 
     A, B: sequences of device bf16 tensors, A[i] [r_i, h_in], B[i] [h_out, r_i]
     (None allowed for rank 0). The pointer tables are int64 device tensors,
-    so they can be rewritten in place between calls.
+    so they can be rewritten in place between calls. With host_tables (the
+    default) host copies of the tables go with every call too, and small
+    launches take the addresses from them: after rewriting a device table in
+    place, rewrite A_host / B_host (uint64 numpy arrays) the same way, or
+    build the object with host_tables=False.
     """
 
     def __init__(self, A: Sequence, B: Sequence, ranks, scales, h_in: int, h_out: int,
-                 device=None):
+                 device=None, host_tables: bool = True):
         import torch
         self.A, self.B = list(A), list(B)
         self.ranks = np.ascontiguousarray(ranks, dtype=np.int32)
@@ -129,8 +134,12 @@ class Adapters:
         dev = device if device is not None else "cuda"
         self.A_ptrs = torch.tensor([_ptr(a) for a in self.A], dtype=torch.int64, device=dev)
         self.B_ptrs = torch.tensor([_ptr(b) for b in self.B], dtype=torch.int64, device=dev)
+        self.A_host = np.array([_ptr(a) for a in self.A], dtype=np.uint64)
+        self.B_host = np.array([_ptr(b) for b in self.B], dtype=np.uint64)
         self._c = CAdapters(len(self.ranks), self.h_in, self.h_out, _ptr(self.A_ptrs),
-                            _ptr(self.B_ptrs), self.ranks.ctypes.data, self.scales.ctypes.data)
+                            _ptr(self.B_ptrs), self.ranks.ctypes.data, self.scales.ctypes.data,
+                            self.A_host.ctypes.data if host_tables else 0,
+                            self.B_host.ctypes.data if host_tables else 0)
 
     @property
     def c(self):

@@ -22,13 +22,23 @@ def hipcc() -> str:
     return p if os.path.exists(p) else "hipcc"
 
 
+# Code-generation flags of every device compile (the library and the ISA checks).
+CODEGEN_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+    # packed fp32 instructions stay disabled on this target
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the kernels read their plan (the kernel argument) in many places; above
+    # LLVM's default of 300 such reads it keeps a private copy of the plan in
+    # scratch memory instead of reading the argument itself
+    "-mllvm", "-instcombine-max-copied-from-constant-users=4096",
+]
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link the shared library."""
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           # packed fp32 instructions stay disabled on this target
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function",
-           "-o", LIB + ".tmp"]
+    cmd = [hipcc()] + CODEGEN_FLAGS + ["-fPIC", "-shared",
+                                       "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function",
+                                       "-o", LIB + ".tmp"]
     for s in SOURCES:
         src = os.path.join(CSRC, s)
         if s.endswith(".cpp"):

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -12,13 +13,15 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <unistd.h>
 #include <vector>
 
 #include "../../include/lora_sgmv.h"
 #include "lora_plan.h"
 
 namespace lora {
-hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream);
+hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream, const uint64_t* wptr,
+                      const uint64_t* vptr);
 hipError_t launch_transpose(const TransposePlan& P, hipStream_t stream);
 hipError_t launch_wgrad(const WgradPlan& P, int grid, hipStream_t stream);
 int wgrad_items_for_rank(int rank, int h_in, int h_out);
@@ -44,9 +47,8 @@ int fail(int status, const char* fmt, ...) {
 // Tunables of the planner
 // ---------------------------------------------------------------------------
 constexpr int kMaxKs = 16;            // largest split of the shrink reduction
-constexpr int kMaxPartials = 512;     // tiles * ks in split modes (bounds the workspace)
 constexpr int kMaxDepTiles = 1024 - kCtrTiles;  // counter slots
-constexpr size_t kCounterBytes = 4096;
+constexpr size_t kCounterBytes = 8192;  // tile counters, then the part stamps
 constexpr int kShrinkChunk = 1280;    // k elements per item of a split shrink
 constexpr int kMaxSlots = kMaxJobs;   // adapters per backward group
 
@@ -238,6 +240,8 @@ struct FwdCall {
   bool write_u;
   const uint64_t* Wtab;
   const uint64_t* Vtab;
+  const uint64_t* Wtab_host;  // host copies of the tables, or null
+  const uint64_t* Vtab_host;
   const uint16_t* Wslots;
   const uint16_t* Vslots;
   int64_t w_slot_elems, v_slot_elems;
@@ -252,18 +256,23 @@ struct FwdCall {
 
 // Optional planner override for tuning, read once from LORA_SGMV_FORCE:
 // "tile:NC" forces the on-chip fused mode with NC column chunks per tile,
-// "dep:KS:NC" the split-shrink mode. Applies to fused calls only.
+// "dep:KS:NC" the split-shrink mode, "loc:KS:NC" the split-shrink mode with
+// every item of a tile on one XCD. A third field ("dep:KS:NC:TICKS") sets how
+// long an expand waits for the parts before it computes the shrink itself
+// (0: one look, so most expands take that path). Applies to fused calls only.
 struct ForcePlan {
-  int mode = -1, ks = 0, nc = 0;
+  int mode = -1, ks = 0, nc = 0, local = 0, spin = -1;
 };
 ForcePlan force_plan() {
   static ForcePlan f = [] {
     ForcePlan r;
     const char* e = std::getenv("LORA_SGMV_FORCE");
     if (!e) return r;
-    int a = 0, b = 0;
+    int a = 0, b = 0, t = -1;
     if (std::sscanf(e, "tile:%d", &a) == 1 && a > 0) { r.mode = kModeFusedTile; r.nc = a; }
-    else if (std::sscanf(e, "dep:%d:%d", &a, &b) == 2 && a > 0 && b > 0) { r.mode = kModeFusedDep; r.ks = a; r.nc = b; }
+    else if (std::sscanf(e, "dep:%d:%d:%d", &a, &b, &t) >= 2 && a > 0 && b > 0) { r.mode = kModeFusedDep; r.ks = a; r.nc = b; }
+    else if (std::sscanf(e, "loc:%d:%d:%d", &a, &b, &t) >= 2 && a > 0 && b > 0) { r.mode = kModeFusedDep; r.ks = a; r.nc = b; r.local = 1; }
+    if (r.mode == kModeFusedDep && t >= 0) r.spin = t;
     return r;
   }();
   return f;
@@ -283,6 +292,29 @@ bool xcd_remap_enabled(bool small_batch) {
   return env >= 0 ? env == 1 : small_batch;
 }
 
+// A launch id that no earlier launch of any process used with the same
+// workspace: split-shrink parts are stamped with it, so a stamp left in the
+// workspace by an earlier call can never be taken for a current one.
+uint64_t next_launch_id() {
+  static std::atomic<uint64_t> next{[] {
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    return ((t << 12) ^ ((uint64_t)getpid() << 36)) & ((1ull << 56) - 1);
+  }()};
+  uint64_t id;
+  do {
+    id = next.fetch_add(1, std::memory_order_relaxed) & ((1ull << 56) - 1);
+  } while (id == 0);
+  return id;
+}
+
+// XCD-local split layout: the items of tile g (its ks shrink parts, then its
+// nc expands) run on XCD g % 8, in dispatch order parts before expands.
+// Returns the grid (8 x the largest per-XCD item count).
+int local_grid(int tiles, int ks, int nc) {
+  const int per_xcd_tiles = (tiles + 7) / 8;
+  return 8 * per_xcd_tiles * (ks + nc);
+}
+
 int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int>& slot_of,
             hipStream_t stream) {
   if (segs.empty()) return LORA_OK;
@@ -298,6 +330,8 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
     P.Wtab = c.Wtab; P.Vtab = c.Vtab; P.Wslots = c.Wslots; P.Vslots = c.Vslots;
     P.w_slot_elems = c.w_slot_elems; P.v_slot_elems = c.v_slot_elems;
     P.token_rows = c.token_rows; P.partials = c.partials; P.counters = c.counters;
+    P.stamps = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(c.counters) + kStampOffset);
+    P.launch_id = next_launch_id();
     P.K = c.K; P.N = c.N; P.v_round = c.v_round; P.scale_in_shrink = c.scale_in_shrink;
     P.write_u = c.write_u ? 1 : 0;
     P.rpad = rpad_for(c.rmax);
@@ -357,7 +391,7 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
         P.nc = cdiv(nblocks, P.nblk);
         P.n_items_a = tiles * P.nc;
         P.grid = P.n_items_a;
-      } else if (fp.mode == kModeFusedDep && tiles <= kMaxDepTiles && tiles * fp.ks <= kMaxPartials) {
+      } else if (fp.mode == kModeFusedDep && tiles * fp.ks <= kMaxPartials) {
         P.mode = kModeFusedDep;
         P.kchunk = round_up(cdiv(c.K, fp.ks), 64);
         P.ks = cdiv(c.K, P.kchunk);
@@ -365,20 +399,36 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
         P.nc = cdiv(nblocks, P.nblk);
         P.n_items_a = tiles * P.ks;
         P.n_items_b = tiles * P.nc;
-        P.grid = P.n_items_a + P.n_items_b;
+        P.xcd_local = fp.local;
+        P.grid = P.xcd_local ? local_grid(tiles, P.ks, P.nc) : P.n_items_a + P.n_items_b;
+        if (fp.spin >= 0) P.spin_ticks = fp.spin;
+      } else if (4 * tiles <= cus && xcd_remap_enabled(true)) {
+        // small batch: each tile's shrink is split along k into parts and its
+        // expand into column chunks, all on one XCD, so the parts reach the
+        // expands through that XCD's L2. About two workgroups per CU.
+        P.mode = kModeFusedDep;
+        const int per_xcd_tiles = (tiles + 7) / 8;
+        const int slots_per_xcd = 2 * cus / 8;
+        int ks = std::max(1, std::min({kMaxKs, cdiv(c.K, 512), kMaxPartials / tiles}));
+        P.kchunk = round_up(cdiv(c.K, ks), 64);
+        P.ks = cdiv(c.K, P.kchunk);
+        const int nc = std::max(1, std::min(nblocks, slots_per_xcd / per_xcd_tiles - P.ks));
+        P.nblk = cdiv(nblocks, nc);
+        P.nc = cdiv(nblocks, P.nblk);
+        P.n_items_a = tiles * P.ks;
+        P.n_items_b = tiles * P.nc;
+        P.xcd_local = 1;
+        P.grid = local_grid(tiles, P.ks, P.nc);
       } else if (4 * tiles <= cus) {
-        // small batch: at most one workgroup per CU. Each computes its tile's
-        // full shrink on chip and one column chunk of the expand: a split
-        // shrink would hand partial sums between XCDs, which costs more than
-        // the repeated shrink reads
+        // small batch without the XCD-local layout: each item computes its
+        // tile's full shrink on chip and one column chunk of the expand
         P.mode = kModeFusedTile;
         P.ks = 1;
         P.kchunk = round_up(c.K, 64);
         P.nblk = cdiv(nblocks, std::max(1, std::min(nblocks, cus / tiles)));
         P.nc = cdiv(nblocks, P.nblk);
         P.n_items_a = tiles * P.nc;
-        P.xcd_remap = xcd_remap_enabled(true) ? 1 : 0;
-        P.grid = P.xcd_remap ? round_up(P.n_items_a, 8) : P.n_items_a;
+        P.grid = P.n_items_a;
       } else if (tiles >= cus || tiles > std::min(kMaxDepTiles, kMaxPartials)) {
         // the tiles alone give every CU work: keep u on chip, one item per tile
         P.mode = kModeFusedTile;
@@ -408,7 +458,21 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
     int rmax_launch = 0;
     for (int i = 0; i < ns; ++i) rmax_launch = std::max(rmax_launch, (int)P.seg_rank[i]);
     const int rbmax = rmax_launch <= 32 ? 1 : (rmax_launch <= 64 ? 2 : 4);
-    const hipError_t e = launch_fwd(P, rbmax, stream);
+    // small plans take the weight addresses from the host copies of the
+    // tables (when the call uses tables and has the copies of those it uses)
+    uint64_t wq[kSmallSeg], vq[kSmallSeg];
+    const bool need_w = c.mode_op != LORA_OP_EXPAND, need_v = c.mode_op != LORA_OP_SHRINK;
+    if (ns <= kSmallSeg && (c.Wtab || c.Vtab) && (!need_w || (c.Wtab && c.Wtab_host)) &&
+        (!need_v || (c.Vtab && c.Vtab_host))) {
+      for (int i = 0; i < ns; ++i) {
+        const int a = segs[base + i].adapter;
+        wq[i] = need_w ? c.Wtab_host[a] : 0;
+        vq[i] = need_v ? c.Vtab_host[a] : 0;
+      }
+      P.ptrs_in_plan = 1;
+    }
+    const hipError_t e = P.ptrs_in_plan ? launch_fwd(P, rbmax, stream, wq, vq)
+                                        : launch_fwd(P, rbmax, stream, nullptr, nullptr);
     if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
   }
   return LORA_OK;
@@ -443,7 +507,7 @@ const char* lora_status_string(int status) {
 
 const char* lora_last_error(void) { return g_last_error.c_str(); }
 
-int lora_version(void) { return 100; }
+int lora_version(void) { return 200; }
 
 int lora_segments_from_ids(const int32_t* ids, int32_t T, int32_t N, int32_t* perm,
                            int32_t* seg_starts, int32_t* seg_adapter) {
@@ -508,6 +572,7 @@ int lora_sgmv_shrink(const void* x, int64_t ldx, const lora_adapters_t* adapters
   c.X = static_cast<const uint16_t*>(x); c.ldx = ldx;
   c.U = u; c.ldu = ldu;
   c.Wtab = adapters->A_ptrs; c.v_round = 1;
+  if (adapters->A_ptrs_host && adapters->B_ptrs_host) c.Wtab_host = adapters->A_ptrs_host;
   c.K = adapters->h_in; c.N = adapters->h_out;
   c.token_rows = segments->token_rows;
   c.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
@@ -534,6 +599,7 @@ int lora_sgmv_expand(const float* u, int64_t ldu, const lora_adapters_t* adapter
   c.Y = static_cast<uint16_t*>(y); c.ldy = ldy;
   c.U = const_cast<float*>(u); c.ldu = ldu;
   c.Vtab = adapters->B_ptrs; c.v_round = 1;
+  if (adapters->A_ptrs_host && adapters->B_ptrs_host) c.Vtab_host = adapters->B_ptrs_host;
   c.K = adapters->h_in; c.N = adapters->h_out;
   c.token_rows = segments->token_rows;
   c.rmax = max_rank_all(adapters);
@@ -560,6 +626,10 @@ int lora_sgmv_fused(const void* x, int64_t ldx, const lora_adapters_t* adapters,
   c.Y = static_cast<uint16_t*>(y); c.ldy = ldy;
   c.U = u_save; c.ldu = ldu; c.write_u = u_save != nullptr;
   c.Wtab = adapters->A_ptrs; c.Vtab = adapters->B_ptrs; c.v_round = 1;
+  if (adapters->A_ptrs_host && adapters->B_ptrs_host) {
+    c.Wtab_host = adapters->A_ptrs_host;
+    c.Vtab_host = adapters->B_ptrs_host;
+  }
   c.K = adapters->h_in; c.N = adapters->h_out;
   c.token_rows = segments->token_rows;
   c.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
@@ -615,6 +685,7 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
     c.X = static_cast<const uint16_t*>(x); c.ldx = ldx;
     c.U = reinterpret_cast<float*>(wsb + L.urec); c.ldu = L.lddu;
     c.Wtab = adapters->A_ptrs; c.v_round = 1;
+    if (adapters->A_ptrs_host && adapters->B_ptrs_host) c.Wtab_host = adapters->A_ptrs_host;
     c.K = adapters->h_in; c.N = adapters->h_out;
     c.token_rows = segments->token_rows;
     c.partials = partials; c.counters = counters; c.rmax = rmax;

@@ -56,11 +56,16 @@ __device__ __forceinline__ i32x4 mk_rsrc_words(const void* base, int64_t bytes) 
 // load counts in vmcnt like any vector load.
 // M0 (which holds the LDS address) is declared as an output of the
 // statement, so the compiler keeps no value of its own in it across the load.
+// The descriptor words pass through readfirstlane so that they are SGPR
+// values even where the compiler has kept a copy of them in VGPRs.
 __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
   int m0_out;
+  i32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] = __builtin_amdgcn_readfirstlane(rsrc[q]);
   asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
                : "={m0}"(m0_out)
-               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "s"(lds_addr), "v"(voff), "s"(r)
                : "memory");
   (void)m0_out;
 }
@@ -99,11 +104,14 @@ __device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
     f[2 * q + 1] = __builtin_bit_cast(float, v[q] & 0xffff0000u);
   }
 }
-// Pack 8 floats to 8 bf16 (round to nearest even).
+// Pack 8 floats to 8 bf16 (round to nearest even), two per conversion.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
   u32x4 v;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = f2bf(f[2 * q]) | (f2bf(f[2 * q + 1]) << 16);
+  for (int q = 0; q < 4; ++q)
+    v[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{f[2 * q], f[2 * q + 1]}, bf16x2_t));
   return v;
 }
 

@@ -32,14 +32,22 @@ struct TileInfo {
   int rank;
   int slot;
   float scale;
+  uint64_t wptr, vptr;  // small plans with ptrs_in_plan: the segment's weight addresses
 };
 
 template <typename PT>
 struct PlanCap;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winvalid-offsetof"
 template <int CAP>
 struct PlanCap<FwdPlanT<CAP>> {
   static constexpr int v = CAP;  // segment capacity of a plan type
+  // byte offsets of the weight-address arrays in the plan, which is the
+  // kernel's only explicit argument and so starts the kernel-argument segment
+  static constexpr int kOffW = __builtin_offsetof(FwdPlanT<CAP>, seg_wptr);
+  static constexpr int kOffV = __builtin_offsetof(FwdPlanT<CAP>, seg_vptr);
 };
+#pragma clang diagnostic pop
 
 // Finds the segment that holds tile g. Small plans (decode batches): a scalar
 // scan of the whole table, which the compiler reads from the kernel
@@ -63,6 +71,15 @@ __device__ __forceinline__ TileInfo tile_info(const PT& P, int g, TileInfo* lds)
     t.rank = P.seg_rank[sel];
     t.slot = P.seg_slot[sel];
     t.scale = P.seg_scale[sel];
+    // one scalar load each from the kernel-argument segment at the selected
+    // entry (indexing the arrays by value would hold all of them in SGPRs)
+    t.wptr = t.vptr = 0;
+    if (P.ptrs_in_plan) {
+      typedef const uint64_t __attribute__((address_space(4)))* KPtr;
+      const auto* kb = (const char __attribute__((address_space(4)))*)__builtin_amdgcn_kernarg_segment_ptr();
+      t.wptr = *reinterpret_cast<KPtr>(kb + PlanCap<PT>::kOffW + sel * 8);
+      t.vptr = *reinterpret_cast<KPtr>(kb + PlanCap<PT>::kOffV + sel * 8);
+    }
     return t;
   }
   // the table reads do not wait for n_seg: entries past it are in the plan
@@ -102,11 +119,15 @@ __device__ __forceinline__ TileInfo tile_info(const PT& P, int g, TileInfo* lds)
 
 template <typename PT>
 __device__ __forceinline__ const uint16_t* w_ptr(const PT& P, const TileInfo& t) {
+  if constexpr (PlanCap<PT>::v <= kSmallSeg)
+    if (P.ptrs_in_plan) return reinterpret_cast<const uint16_t*>(t.wptr);
   if (P.Wtab) return reinterpret_cast<const uint16_t*>(P.Wtab[t.adapter]);
   return P.Wslots + (int64_t)t.slot * P.w_slot_elems;
 }
 template <typename PT>
 __device__ __forceinline__ const uint16_t* v_ptr(const PT& P, const TileInfo& t) {
+  if constexpr (PlanCap<PT>::v <= kSmallSeg)
+    if (P.ptrs_in_plan) return reinterpret_cast<const uint16_t*>(t.vptr);
   if (P.Vtab) return reinterpret_cast<const uint16_t*>(P.Vtab[t.adapter]);
   return P.Vslots + (int64_t)t.slot * P.v_slot_elems;
 }
@@ -136,7 +157,7 @@ struct Geo {
   static constexpr int NBW = 32 * RB / R;                         // blocks of W rows
   static constexpr int BPW = (NBX + NBW) / 4;                     // block loads per wave
   static constexpr int SHRINK_BYTES = (NBX + NBW) * BS;
-  static constexpr int CW = RB == 1 ? 256 : 128;                  // expand column chunk
+  static constexpr int CW = RB == 1 ? 256 : 128;                  // staged expand column chunk
   static constexpr int CWP = CW + 8;                              // LDS row of y (elements)
   static constexpr int RP = 32 * RB + 8;                          // LDS row of V (elements)
   static constexpr int YV = (32 * CW / 8) / kThreads;             // y vectors per thread
@@ -154,7 +175,7 @@ struct LdsBytes {
                                                                 RBMAX >= 4 ? Geo<4>::SHRINK_BYTES : 0));
   static constexpr int expand = cmax(Geo<1>::EXPAND_BYTES, cmax(RBMAX >= 2 ? Geo<2>::EXPAND_BYTES : 0,
                                                                 RBMAX >= 4 ? Geo<4>::EXPAND_BYTES : 0));
-  // buffer 0: shrink chunks, the wave reduction, the expand stage
+  // buffer 0: shrink chunks, the wave reduction, the staged expand
   static constexpr int b0 = cmax(shrink, cmax(expand, kRedBytes));
   // buffer 1: shrink chunks, the tile's P
   static constexpr int b1 = cmax(shrink, kPlBytes);
@@ -307,7 +328,7 @@ __device__ __forceinline__ void shrink_lds(const PT& P, const TileInfo& t, int k
   // wait for this wave's loads of the chunk (its later chunk may stay in
   // flight), then barrier. Before a buffer is loaded again, every wave's
   // reads of it must be done: wait for LDS reads, then barrier.
-  auto step = [&](uint8_t* buf, int cc) {
+  auto step = [&](uint8_t* buf, int cc) __attribute__((always_inline)) {
     if (cc + 1 < nch)
       wait_vmcnt<G::BPW>();
     else
@@ -379,20 +400,22 @@ __device__ __forceinline__ void build_pfrags(const float* Pl, int rank, int lane
   }
 }
 
-// Expand of the item's columns [c0, c1) in chunks of CW columns. A chunk's
+// Staged expand, for items of many blocks: the item's columns [c0, c1) in
+// chunks of CW columns. A chunk's
 // 32 y rows and its CW rows of V (one contiguous span of V) are staged
 // through LDS; every wave computes whole 32-column blocks from LDS, with the
 // rows of a block permuted by colmap so that a lane owns two runs of 8
 // contiguous bf16 of one y row; the results go back into the LDS y tile,
-// which is then stored row-contiguously.
+// which is then stored row-contiguously (whole rows per store instruction,
+// where the register-only expand stores 32 bytes of each row).
 template <int RB>
-struct ExpRegs {
+struct StgRegs {
   u32x4 y[Geo<RB>::YV];
   u32x4 v[Geo<RB>::VV];
 };
 
 template <int RB>
-struct ExpCtx {
+struct StgCtx {
   __amdgpu_buffer_rsrc_t yr, vr;
   uint32_t yoff[Geo<RB>::YV];  // byte offset of this thread's y rows
   uint16_t vrow[Geo<RB>::VV];  // V vector f = t + 256j of a chunk: row within the chunk
@@ -406,7 +429,7 @@ struct ExpCtx {
 };
 
 template <int RB>
-__device__ __forceinline__ void exp_load(const ExpCtx<RB>& C, int cs, ExpRegs<RB>& R) {
+__device__ __forceinline__ void stg_load(const StgCtx<RB>& C, int cs, StgRegs<RB>& R) {
   using G = Geo<RB>;
   constexpr int YPR = G::CW / 8;
   const int col = cs + 8 * (threadIdx.x % YPR);
@@ -427,7 +450,7 @@ __device__ __forceinline__ void exp_load(const ExpCtx<RB>& C, int cs, ExpRegs<RB
 }
 
 template <int RB>
-__device__ __forceinline__ void exp_to_lds(const ExpCtx<RB>& C, int cs, const ExpRegs<RB>& R,
+__device__ __forceinline__ void stg_to_lds(const StgCtx<RB>& C, int cs, const StgRegs<RB>& R,
                                            uint16_t* ys, uint16_t* vs) {
   using G = Geo<RB>;
   constexpr int YPR = G::CW / 8;
@@ -451,7 +474,7 @@ __device__ __forceinline__ void exp_to_lds(const ExpCtx<RB>& C, int cs, const Ex
 }
 
 template <int RB>
-__device__ __forceinline__ void exp_mfma(const ExpCtx<RB>& C, const PFrags<RB>& F, int cs, uint16_t* ys,
+__device__ __forceinline__ void stg_mfma(const StgCtx<RB>& C, const PFrags<RB>& F, int cs, uint16_t* ys,
                                          const uint16_t* vs, int wave, int lane) {
   using G = Geo<RB>;
   constexpr int NB = G::CW / 32;  // 32-column blocks per chunk
@@ -485,7 +508,7 @@ __device__ __forceinline__ void exp_mfma(const ExpCtx<RB>& C, const PFrags<RB>& 
 }
 
 template <int RB>
-__device__ __forceinline__ void exp_store(const ExpCtx<RB>& C, int cs, const uint16_t* ys) {
+__device__ __forceinline__ void stg_store(const StgCtx<RB>& C, int cs, const uint16_t* ys) {
   using G = Geo<RB>;
   constexpr int YPR = G::CW / 8;
   constexpr int RPJ = kThreads / YPR;
@@ -499,11 +522,11 @@ __device__ __forceinline__ void exp_store(const ExpCtx<RB>& C, int cs, const uin
 }
 
 template <int RB, typename PT>
-__device__ __forceinline__ ExpCtx<RB> exp_ctx(const PT& P, const TileInfo& t, int c) {
+__device__ __forceinline__ StgCtx<RB> stg_ctx(const PT& P, const TileInfo& t, int c) {
   using G = Geo<RB>;
   constexpr int YPR = G::CW / 8;
   constexpr int RPJ = kThreads / YPR;
-  ExpCtx<RB> C;
+  StgCtx<RB> C;
   const TileRows yt = tile_rows(P.Y, P.ldy, P.N, P, t);
   C.yr = yt.r;
   const int r0 = threadIdx.x / YPR;
@@ -535,14 +558,14 @@ __device__ __forceinline__ ExpCtx<RB> exp_ctx(const PT& P, const TileInfo& t, in
 
 // Chunks of the expand whose loads are in flight (register sets).
 template <int RB>
-struct ExpDepth {
+struct StgDepth {
   static constexpr int v = RB <= 2 ? 2 : 1;
 };
 
 // Runs the expand over the item's columns. R holds the loads of the first NE
 // chunks, issued by the caller (so they can be issued before a wait).
 template <int RB, int NE>
-__device__ __forceinline__ void expand_run(const ExpCtx<RB>& C, const PFrags<RB>& F, ExpRegs<RB> (&R)[NE],
+__device__ __forceinline__ void stg_run(const StgCtx<RB>& C, const PFrags<RB>& F, StgRegs<RB> (&R)[NE],
                                            uint8_t* stage) {
   using G = Geo<RB>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -552,13 +575,13 @@ __device__ __forceinline__ void expand_run(const ExpCtx<RB>& C, const PFrags<RB>
   // the last step is zero in every V row (written once; chunks never touch it)
   if (C.vec16 && (C.ldv & 8) && threadIdx.x < G::CW)
     st16(vs + threadIdx.x * G::RP + C.ldv, zero16());
-  auto chunk = [&](int cs, ExpRegs<RB>& Rq) {
-    exp_to_lds<RB>(C, cs, Rq, ys, vs);
+  auto chunk = [&](int cs, StgRegs<RB>& Rq) __attribute__((always_inline)) {
+    stg_to_lds<RB>(C, cs, Rq, ys, vs);
     lds_sync();
-    exp_load<RB>(C, cs + NE * G::CW, Rq);  // past the range: reads nothing
-    exp_mfma<RB>(C, F, cs, ys, vs, wave, lane);
+    stg_load<RB>(C, cs + NE * G::CW, Rq);  // past the range: reads nothing
+    stg_mfma<RB>(C, F, cs, ys, vs, wave, lane);
     lds_sync();
-    exp_store<RB>(C, cs, ys);
+    stg_store<RB>(C, cs, ys);
     lds_sync();
   };
   // the first chunk is peeled so that the loop is entered with the same
@@ -577,68 +600,151 @@ __device__ __forceinline__ void expand_run(const ExpCtx<RB>& C, const PFrags<RB>
   }
 }
 
-// ---------------------------------------------------------------------------
-// Cross-workgroup hand-off of split-K partial sums (see item_shrink and
-// item_expand_wait). LORA_XWG selects the protocol:
-//  1: every thread fences at agent scope (release before, acquire after).
-//  2: one thread per workgroup fences, ordered with the others by barriers.
-//  3: partials move with agent-scope (cache-coherent) accesses and the
-//     counters with atomics; no cache-wide writeback or invalidate.
-// ---------------------------------------------------------------------------
-#ifndef LORA_XWG
-#define LORA_XWG 3
-#endif
+// Register-only expand, for items of at most one block per wave: the item's columns [c0, c1) in 32-column blocks, from registers.
+// Wave w computes blocks w, w+4, ... of the item. Lane (m, h) loads the V row
+// of output column col0 + colmap(m) (16 bytes per 16-wide k-step: k = 16 kb +
+// 8 h .. +8), which is its A operand, and the two 16-byte runs of token m's
+// y row that its 16 results update (columns col0 + 8 h and col0 + 16 + 8 h,
+// 8 each), so the expand uses neither LDS nor barriers. The loads of the
+// wave's next ExpDepth blocks are in flight while a block is computed.
+template <int RB>
+struct BlkRegs {
+  u32x4 v[2 * RB];  // V rows (A fragments), one per 16-wide k-step
+  u32x4 y[2];       // y runs of token m
+};
 
-// Returns a value that depends on the store having been performed (protocol
-// 3 uses a returning atomic swap; the caller folds the results into LDS so
-// the wave waits for every swap before it reaches the barrier).
-__device__ __forceinline__ float xwg_store(float* p, float v) {
-#if LORA_XWG == 3
-  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-  *p = v;
-  return 0.f;
-#endif
+// Blocks whose loads each wave keeps in flight (16, 24 and 40 VGPRs a block
+// for RB = 1, 2, 4).
+template <int RB>
+struct ExpDepth {
+  static constexpr int v = RB == 1 ? 4 : (RB == 2 ? 3 : 1);
+};
+
+template <int RB>
+struct ExpCtx {
+  __amdgpu_buffer_rsrc_t yr, vr;
+  uint32_t yrow;  // byte offset of token m's y row, kOff past the tile
+  int ldv;        // V row stride (elements)
+  int rank, kbn;  // rank, k-steps of 16 that hold rank columns
+  bool vec16;     // V rows are whole 16-byte vectors
+  int c0, c1;     // column range of the item
+  int nb;         // its 32-column blocks
+  float oscale;
+};
+
+// Byte offset off, or one past every buffer (bit 31 set: the access reads
+// zero or is dropped) when index >= limit. Plain arithmetic, so that no lane
+// mask stays live across the expand loop.
+__device__ __forceinline__ uint32_t off_if_below(uint32_t off, int index, int limit) {
+  return off | ((uint32_t)((limit - 1 - index) >> 31) & 0x80000000u);
 }
-__device__ __forceinline__ float xwg_load(const float* p) {
-#if LORA_XWG == 3
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-  return *p;
-#endif
-}
-// Called by every thread after its partial stores; thread 0 increments *ctr
-// and gets the previous value (other threads get 0).
-__device__ __forceinline__ int xwg_signal(int* ctr) {
-  int old = 0;
-#if LORA_XWG == 1
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (threadIdx.x == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-#elif LORA_XWG == 2
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+// Issues the loads of block j of the item (j >= nb: nothing is read).
+template <int RB>
+__device__ __forceinline__ void exp_load(const ExpCtx<RB>& C, int j, BlkRegs<RB>& R) {
+  const int lane = threadIdx.x & 63, m = lane & 31, h = lane >> 5;
+  const int col0 = C.c0 + 32 * j;
+  const int vrow = col0 + colmap(m);
+  // rows past the item (and so every row of a block past it) read zero
+  const uint32_t vbase = off_if_below((uint32_t)(vrow * C.ldv * 2), vrow, C.c1);
+#pragma unroll
+  for (int kb = 0; kb < 2 * RB; ++kb) {
+    if (kb >= C.kbn) continue;
+    const int k0 = 16 * kb + 8 * h;
+    if (C.vec16) {
+      R.v[kb] = bld16(C.vr, off_if_below(vbase + 2u * (uint32_t)k0, k0, C.rank));
+    } else {
+      // rank not a multiple of 8 (V rows not 16-byte aligned): element
+      // loads, zero past the rank. They are waited for here, so that this
+      // rare layout holds no more registers in flight than the usual one.
+      u32x4 v = zero16();
+#pragma nounroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = bld2(C.vr, off_if_below(vbase + 2u * (uint32_t)(k0 + e), k0 + e, C.rank));
+        const uint32_t sh = 16u * (uint32_t)(e & 1);
+        if (e < 2) v[0] |= w << sh;
+        else if (e < 4) v[1] |= w << sh;
+        else if (e < 6) v[2] |= w << sh;
+        else v[3] |= w << sh;
+      }
+      R.v[kb] = v;
+    }
   }
-#else
-  __syncthreads();
-  if (threadIdx.x == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#endif
-  return old;
+  // y: token rows past the tile have yrow = kOff (bit 31 set) already
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int col = col0 + 16 * r + 8 * h;
+    R.y[r] = bld16(C.yr, off_if_below(C.yrow + 2u * (uint32_t)col, col, C.c1));
+  }
 }
-// Thread 0 has seen the counter complete; make the partials visible to the
-// whole workgroup (ends with a barrier).
-__device__ __forceinline__ void xwg_acquire() {
-#if LORA_XWG == 2
-  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  __syncthreads();
-#elif LORA_XWG == 1
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#else
-  __syncthreads();
-#endif
+
+// Computes block j from its loaded registers and stores its y runs.
+template <int RB>
+__device__ __forceinline__ void exp_block(const ExpCtx<RB>& C, const PFrags<RB>& F, int j,
+                                          const BlkRegs<RB>& R) {
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  f32x16 acc = zero_acc16();
+#pragma unroll
+  for (int kb = 0; kb < 2 * RB; ++kb)
+    if (kb < C.kbn) {
+      acc = mfma32(as_bf16x8(R.v[kb]), F.hi[kb], acc);
+      acc = mfma32(as_bf16x8(R.v[kb]), F.lo[kb], acc);
+    }
+  const int col0 = C.c0 + 32 * j;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int col = col0 + 16 * r + 8 * h;
+    float f[8];
+    unpack8(R.y[r], f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = f[i] + C.oscale * acc[8 * r + i];
+    bst16(C.yr, off_if_below(C.yrow + 2u * (uint32_t)col, col, C.c1), pack8(f));
+  }
+}
+
+template <int RB, typename PT>
+__device__ __forceinline__ ExpCtx<RB> exp_ctx(const PT& P, const TileInfo& t, int c) {
+  ExpCtx<RB> C;
+  const TileRows yt = tile_rows(P.Y, P.ldy, P.N, P, t);
+  C.yr = yt.r;
+  C.yrow = row_off(P, t, yt, threadIdx.x & 31);
+  C.ldv = ((t.rank + P.v_round - 1) / P.v_round) * P.v_round;
+  C.vec16 = (C.ldv & 7) == 0;
+  C.vr = mk_rsrc(v_ptr(P, t), (int64_t)P.N * C.ldv * 2);
+  C.rank = t.rank;
+  C.kbn = (t.rank + 15) >> 4;
+  const int nblocks = (P.N + 31) >> 5;
+  const int cb0 = c * P.nblk;
+  C.c0 = 32 * cb0;
+  C.c1 = min(P.N, 32 * min(nblocks, cb0 + P.nblk));
+  C.nb = (C.c1 - C.c0 + 31) >> 5;
+  C.oscale = P.scale_in_shrink ? 1.f : t.scale;
+  return C;
+}
+
+// Issues the loads of the wave's first ExpDepth blocks.
+template <int RB, int NE>
+__device__ __forceinline__ void exp_prefetch(const ExpCtx<RB>& C, BlkRegs<RB> (&R)[NE]) {
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 0; d < NE; ++d) exp_load<RB>(C, wave + 4 * d, R[d]);
+}
+
+// Runs the wave's blocks. R holds the loads of its first NE blocks (issued by
+// the caller, so that they can be in flight during a wait).
+template <int RB, int NE>
+__device__ __forceinline__ void expand_run(const ExpCtx<RB>& C, const PFrags<RB>& F, BlkRegs<RB> (&R)[NE]) {
+  const int wave = threadIdx.x >> 6;
+  for (int i = 0; wave + 4 * i < C.nb; i += NE) {
+#pragma unroll
+    for (int d = 0; d < NE; ++d) {
+      const int j = wave + 4 * (i + d);
+      if (j < C.nb) {
+        exp_block<RB>(C, F, j, R[d]);
+        exp_load<RB>(C, j + 4 * NE, R[d]);  // past the item: reads nothing
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -653,17 +759,32 @@ __device__ __forceinline__ void store_u_from_lds(const PT& P, const TileInfo& t,
   }
 }
 
+// Items of at most one 32-column block per wave take the register-only
+// expand (no LDS stage or barriers); longer ones the staged expand, whose
+// stores cover whole rows.
+template <int RB>
+__device__ __forceinline__ bool direct_expand(int nblk) { return nblk <= 4; }
+
 template <int RB, typename PT>
 __device__ __forceinline__ void expand_from_lds(const PT& P, const TileInfo& t, int c, const float* Pl,
                                                 uint8_t* stage) {
-  const ExpCtx<RB> C = exp_ctx<RB>(P, t, c);
-  constexpr int NE = ExpDepth<RB>::v;
-  ExpRegs<RB> R[NE];
-#pragma unroll
-  for (int q = 0; q < NE; ++q) exp_load<RB>(C, C.c0 + q * Geo<RB>::CW, R[q]);  // empty ranges read nothing
   PFrags<RB> F;
-  build_pfrags<RB>(Pl, t.rank, threadIdx.x & 63, F);
-  expand_run<RB, NE>(C, F, R, stage);
+  if (direct_expand<RB>(P.nblk)) {
+    const ExpCtx<RB> C = exp_ctx<RB>(P, t, c);
+    constexpr int NE = ExpDepth<RB>::v;
+    BlkRegs<RB> R[NE];
+    exp_prefetch<RB, NE>(C, R);
+    build_pfrags<RB>(Pl, t.rank, threadIdx.x & 63, F);
+    expand_run<RB, NE>(C, F, R);
+  } else {
+    const StgCtx<RB> C = stg_ctx<RB>(P, t, c);
+    constexpr int NE = StgDepth<RB>::v;
+    StgRegs<RB> R[NE];
+#pragma unroll
+    for (int q = 0; q < NE; ++q) stg_load<RB>(C, C.c0 + q * Geo<RB>::CW, R[q]);  // empty ranges read nothing
+    build_pfrags<RB>(Pl, t.rank, threadIdx.x & 63, F);
+    stg_run<RB, NE>(C, F, R, stage);
+  }
 }
 
 // kModeFusedTile: full shrink of one tile on chip, then its n-chunk c.
@@ -674,7 +795,7 @@ __device__ __forceinline__ void item_fused_tile(const PT& P, const Lds& L, const
   shrink_lds<RB>(P, t, 0, P.K, L, acc);
   const float ps = P.scale_in_shrink ? t.scale : 1.f;
   float* Pl = L.Pl();
-  reduce_waves<RB>(L.red(), acc, wave, lane, [&](int k, int n, float v) { Pl[n * kLdp + k] = v * ps; });
+  reduce_waves<RB>(L.red(), acc, wave, lane, [&](int k, int n, float v) __attribute__((always_inline)) { Pl[n * kLdp + k] = v * ps; });
   if (P.write_u && c == 0) store_u_from_lds(P, t, Pl);
   expand_from_lds<RB>(P, t, c, Pl, L.b0);
 }
@@ -691,9 +812,39 @@ __device__ __forceinline__ void item_expand(const PT& P, const Lds& L, const Til
   expand_from_lds<RB>(P, t, c, Pl, L.b0);
 }
 
+// ---------------------------------------------------------------------------
+// Hand-off of split-shrink parts (kModeFusedDep). A part is published by
+// storing it, waiting until every store of the workgroup has been performed,
+// and then storing its stamp (launch id << 8 | XCD of the writer). An expand
+// waits until every part of its tile carries the current launch id, then
+// reads the parts. Launch ids are unique, so a stamp left by an earlier call
+// never matches, and no counter has to be returned to zero.
+// Stamps are always stored and read with device scope (the reads miss both
+// the CU's L1 and a stale L2 line).
+//  XCD-local layout: all items of a tile run on one XCD, so the parts
+//  themselves are plain stores that meet the expands' loads in that XCD's L2
+//  (the expand's CU has not read those lines before in this launch, so its L1
+//  holds no stale copy). A stamp written on another XCD is never trusted: the
+//  expand then computes the parts itself.
+//  Otherwise: the parts too use device-scope stores and loads.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t xcc_id() {
+  return (uint32_t)__builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11));  // HW_REG_XCC_ID[3:0]
+}
+constexpr int kAuxDev = 16;  // sc1: device scope
+
 template <typename PT>
 __device__ __forceinline__ float* partial_ptr(const PT& P, int g, int c) {
   return P.partials + ((int64_t)g * P.ks + c) * kTileM * P.rpad;
+}
+
+// Stamp of part (g, c) as seen by this workgroup's thread.
+template <typename PT>
+__device__ __forceinline__ uint64_t load_stamp(const PT& P, int idx) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const __amdgpu_buffer_rsrc_t r = mk_rsrc(P.stamps, (int64_t)kMaxPartials * 8);
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, idx * 8, 0, kAuxDev);
+  return ((uint64_t)v[1] << 32) | v[0];
 }
 
 // kModeShrink / kModeFusedDep phase A: shrink over k-chunk c.
@@ -707,90 +858,175 @@ __device__ __forceinline__ void item_shrink(const PT& P, const Lds& L, const Til
   float* red = L.red();
   const float ps = P.scale_in_shrink ? t.scale : 1.f;
   if (P.mode == kModeShrink && P.ks == 1) {
-    reduce_waves<RB>(red, acc, wave, lane, [&](int k, int n, float v) {
-      if (n < t.cnt && k < t.rank) P.U[(int64_t)(t.p0 + n) * P.ldu + k] = v * ps;
+    // the lambda takes plain values, not the plan (a reference to the kernel
+    // argument held in a closure can make the compiler copy the plan to scratch)
+    float* const U = P.U + (int64_t)t.p0 * P.ldu;
+    const int64_t ldu = P.ldu;
+    const int cnt = t.cnt, rank = t.rank;
+    reduce_waves<RB>(red, acc, wave, lane, [&](int k, int n, float v) __attribute__((always_inline)) {
+      if (n < cnt && k < rank) U[(int64_t)n * ldu + k] = v * ps;
     });
     return;
   }
   float* part = partial_ptr(P, t.g, c);
   const int rpad = P.rpad;
+  if (P.mode == kModeFusedDep) {
+    if (P.xcd_local)
+      reduce_waves<RB>(red, acc, wave, lane, [&](int k, int n, float v) __attribute__((always_inline)) { part[n * rpad + k] = v; });
+    else
+      reduce_waves<RB>(red, acc, wave, lane, [&](int k, int n, float v) __attribute__((always_inline)) {
+        __hip_atomic_store(part + n * rpad + k, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      });
+    asm volatile("" ::: "memory");
+    wait_vmcnt<0>();  // this thread's part stores have been performed
+    __syncthreads();  // ... and every thread's
+    if (threadIdx.x == 0) {
+      const uint64_t stamp = (P.launch_id << 8) | xcc_id();
+      __hip_atomic_store(P.stamps + (t.g * P.ks + c), stamp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  // kModeShrink, ks > 1: partials move with device-coherent atomic swaps
+  // whose returned values each thread waits for; the last arriving chunk
+  // (per-tile counter) sums all chunks in order and returns the counter to 0
   float sink = 0.f;
-  reduce_waves<RB>(red, acc, wave, lane,
-                   [&](int k, int n, float v) { sink += xwg_store(part + n * rpad + k, v); });
-#if LORA_XWG == 3
+  reduce_waves<RB>(red, acc, wave, lane, [&](int k, int n, float v) __attribute__((always_inline)) {
+    sink += __hip_atomic_exchange(part + n * rpad + k, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  });
   red[threadIdx.x] = sink;  // waits for every swap of this thread
-#else
-  (void)sink;
-#endif
   int* ctr = P.counters + kCtrTiles + t.g;
-  const int old = xwg_signal(ctr);
-  // storing the returned count makes thread 0 wait for its increment to be
-  // performed before anything later (e.g. the done count) is issued
-  if (threadIdx.x == 0) *L.flag = old;
-  if (P.mode == kModeFusedDep) return;
-  // kModeShrink, ks > 1: the last arriving chunk sums all chunks in order
+  __syncthreads();
+  if (threadIdx.x == 0) *L.flag = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (*L.flag != P.ks - 1) return;
-  xwg_acquire();
   for (int e = threadIdx.x; e < kTileM * t.rank; e += kThreads) {
     const int n = e / t.rank, k = e - n * t.rank;
     if (n >= t.cnt) continue;
-    float s = xwg_load(partial_ptr(P, t.g, 0) + n * rpad + k);
-    for (int q = 1; q < P.ks; ++q) s += xwg_load(partial_ptr(P, t.g, q) + n * rpad + k);
+    float s = __hip_atomic_load(partial_ptr(P, t.g, 0) + n * rpad + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int q = 1; q < P.ks; ++q)
+      s += __hip_atomic_load(partial_ptr(P, t.g, q) + n * rpad + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     P.U[(int64_t)(t.p0 + n) * P.ldu + k] = s * ps;
   }
   if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// kModeFusedDep phase B: wait for the tile's k-chunks, sum them, expand.
-// If the chunks do not arrive within spin_ticks (e.g. their workgroups are
-// not resident), the item computes the same chunks itself in the same order,
-// so the result is identical and no wait is unbounded.
+// kModeFusedDep phase B: wait for the tile's parts, sum them in order,
+// expand n-chunk c. If the parts do not all arrive within spin_ticks (their
+// workgroups not resident, or written on another XCD in the XCD-local
+// layout), the item computes the same parts itself in the same order, so the
+// result is identical and no wait is unbounded.
+// Waits for the stamps of tile t's parts; on success sums the parts in order
+// q = 0, 1, ... into Pl (scaled) and returns true.
 template <int RB, typename PT>
-__device__ __forceinline__ void item_expand_wait(const PT& P, const Lds& L, const TileInfo& t, int c) {
+__device__ __forceinline__ bool wait_and_sum_parts(const PT& P, const Lds& L, const TileInfo& t, float* Pl) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int* ctr = P.counters + kCtrTiles + t.g;
-  // y rows and expand weights do not depend on the shrink: issue the first
-  // chunk's loads before waiting
-  const ExpCtx<RB> C = exp_ctx<RB>(P, t, c);
-  constexpr int NE = ExpDepth<RB>::v;
-  ExpRegs<RB> R[NE];
-#pragma unroll
-  for (int q = 0; q < NE; ++q) exp_load<RB>(C, C.c0 + q * Geo<RB>::CW, R[q]);  // empty ranges read nothing
-  if (threadIdx.x == 0) {
+  if (wave == 0) {
+    // lane q < ks watches the stamp of part q
+    const bool mine = lane < P.ks;
+    const int idx = t.g * P.ks + (mine ? lane : 0);
+    const uint64_t want = P.launch_id;
+    const uint32_t here = xcc_id();
     const uint64_t t0 = wall_clock64();
-    int ready = 0;
+    bool ready = false, trusted = true;
     while (true) {
-      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= P.ks) { ready = 1; break; }
+      const uint64_t st = load_stamp(P, idx);
+      const bool arrived = !mine || (st >> 8) == want;
+      const bool local_ok = !mine || !P.xcd_local || (uint32_t)(st & 0xff) == here;
+      if (__builtin_amdgcn_ballot_w64(!arrived) == 0) {
+        ready = true;
+        trusted = __builtin_amdgcn_ballot_w64(!local_ok) == 0;
+        break;
+      }
       if (wall_clock64() - t0 > (uint64_t)P.spin_ticks) break;
       __builtin_amdgcn_s_sleep(1);
     }
-    *L.flag = ready;
+    if (lane == 0) *L.flag = (ready && trusted) ? 1 : 0;
   }
-  xwg_acquire();
+  __syncthreads();
+  if (!*L.flag) return false;
   const float ps = P.scale_in_shrink ? t.scale : 1.f;
-  float* Pl = L.Pl();
-  const int rcols = 32 * RB;
-  if (*L.flag) {
-    const int rpad = P.rpad;
-    for (int e = threadIdx.x; e < kTileM * rcols; e += kThreads) {
-      const int n = e / rcols, k = e - n * rcols;
-      float s = xwg_load(partial_ptr(P, t.g, 0) + n * rpad + k);
-      for (int q = 1; q < P.ks; ++q) s += xwg_load(partial_ptr(P, t.g, q) + n * rpad + k);
-      Pl[n * kLdp + k] = s * ps;
-    }
-    lds_sync();
-    if (P.write_u && c == 0) store_u_from_lds(P, t, Pl);
-    PFrags<RB> F;
-    build_pfrags<RB>(Pl, t.rank, lane, F);
-    expand_run<RB, NE>(C, F, R, L.b0);
-    return;
+  constexpr int RC = 32 * RB;                  // rank columns of the P tile
+  constexpr int EPT = kTileM * RC / kThreads;  // elements per thread
+  // the loads of PD parts (all of them for the usual k split) are in flight
+  // together
+  const __amdgpu_buffer_rsrc_t r = mk_rsrc(partial_ptr(P, t.g, 0), (int64_t)P.ks * kTileM * P.rpad * 4);
+  const uint32_t part_bytes = (uint32_t)(kTileM * P.rpad * 4);
+  float s[EPT];
+  uint32_t off[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = threadIdx.x + kThreads * j;
+    const int n = e / RC, k = e - n * RC;
+    off[j] = (uint32_t)((n * P.rpad + k) * 4);
+    s[j] = 0.f;
   }
+  constexpr int PD = 8 / RB;
+  for (int q0 = 0; q0 < P.ks; q0 += PD) {
+    float v[PD][EPT];
+#pragma unroll
+    for (int d = 0; d < PD; ++d)
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const uint32_t o = q0 + d < P.ks ? (uint32_t)(q0 + d) * part_bytes + off[j] : kOff;
+        v[d][j] = __builtin_bit_cast(float, P.xcd_local ? __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0)
+                                                        : __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, kAuxDev));
+      }
+#pragma unroll
+    for (int d = 0; d < PD; ++d)
+#pragma unroll
+      for (int j = 0; j < EPT; ++j)
+        if (q0 + d < P.ks) s[j] = (q0 + d == 0) ? v[d][j] : s[j] + v[d][j];
+  }
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = threadIdx.x + kThreads * j;
+    const int n = e / RC, k = e - n * RC;
+    Pl[n * kLdp + k] = s[j] * ps;
+  }
+  lds_sync();
+  return true;
+}
+
+template <int RB, typename PT>
+__device__ __forceinline__ void item_expand_wait(const PT& P, const Lds& L, const TileInfo& t, int c) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* Pl = L.Pl();
+  // y rows and expand weights do not depend on the shrink: the first loads
+  // are issued before waiting
+  bool done = false;
+  if (direct_expand<RB>(P.nblk)) {
+    const ExpCtx<RB> C = exp_ctx<RB>(P, t, c);
+    constexpr int NE = ExpDepth<RB>::v;
+    BlkRegs<RB> R[NE];
+    exp_prefetch<RB, NE>(C, R);
+    if (wait_and_sum_parts<RB>(P, L, t, Pl)) {
+      if (P.write_u && c == 0) store_u_from_lds(P, t, Pl);
+      PFrags<RB> F;
+      build_pfrags<RB>(Pl, t.rank, lane, F);
+      expand_run<RB, NE>(C, F, R);
+      done = true;
+    }
+  } else {
+    const StgCtx<RB> C = stg_ctx<RB>(P, t, c);
+    constexpr int NE = StgDepth<RB>::v;
+    StgRegs<RB> R[NE];
+#pragma unroll
+    for (int q = 0; q < NE; ++q) stg_load<RB>(C, C.c0 + q * Geo<RB>::CW, R[q]);  // empty ranges read nothing
+    if (wait_and_sum_parts<RB>(P, L, t, Pl)) {
+      if (P.write_u && c == 0) store_u_from_lds(P, t, Pl);
+      PFrags<RB> F;
+      build_pfrags<RB>(Pl, t.rank, lane, F);
+      stg_run<RB, NE>(C, F, R, L.b0);
+      done = true;
+    }
+  }
+  if (done) return;
   // Fallback. The early loads are dropped and issued again after the shrink
   // (a separate expand, so that they are not held in registers through it).
   // The chunk sums run in registers (each thread always receives the same
   // elements from the reduction) because the shrink reuses P's LDS buffer;
   // the last chunk's pass writes P.
+  const float ps = P.scale_in_shrink ? t.scale : 1.f;
   float run[4 * RB];
   for (int q = 0; q < P.ks; ++q) {
     const int kb = q * P.kchunk;
@@ -799,7 +1035,7 @@ __device__ __forceinline__ void item_expand_wait(const PT& P, const Lds& L, cons
     shrink_lds<RB>(P, t, kb, ke, L, acc);
     int idx = 0;
     const bool last = q == P.ks - 1;
-    reduce_waves<RB>(L.red(), acc, wave, lane, [&](int k, int n, float v) {
+    reduce_waves<RB>(L.red(), acc, wave, lane, [&](int k, int n, float v) __attribute__((always_inline)) {
       const float sum = (q == 0) ? v : run[idx] + v;
       run[idx] = sum;
       if (last) Pl[n * kLdp + k] = sum * ps;
@@ -829,41 +1065,47 @@ __global__ __launch_bounds__(kThreads, 2) void sgmv_fwd_kernel(PT P) {
   __shared__ int lds_flag;
   const Lds L{lds_b0, lds_b1, &lds_ti, &lds_flag};
   const int b = blockIdx.x;
-  int item = -1, kind = 0, per = 1;
+  // Read the launch parameters that select the item and its tile in one
+  // batch of scalar loads: left to itself the compiler loads them one branch
+  // at a time, a memory round trip each, before the item's first data load.
+  asm volatile("" ::"s"(P.mode), "s"(P.xcd_local), "s"(P.xcd_remap), "s"(P.n_tiles), "s"(P.ks),
+               "s"(P.nc), "s"(P.n_items_a), "s"(P.n_items_b), "s"(P.grid), "s"(P.n_seg),
+               "s"(P.ptrs_in_plan), "s"(P.seg_tile0[0]), "s"(P.seg_tok0[0]), "s"(P.seg_ntok[0]));
+  int g = -1, c = 0, kind = 0;
   if (P.mode == kModeFusedDep) {
-    if (b < P.n_items_a) { item = b; kind = 0; per = P.ks; }
-    else if (b < P.n_items_a + P.n_items_b) { item = b - P.n_items_a; kind = 3; per = P.nc; }
+    if (P.xcd_local) {
+      // XCD x = b % 8 runs tiles x, x + 8, ...: their shrink parts first, then
+      // their expands (workgroup b runs on XCD b % 8)
+      const int x = b & 7, j = b >> 3;
+      const int tx = (P.n_tiles - x + 7) >> 3;
+      if (j < tx * P.ks) {
+        const int i = j / P.ks;
+        g = x + 8 * i; c = j - i * P.ks; kind = 0;
+      } else if (j < tx * (P.ks + P.nc)) {
+        const int j2 = j - tx * P.ks, i = j2 / P.nc;
+        g = x + 8 * i; c = j2 - i * P.nc; kind = 3;
+      }
+    } else if (b < P.n_items_a) {
+      g = b / P.ks; c = b - g * P.ks; kind = 0;
+    } else if (b < P.n_items_a + P.n_items_b) {
+      const int it = b - P.n_items_a;
+      g = it / P.nc; c = it - g * P.nc; kind = 3;
+    }
   } else {
     int it = b;
     if (P.xcd_remap) {
       const int q = P.grid >> 3;
       it = (b & 7) * q + (b >> 3);
     }
-    if (it < P.n_items_a) item = it;
+    const int per = P.mode == kModeShrink ? P.ks : P.nc;
+    if (it < P.n_items_a) { g = it / per; c = it - g * per; }
     kind = P.mode == kModeShrink ? 0 : (P.mode == kModeExpand ? 1 : 2);
-    per = P.mode == kModeShrink ? P.ks : P.nc;
   }
-  if (item >= 0) {
-    const int g = item / per, c = item - g * per;
+  if (g >= 0) {
     const TileInfo t = tile_info(P, g, L.ti);
     if (RBMAX == 1 || t.rank <= 32) run_item<1>(P, L, t, kind, c);
     else if (RBMAX == 2 || t.rank <= 64) run_item<(RBMAX >= 2 ? 2 : 1)>(P, L, t, kind, c);
     else run_item<RBMAX>(P, L, t, kind, c);
-  }
-  if (P.mode == kModeFusedDep) {
-    // the last workgroup to finish returns every counter of this launch to
-    // zero (thread 0's earlier counter atomics have returned before this one
-    // is issued, so every tile increment lands before the done count does)
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int old = __hip_atomic_fetch_add(P.counters + kCtrDone, 1, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      if (old == P.grid - 1) {
-        for (int g = 0; g < P.n_tiles; ++g)
-          __hip_atomic_store(P.counters + kCtrTiles + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(P.counters + kCtrDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
   }
 }
 
@@ -880,11 +1122,16 @@ static hipError_t launch_fwd_t(const PT& P, int rbmax, hipStream_t stream) {
 
 // Launches with the smallest plan type that holds the segments: the plan is
 // the kernel argument, and its size is part of every launch's host cost.
-hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream) {
+// wptr / vptr (or null): per segment weight addresses for small plans whose
+// header sets ptrs_in_plan.
+hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream, const uint64_t* wptr,
+                      const uint64_t* vptr) {
   if (P.n_seg <= kSmallSeg) {
     FwdPlanT<kSmallSeg> Q{};
     static_cast<FwdHeader&>(Q) = static_cast<const FwdHeader&>(P);
     for (int i = 0; i < P.n_seg; ++i) {
+      Q.seg_wptr[i] = wptr ? wptr[i] : 0;
+      Q.seg_vptr[i] = vptr ? vptr[i] : 0;
       Q.seg_tok0[i] = P.seg_tok0[i];
       Q.seg_ntok[i] = P.seg_ntok[i];
       Q.seg_tile0[i] = P.seg_tile0[i];

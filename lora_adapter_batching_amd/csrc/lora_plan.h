@@ -14,6 +14,7 @@ constexpr int kTileM = 32;     // tokens per tile (the N side of a 32x32 MFMA)
 constexpr int kMaxSeg = 128;   // segments per forward launch
 constexpr int kMaxJobs = 64;   // adapter jobs per weight-gradient launch
 constexpr int kMaxJobSeg = 128;
+constexpr int kMaxPartials = 512;  // (tile, k-chunk) parts in split modes (bounds the workspace)
 
 // Forward-style launch modes (also used for the backward du/dx pass).
 enum FwdMode : int32_t {
@@ -21,12 +22,14 @@ enum FwdMode : int32_t {
   kModeExpand = 1,     // items: (tile, n-chunk). U is read from memory
   kModeFusedTile = 2,  // items: (tile, n-chunk). Each computes the tile's full shrink on chip
   kModeFusedDep = 3,   // items [0, a): (tile, k-chunk) shrink parts; [a, a+b): (tile, n-chunk)
-                       // expands that wait on the tile's counter, then sum the parts
+                       // expands that wait for the parts' stamps, then sum the parts
 };
 
-// Counter layout inside the workspace (int32 words).
-constexpr int kCtrDone = 0;      // workgroups finished (kModeFusedDep)
-constexpr int kCtrTiles = 64;    // per-tile arrival counters start here
+// Counter layout inside the workspace (int32 words): per-tile arrival
+// counters of split shrink-only calls. The part stamps of kModeFusedDep
+// follow at byte offset kStampOffset (one uint64 per (tile, k-chunk)).
+constexpr int kCtrTiles = 64;        // per-tile arrival counters start here
+constexpr int kStampOffset = 4096;   // bytes from the counters to the stamps
 
 struct FwdHeader {
   const uint16_t* X;  // shrink input rows, bf16 (x forward, dy backward)
@@ -44,6 +47,8 @@ struct FwdHeader {
   const int32_t* token_rows;  // row of X/Y for each sorted position, or null
   float* partials;            // split-K partial sums [tile][ks][32][rpad]
   int32_t* counters;          // workspace counters (zero on entry and on exit)
+  uint64_t* stamps;           // kModeFusedDep: stamp of each shrink part ((launch_id << 8) | XCD)
+  uint64_t launch_id;         // unique per launch (56 bits, never 0)
   int32_t K;                  // shrink reduction length
   int32_t N;                  // expand output width
   int32_t v_round;            // expand weight row stride = round_up(rank, v_round)
@@ -60,13 +65,22 @@ struct FwdHeader {
   int32_t n_items_a;
   int32_t n_items_b;
   int32_t xcd_remap;    // 1: map consecutive items of phase A to the same XCD
+  int32_t xcd_local;    // kModeFusedDep: all items of a tile run on XCD (tile % 8)
   int32_t grid;         // launched workgroups
   int32_t spin_ticks;   // wall-clock ticks an expand waits before computing the shrink itself
+  int32_t ptrs_in_plan; // small plans: weight addresses are in seg_wptr / seg_vptr
 };
 
-// Segment table of a launch (struct of arrays), CAP entries.
+constexpr int kSmallSeg = 16;  // capacity of the small plan (decode batches)
+
+// Segment table of a launch (struct of arrays), CAP entries. Small plans can
+// also carry each segment's weight addresses (taken from the caller's host
+// copies of the pointer tables).
 template <int CAP>
 struct FwdPlanT : FwdHeader {
+  static constexpr int kPtrCap = CAP <= kSmallSeg ? CAP : 1;
+  uint64_t seg_wptr[kPtrCap];
+  uint64_t seg_vptr[kPtrCap];
   int32_t seg_tok0[CAP];
   int32_t seg_ntok[CAP];
   int32_t seg_tile0[CAP];
@@ -75,7 +89,6 @@ struct FwdPlanT : FwdHeader {
   uint8_t seg_rank[CAP];
   uint8_t seg_slot[CAP];
 };
-constexpr int kSmallSeg = 16;  // capacity of the small plan (decode batches)
 using FwdPlan = FwdPlanT<kMaxSeg>;
 
 // Weight-gradient launch: items are (job, kind, column chunk); a job is one

@@ -46,7 +46,7 @@ class GpuProblem:
     permuted on the host before upload.
     """
 
-    def __init__(self, prob, use_token_rows: bool = False, y0: bool = False):
+    def __init__(self, prob, use_token_rows: bool = False, y0: bool = False, host_tables: bool = True):
         import torch
         import lora_adapter_batching_amd as L
         self.prob = prob
@@ -66,7 +66,8 @@ class GpuProblem:
             self.y_init = torch.zeros((prob.T, prob.h_out), dtype=torch.bfloat16, device="cuda")
         self.A = [dev_bf16(a) if a.size else None for a in prob.A]
         self.B = [dev_bf16(b) if b.size else None for b in prob.B]
-        self.adapters = L.Adapters(self.A, self.B, prob.ranks, prob.scales, prob.h_in, prob.h_out)
+        self.adapters = L.Adapters(self.A, self.B, prob.ranks, prob.scales, prob.h_in, prob.h_out,
+                                   host_tables=host_tables)
         tr = torch.from_numpy(self.perm.copy()).to("cuda") if use_token_rows else None
         self.token_rows = tr
         self.segments = L.Segments(self.seg_starts, self.seg_adapter, tr)

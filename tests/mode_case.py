@@ -1,7 +1,7 @@
 """One forward parity case under a forced launch layout (run as a child
 process by test_gpu_modes.py: the layout override is read once per process).
 
-Usage: LORA_SGMV_FORCE=<tile:NC | dep:KS:NC> python mode_case.py <seed>
+Usage: LORA_SGMV_FORCE=<tile:NC | dep:KS:NC[:TICKS] | loc:KS:NC[:TICKS]> python mode_case.py <seed>
 Prints one line "max_y_err max_u_err" and exits 0.
 """
 import os

@@ -101,6 +101,34 @@ def _mixed_problem(seed, T=300, h_in=264, h_out=200, y0=True):
     return make_custom(seed, h_in, h_out, ranks, scales="random", ids=ids, y0=y0)
 
 
+def test_weight_addresses_from_device_tables_and_host_copies():
+    """Small launches take weight addresses from the host copies of the
+    pointer tables when the caller gives them, else from the device tables:
+    both against the oracle, and bit-identical to each other (fused, shrink
+    and expand)."""
+    L = _L()
+    import torch
+    prob = _mixed_problem(4)
+    ob = oracle_batch(prob)
+    outs = []
+    for host_tables in (True, False):
+        gp = GpuProblem(prob, host_tables=host_tables)
+        assert len(gp.seg_adapter) <= 16
+        _say(f"weight addresses host_tables={host_tables}")
+        y, u = _run_fused(gp)
+        _check_forward(gp, ob, y, u)
+        u2 = gp.new_u()
+        L.sgmv_shrink(gp.x, gp.adapters, gp.segments, u2, L.new_workspace(L.OP_SHRINK, gp.adapters, gp.segments))
+        y2 = gp.new_y()
+        L.sgmv_expand(u2, gp.adapters, gp.segments, y2)
+        torch.cuda.synchronize()
+        _check_forward(gp, ob, y2, u2)
+        outs.append([t.view(torch.int16).cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+                     for t in (y, u, y2, u2)])
+    for a, b in zip(*outs):  # u starts as NaN: unwritten entries stay NaN in both
+        assert np.array_equal(a, b, equal_nan=True)
+
+
 @pytest.mark.parametrize("use_token_rows", [False, True])
 def test_mixed_ranks_ragged(use_token_rows):
     L = _L()

@@ -26,6 +26,32 @@ def test_library_exports_every_declared_symbol():
     assert L.version() >= 100
 
 
+def test_binding_structs_match_the_c_header(tmp_path):
+    """Field offsets and sizes of the ctypes mirrors equal the C compiler's
+    layout of lora_adapters_t and lora_segments_t."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    checks = []
+    for cname, py in (("lora_adapters_t", B.CAdapters), ("lora_segments_t", B.CSegments)):
+        checks.append((cname, "sizeof", f"sizeof({cname})", ctypes.sizeof(py)))
+        for f, _ in py._fields_:
+            checks.append((cname, f, f"offsetof({cname}, {f})", getattr(py, f).offset))
+    src = "#include <stddef.h>\n#include <stdio.h>\n#include \"lora_sgmv.h\"\nint main(void) {\n"
+    for _, _, expr, _ in checks:
+        src += f'  printf("%zu\\n", (size_t)({expr}));\n'
+    src += "  return 0;\n}\n"
+    c = tmp_path / "layout.c"
+    c.write_text(src)
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    for (cname, f, _, want), g in zip(checks, got):
+        assert g == want, f"{cname}.{f}: C {g}, ctypes {want}"
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_segments_from_ids_bit_exact(seed):
     rng = np.random.default_rng(seed)

@@ -23,9 +23,9 @@ def _device_asm(src, tmp_path):
     if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
         pytest.skip("hipcc not available")
     out = tmp_path / (os.path.basename(src) + ".s")
-    cmd = [HIPCC if os.path.exists(HIPCC) else "hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
-           "--cuda-device-only", "-S", "-o", str(out), src]
+    from lora_adapter_batching_amd.build import CODEGEN_FLAGS
+    cmd = [HIPCC if os.path.exists(HIPCC) else "hipcc"] + CODEGEN_FLAGS + [
+        "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S", "-o", str(out), src]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
     return out.read_text()

@@ -390,7 +390,8 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
         P.nblk = cdiv(nblocks, std::min(fp.nc, nblocks));
         P.nc = cdiv(nblocks, P.nblk);
         P.n_items_a = tiles * P.nc;
-        P.grid = P.n_items_a;
+        P.xcd_remap = xcd_remap_enabled(false) ? 1 : 0;
+        P.grid = P.xcd_remap ? round_up(P.n_items_a, 8) : P.n_items_a;
       } else if (fp.mode == kModeFusedDep && tiles * fp.ks <= kMaxPartials) {
         P.mode = kModeFusedDep;
         P.kchunk = round_up(cdiv(c.K, fp.ks), 64);

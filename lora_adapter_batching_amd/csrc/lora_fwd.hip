@@ -478,33 +478,49 @@ __device__ __forceinline__ void stg_mfma(const StgCtx<RB>& C, const PFrags<RB>& 
                                          const uint16_t* vs, int wave, int lane) {
   using G = Geo<RB>;
   constexpr int NB = G::CW / 32;  // 32-column blocks per chunk
+  constexpr int BW = NB / 4;      // blocks per wave
   const int m = lane & 31, h = lane >> 5;
+  // all LDS reads first, then the blocks' MFMA chains interleaved so that
+  // their latencies overlap; blocks past the item's columns are computed
+  // into LDS columns that are never stored
+  u32x4 vf[BW][2 * RB], y0[BW], y1[BW];
 #pragma unroll
-  for (int q = wave; q < NB; q += 4) {
-    const int col0 = 32 * q;
-    if (cs + col0 >= C.c1) break;  // uniform
-    f32x16 acc = zero_acc16();
+  for (int b = 0; b < BW; ++b) {
+    const int col0 = 32 * (wave + 4 * b);
     const uint16_t* vrow = vs + (col0 + colmap(m)) * G::RP + 8 * h;
 #pragma unroll
-    for (int kb = 0; kb < 2 * RB; ++kb) {
-      if (kb < C.kbn) {
-        const u32x4 vf = ld16(vrow + 16 * kb);
-        acc = mfma32(as_bf16x8(vf), F.hi[kb], acc);
-        acc = mfma32(as_bf16x8(vf), F.lo[kb], acc);
-      }
-    }
+    for (int kb = 0; kb < 2 * RB; ++kb)
+      if (kb < C.kbn) vf[b][kb] = ld16(vrow + 16 * kb);
     // token m, columns col0 + 8h + [0, 8) and col0 + 16 + 8h + [0, 8)
-    uint16_t* yr = ys + m * G::CWP + col0 + 8 * h;
+    const uint16_t* yr = ys + m * G::CWP + col0 + 8 * h;
+    y0[b] = ld16(yr);
+    y1[b] = ld16(yr + 16);
+  }
+  f32x16 acc[BW];
+#pragma unroll
+  for (int b = 0; b < BW; ++b) acc[b] = zero_acc16();
+#pragma unroll
+  for (int kb = 0; kb < 2 * RB; ++kb)
+    if (kb < C.kbn) {
+#pragma unroll
+      for (int b = 0; b < BW; ++b) acc[b] = mfma32(as_bf16x8(vf[b][kb]), F.hi[kb], acc[b]);
+#pragma unroll
+      for (int b = 0; b < BW; ++b) acc[b] = mfma32(as_bf16x8(vf[b][kb]), F.lo[kb], acc[b]);
+    }
+#pragma unroll
+  for (int b = 0; b < BW; ++b) {
+    uint16_t* yr = ys + m * G::CWP + 32 * (wave + 4 * b) + 8 * h;
     float f[8];
-    unpack8(ld16(yr), f);
+    unpack8(y0[b], f);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = f[i] + C.oscale * acc[i];
+    for (int i = 0; i < 8; ++i) f[i] = f[i] + C.oscale * acc[b][i];
     st16(yr, pack8(f));
-    unpack8(ld16(yr + 16), f);
+    unpack8(y1[b], f);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = f[i] + C.oscale * acc[8 + i];
+    for (int i = 0; i < 8; ++i) f[i] = f[i] + C.oscale * acc[b][8 + i];
     st16(yr + 16, pack8(f));
   }
+  (void)cs;
 }
 
 template <int RB>

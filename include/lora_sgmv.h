@@ -40,9 +40,10 @@
  *    enqueue work and never synchronise the device.
  *  - Workspace: size it with lora_workspace_size(). It must be filled with
  *    zero bytes once before its first use; every call returns its counters
- *    to zero when its work completes. Calls that share a workspace must be
- *    ordered (same stream, or synchronised): concurrent calls on one
- *    workspace race.
+ *    to zero when its work completes. The hand-off stamps a call leaves in
+ *    it carry that call's unique 56-bit id, so no later call can take them
+ *    for its own. Calls that share a workspace must be ordered (same stream,
+ *    or synchronised): concurrent calls on one workspace race.
  *  - Errors: every entry point returns a lora_status_t and never aborts.
  *    All metadata checks run on the HOST mirrors before any HIP call, so a
  *    rejected call has touched no device state. A failed HIP call returns

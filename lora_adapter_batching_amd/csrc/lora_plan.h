@@ -46,7 +46,7 @@ struct FwdHeader {
   int64_t v_slot_elems;
   const int32_t* token_rows;  // row of X/Y for each sorted position, or null
   float* partials;            // split-K partial sums [tile][ks][32][rpad]
-  int32_t* counters;          // workspace counters (zero on entry and on exit)
+  int32_t* counters;          // shrink-only arrival counters (zero on entry and on exit)
   uint64_t* stamps;           // kModeFusedDep: stamp of each shrink part ((launch_id << 8) | XCD)
   uint64_t launch_id;         // unique per launch (56 bits, never 0)
   int32_t K;                  // shrink reduction length

@@ -55,6 +55,7 @@ constexpr int kMaxSlots = kMaxJobs;   // adapters per backward group
 struct DeviceInfo {
   int cus = 256;
   int wall_khz = 100000;
+  int xccs = 8;  // XCDs of the device (workgroup b runs on XCD b % xccs)
 };
 
 DeviceInfo device_info() {
@@ -71,6 +72,8 @@ DeviceInfo device_info() {
       d.cus = v;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) == hipSuccess && v > 0)
       d.wall_khz = v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && v > 0)
+      d.xccs = v;
     cache[dev] = d;
     have[dev] = true;
   }
@@ -400,13 +403,14 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
         P.nc = cdiv(nblocks, P.nblk);
         P.n_items_a = tiles * P.ks;
         P.n_items_b = tiles * P.nc;
-        P.xcd_local = fp.local;
+        P.xcd_local = fp.local && dev.xccs == 8 ? 1 : 0;
         P.grid = P.xcd_local ? local_grid(tiles, P.ks, P.nc) : P.n_items_a + P.n_items_b;
         if (fp.spin >= 0) P.spin_ticks = fp.spin;
-      } else if (4 * tiles <= cus && xcd_remap_enabled(true)) {
+      } else if (4 * tiles <= cus && dev.xccs == 8 && xcd_remap_enabled(true)) {
         // small batch: each tile's shrink is split along k into parts and its
         // expand into column chunks, all on one XCD, so the parts reach the
-        // expands through that XCD's L2. About two workgroups per CU.
+        // expands with plain accesses through that XCD's L2 (the item order
+        // assumes 8 XCDs). About two workgroups per CU.
         P.mode = kModeFusedDep;
         const int per_xcd_tiles = (tiles + 7) / 8;
         const int slots_per_xcd = 2 * cus / 8;

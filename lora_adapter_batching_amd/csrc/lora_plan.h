@@ -14,7 +14,7 @@ constexpr int kTileM = 32;     // tokens per tile (the N side of a 32x32 MFMA)
 constexpr int kMaxSeg = 128;   // segments per forward launch
 constexpr int kMaxJobs = 64;   // adapter jobs per weight-gradient launch
 constexpr int kMaxJobSeg = 128;
-constexpr int kMaxPartials = 512;  // (tile, k-chunk) parts in split modes (bounds the workspace)
+constexpr int kMaxPartials = 2048;  // (tile, k-chunk) parts in split modes (bounds the workspace)
 
 // Forward-style launch modes (also used for the backward du/dx pass).
 enum FwdMode : int32_t {

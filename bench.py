@@ -13,6 +13,7 @@ entries time the prefill, heterogeneous-rank and packed-training workloads
 with HIP events (GB/s, TFLOP/s, fractions of the MI355X peaks).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu]
+       python bench.py --sweep-adapters   (packed vs one-adapter-at-a-time calls, N = 1..32)
 """
 from __future__ import annotations
 
@@ -338,6 +339,129 @@ def bench_secondary(reps=20):
 
 
 # ---------------------------------------------------------------------------
+# Packed vs one-adapter-at-a-time: N adapters in one call against N calls of
+# one adapter each, on the same kernels and the same tokens
+# ---------------------------------------------------------------------------
+def _adapter_subset(L, A, B, ranks, scales, h_in, h_out, idx):
+    return L.Adapters([A[i] for i in idx], [B[i] for i in idx], np.asarray(ranks)[idx],
+                      np.asarray(scales)[idx], h_in, h_out)
+
+
+def _sweep_decode(L, counts, reps):
+    """gate_up (2560->19456, rank 32) over the 256-token decode batch: token
+    ids uniform in [0, 8) are folded onto n adapters (id mod n)."""
+    import torch
+    from workloads import make_c2_projections
+    p = make_c2_projections(1)["gate_up"]
+    A = [dev_bf16(a) for a in p.A]
+    B = [dev_bf16(b) for b in p.B]
+    out = []
+    for n in counts:
+        ids = (np.asarray(p.token_ids) % n).astype(np.int32)
+        perm, starts, adap = L.segments_from_ids(ids, n)
+        x = dev_bf16(p.x[perm])
+        y = torch.zeros((p.T, p.h_out), dtype=torch.bfloat16, device="cuda")
+        ad = _adapter_subset(L, A, B, p.ranks, p.scales, p.h_in, p.h_out, list(range(n)))
+        sg = L.Segments(starts, adap)
+        ws = L.new_workspace(L.OP_FUSED, ad, sg)
+        packed = _time_calls(lambda i: L.sgmv_fused(x, ad, sg, y, None, ws), reps)
+        # one adapter per call: its rows only (views of the same buffers)
+        single = []
+        for a in range(n):
+            t0, t1 = int(starts[a]), int(starts[a + 1])
+            if t1 == t0:
+                continue
+            ad1 = _adapter_subset(L, A, B, p.ranks, p.scales, p.h_in, p.h_out, [a])
+            sg1 = L.Segments(np.array([0, t1 - t0], np.int32), np.array([0], np.int32))
+            single.append((x[t0:t1], ad1, sg1, y[t0:t1], L.new_workspace(L.OP_FUSED, ad1, sg1)))
+
+        def seq(i):
+            for xs, a1, s1, ys, w1 in single:
+                L.sgmv_fused(xs, a1, s1, ys, None, w1)
+        sequential = _time_calls(seq, reps)
+        b, _ = fwd_work(p.h_in, p.h_out, p.ranks[:n], starts, adap)
+        tp, tsq = float(np.median(packed)), float(np.median(sequential))
+        out.append({"adapters": n, "tokens": int(p.T), "packed_us": round(tp * 1e6, 2),
+                    "sequential_us": round(tsq * 1e6, 2), "speedup": round(tsq / tp, 3),
+                    "packed_GBs": round(b / tp / 1e9, 1), "launches_sequential": len(single)})
+        log(f"sweep decode n={n}: {out[-1]}")
+    return out
+
+
+def _sweep_train(L, counts, reps):
+    """Packed training (3584->3584, ranks in {8,16,32,64}, 4 x 512 tokens per
+    adapter, adapter-major): fused forward saving u, then the packed
+    backward, for the first n adapters in one call each, against the same two
+    calls made once per adapter."""
+    import torch
+    from workloads import make_config
+    prob = make_config("train")
+    per = int(prob.T // prob.N)  # tokens per adapter
+    x_all = dev_bf16(prob.x)
+    dy_all = dev_bf16(prob.dy)
+    A = [dev_bf16(a) for a in prob.A]
+    B = [dev_bf16(b) for b in prob.B]
+    rmax = int(prob.ranks.max())
+    dA = [torch.zeros((int(r), prob.h_in), dtype=torch.float32, device="cuda") for r in prob.ranks]
+    dB = [torch.zeros((prob.h_out, int(r)), dtype=torch.float32, device="cuda") for r in prob.ranks]
+    seg_lens = np.asarray(prob.seg_lens)
+    seg_ad = np.asarray(prob.seg_adapter)
+    out = []
+
+    def case(idx):
+        """Buffers for one call over adapters idx (their tokens are contiguous)."""
+        t0, t1 = idx[0] * per, (idx[-1] + 1) * per
+        sel = np.isin(seg_ad, idx)
+        lens = seg_lens[sel]
+        local = np.searchsorted(np.asarray(idx), seg_ad[sel]).astype(np.int32)
+        starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        ad = _adapter_subset(L, A, B, prob.ranks, prob.scales, prob.h_in, prob.h_out, list(idx))
+        sg = L.Segments(starts, local)
+        x, dy = x_all[t0:t1], dy_all[t0:t1]
+        y = torch.zeros((t1 - t0, prob.h_out), dtype=torch.bfloat16, device="cuda")
+        dx = torch.zeros((t1 - t0, prob.h_in), dtype=torch.bfloat16, device="cuda")
+        u = torch.zeros((t1 - t0, rmax), dtype=torch.float32, device="cuda")
+        pa = torch.tensor([dA[i].data_ptr() for i in idx], dtype=torch.int64, device="cuda")
+        pb = torch.tensor([dB[i].data_ptr() for i in idx], dtype=torch.int64, device="cuda")
+        wsf = L.new_workspace(L.OP_FUSED, ad, sg)
+        wsb = L.new_workspace(L.OP_BACKWARD, ad, sg)
+
+        def run():
+            L.sgmv_fused(x, ad, sg, y, u, wsf)
+            L.packed_backward(x, dy, u, ad, sg, dx, pa, pb, 0, wsb)
+        return run, starts, local
+
+    for n in counts:
+        run_p, starts, local = case(list(range(n)))
+        packed = _time_calls(lambda i: run_p(), reps)
+        singles = [case([a])[0] for a in range(n)]
+
+        def seq(i):
+            for r in singles:
+                r()
+        sequential = _time_calls(seq, reps)
+        bf, ff = fwd_work(prob.h_in, prob.h_out, prob.ranks[:n], starts, local, save_u=True)
+        bb, fb = bwd_work(prob.h_in, prob.h_out, prob.ranks[:n], starts, local)
+        tp, tsq = float(np.median(packed)), float(np.median(sequential))
+        out.append({"adapters": n, "tokens": n * per, "packed_us": round(tp * 1e6, 1),
+                    "sequential_us": round(tsq * 1e6, 1), "speedup": round(tsq / tp, 3),
+                    "packed_tokens_per_s": round(n * per / tp), "packed_GBs": round((bf + bb) / tp / 1e9, 1),
+                    "packed_TFLOPs": round((ff + fb) / tp / 1e12, 2)})
+        log(f"sweep train n={n}: {out[-1]}")
+        del singles, run_p
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_adapter_sweep(reps=20):
+    import lora_adapter_batching_amd as L
+    L.load()
+    return {"sweep": "packed_vs_sequential_adapters",
+            "decode_gate_up_2560x19456_256tok_r32": _sweep_decode(L, (1, 2, 4, 8), reps),
+            "train_fwd_bwd_3584x3584_2048tok_per_adapter": _sweep_train(L, (1, 2, 4, 8, 16, 32), reps // 2)}
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on the host cores
 # ---------------------------------------------------------------------------
 def bench_cpu(bytes_per_step, budget_s=10.0):
@@ -369,6 +493,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sweep-adapters", action="store_true",
+                    help="only time N packed adapters in one call against N one-adapter calls")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -385,6 +511,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": a.numel()}))
+        return
+    if args.sweep_adapters:
+        print(json.dumps(bench_adapter_sweep()), flush=True)
         return
     import lora_adapter_batching_amd as L
     L.load()

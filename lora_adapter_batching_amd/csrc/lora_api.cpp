@@ -24,6 +24,7 @@ hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream, const uin
                       const uint64_t* vptr);
 hipError_t launch_transpose(const TransposePlan& P, hipStream_t stream);
 hipError_t launch_wgrad(const WgradPlan& P, int grid, hipStream_t stream);
+hipError_t launch_wgrad_reduce(const WgradReducePlan& R, hipStream_t stream);
 int wgrad_items_for_rank(int rank, int h_in, int h_out);
 }  // namespace lora
 
@@ -86,6 +87,7 @@ int round_up(int a, int b) { return (a + b - 1) / b * b; }
 // RB = 1, 2 or 4 rank blocks of 32.
 int rpad_for(int rmax) { return rmax <= 32 ? 32 : (rmax <= 64 ? 64 : 128); }
 int64_t round_up64(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -184,10 +186,29 @@ int max_rank_used(const std::vector<ActiveSeg>& v) {
 // Workspace layout
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t counters = 0, partials = 0, du = 0, urec = 0, bt = 0, at = 0, total = 0;
+  size_t counters = 0, partials = 0, du = 0, urec = 0, bt = 0, at = 0, wpart = 0, total = 0;
   int64_t lddu = 0;
   int64_t bt_slot = 0, at_slot = 0;  // elements per slot
+  int64_t wpart_stride = 0;          // floats per weight-gradient partial slot
+  int wpart_slots = 0;               // partial slots of split weight-gradient jobs
 };
+
+// Partial slots for token-range splits of the weight gradients: one slot
+// holds one adapter's dB and dA at the largest rank. A part covers at least
+// kSplitMinSteps 32-token steps, so a batch of T tokens has at most
+// T / (32 kSplitMinSteps) parts; the slots together stay under
+// kSplitBudgetBytes.
+constexpr int kSplitMinSteps = 8;
+constexpr size_t kSplitBudgetBytes = (size_t)64 << 20;
+int64_t wpart_stride_for(const lora_adapters_t* a, int rmax) {
+  return round_up64((int64_t)(a->h_in + a->h_out) * std::max(rmax, 1), 64);
+}
+int wpart_slots_for(const lora_adapters_t* a, int rmax, int64_t T) {
+  const int64_t per = wpart_stride_for(a, rmax) * (int64_t)sizeof(float);
+  int64_t n = std::min<int64_t>({(int64_t)kMaxJobs, T / (kTileM * kSplitMinSteps),
+                                 (int64_t)(kSplitBudgetBytes / (size_t)per)});
+  return n >= 2 ? (int)n : 0;
+}
 
 WsLayout ws_layout(int op, const lora_adapters_t* a, const lora_segments_t* s) {
   WsLayout L;
@@ -219,6 +240,9 @@ WsLayout ws_layout(int op, const lora_adapters_t* a, const lora_segments_t* s) {
     L.at_slot = round_up64((int64_t)a->h_in * round_up(std::max(rmax, 1), 8), 8);
     L.bt = take((size_t)slots * L.bt_slot * 2);
     L.at = take((size_t)slots * L.at_slot * 2);
+    L.wpart_stride = wpart_stride_for(a, rmax);
+    L.wpart_slots = wpart_slots_for(a, rmax, T);
+    L.wpart = take((size_t)L.wpart_slots * L.wpart_stride * sizeof(float));
   }
   L.total = off;
   return L;
@@ -765,23 +789,102 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
     if ((st = run_fwd(c, gsegs, slot_of, strm))) return st;
   }
 
-  // weight gradients: one job per adapter (split if it has too many segments)
-  struct Job { int adapter, rank, accum; float scale; std::vector<std::pair<int, int>> segs; };
+  // weight gradients: one job per adapter (several chained jobs if it has
+  // too many segments)
+  struct Job {
+    int adapter, rank, accum;
+    float scale;
+    std::vector<std::pair<int, int>> segs;
+    int part = -1;  // >= 0: a token-range part writing partial slot `part`
+  };
   std::vector<Job> jobs;
+  std::vector<std::vector<std::pair<int, int>>> per(N);
+  for (const auto& s : segs) per[s.adapter].push_back({s.tok0, s.ntok});
+  // Load balance ("Technische Samenvatting: PLoRA" (gist.science),
+  // "Kernelontwerp": balance over heterogeneous adapters): when the jobs
+  // leave at least half of the GPU's resident workgroup slots idle, the
+  // adapters with the longest token walks get their token ranges cut into
+  // parts that run side by side, each into its own partial slot; a reduce
+  // pass adds the parts in slot order, so the result does not depend on
+  // scheduling. Parts go one at a time to the adapter whose part is longest,
+  // while slots and idle workgroup slots last; the split is kept only if it
+  // cuts the longest walk by at least 1.5x (a partial split that leaves an
+  // unsplit adapter as long as before only adds traffic).
+  std::vector<int> nparts(N, 1);
   {
-    std::vector<std::vector<std::pair<int, int>>> per(N);
-    for (const auto& s : segs) per[s.adapter].push_back({s.tok0, s.ntok});
+    const int slots_gpu = 2 * device_info().cus;
+    int64_t items = 0;
+    std::vector<int> steps(N, 0), it(N, 0);
     for (int a = 0; a < N; ++a) {
-      if (adapters->ranks[a] == 0) continue;
-      if (per[a].empty()) {
-        if (!accumulate) jobs.push_back(Job{a, adapters->ranks[a], 0, adapters->scales[a], {}});
-        continue;
+      if (adapters->ranks[a] == 0 || per[a].empty()) continue;
+      for (auto& p : per[a]) steps[a] += cdiv(p.second, kTileM);
+      it[a] = wgrad_items_for_rank(adapters->ranks[a], adapters->h_in, adapters->h_out);
+      items += it[a];
+    }
+    int free_slots = L.wpart_slots;
+    if (items > 0 && 2 * items <= slots_gpu && free_slots >= 2) {
+      auto part_len = [&](int a) { return cdiv(steps[a], nparts[a]); };
+      int crit0 = 0;
+      for (int a = 0; a < N; ++a) crit0 = std::max(crit0, steps[a]);
+      for (;;) {
+        int best = -1;
+        for (int a = 0; a < N; ++a)
+          if (steps[a] > 0 && (best < 0 || part_len(a) > part_len(best))) best = a;
+        if (best < 0) break;
+        const int np = nparts[best] + 1;
+        const int cost = nparts[best] == 1 ? 2 : 1;  // a split adapter uses a slot per part
+        if ((int)per[best].size() > kMaxJobSeg || steps[best] / np < kSplitMinSteps ||
+            cost > free_slots || items + it[best] > slots_gpu)
+          break;
+        nparts[best] = np;
+        free_slots -= cost;
+        items += it[best];
       }
-      for (size_t k = 0; k < per[a].size(); k += kMaxJobSeg) {
-        Job j{a, adapters->ranks[a], (accumulate || k > 0) ? 1 : 0, adapters->scales[a], {}};
-        for (size_t q = k; q < std::min(per[a].size(), k + kMaxJobSeg); ++q) j.segs.push_back(per[a][q]);
+      int crit1 = 0;
+      for (int a = 0; a < N; ++a)
+        if (steps[a] > 0) crit1 = std::max(crit1, part_len(a));
+      if (2 * crit0 < 3 * crit1) std::fill(nparts.begin(), nparts.end(), 1);
+    }
+  }
+  struct Red { int adapter, slot0, nparts; };
+  std::vector<Red> reds;
+  int next_slot = 0;
+  for (int a = 0; a < N; ++a) {
+    if (adapters->ranks[a] == 0) continue;
+    if (per[a].empty()) {
+      if (!accumulate) jobs.push_back(Job{a, adapters->ranks[a], 0, adapters->scales[a], {}});
+      continue;
+    }
+    if (nparts[a] > 1) {
+      // part p takes 32-token steps [p S / P, (p + 1) S / P) of the adapter's
+      // S steps, in segment order; a segment cut inside keeps whole steps
+      int S = 0;
+      for (auto& p : per[a]) S += cdiv(p.second, kTileM);
+      const int P = nparts[a];
+      reds.push_back(Red{a, next_slot, P});
+      size_t seg = 0;
+      int off = 0;  // tokens of per[a][seg] already given out
+      for (int p = 0; p < P; ++p) {
+        int need = (int)((int64_t)(p + 1) * S / P - (int64_t)p * S / P);
+        Job j{a, adapters->ranks[a], 0, adapters->scales[a], {}, next_slot + p};
+        while (need > 0 && seg < per[a].size()) {
+          const int t0 = per[a][seg].first + off;
+          const int left = per[a][seg].second - off;
+          const int take = std::min(left, need * kTileM);
+          j.segs.push_back({t0, take});
+          need -= cdiv(take, kTileM);
+          off += take;
+          if (off >= per[a][seg].second) { ++seg; off = 0; }
+        }
         jobs.push_back(std::move(j));
       }
+      next_slot += P;
+      continue;
+    }
+    for (size_t k = 0; k < per[a].size(); k += kMaxJobSeg) {
+      Job j{a, adapters->ranks[a], (accumulate || k > 0) ? 1 : 0, adapters->scales[a], {}};
+      for (size_t q = k; q < std::min(per[a].size(), k + kMaxJobSeg); ++q) j.segs.push_back(per[a][q]);
+      jobs.push_back(std::move(j));
     }
   }
   // heavy jobs first; continuation jobs of one adapter must land in later launches
@@ -807,19 +910,23 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
     W.U = Uuse; W.ldu = lduse; W.dU = dU; W.lddu = L.lddu;
     W.dA_tab = dA_ptrs; W.dB_tab = dB_ptrs; W.token_rows = segments->token_rows;
     W.h_in = adapters->h_in; W.h_out = adapters->h_out;
+    W.part_base = reinterpret_cast<float*>(wsb + L.wpart);
+    W.part_stride = L.wpart_stride;
     int nj = 0, nseg = 0, grid = 0;
     std::vector<int> adapter_in_launch(N, 0);
     for (size_t ii = 0; ii < idx.size(); ++ii) {
       const size_t j = idx[ii];
       if (done[j]) continue;
       const Job& J = jobs[j];
-      if (adapter_in_launch[J.adapter]) continue;  // keeps an adapter's parts ordered
       if (nj >= kMaxJobs || nseg + (int)J.segs.size() > kMaxJobSeg) break;
-      // a continuation part may only run after its first part
-      bool earlier_pending = false;
-      for (size_t q = 0; q < jobs.size(); ++q)
-        if (!done[q] && q != j && jobs[q].adapter == J.adapter && jobs[q].accum < J.accum) earlier_pending = true;
-      if (earlier_pending) continue;
+      if (J.part < 0) {
+        // chained jobs of one adapter: one per launch, in order
+        if (adapter_in_launch[J.adapter]) continue;
+        bool earlier_pending = false;
+        for (size_t q = 0; q < jobs.size(); ++q)
+          if (!done[q] && q != j && jobs[q].adapter == J.adapter && jobs[q].accum < J.accum) earlier_pending = true;
+        if (earlier_pending) continue;
+      }
       W.job_item0[nj] = grid;
       W.job_adapter[nj] = J.adapter;
       W.job_seg0[nj] = nseg;
@@ -829,9 +936,10 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
       W.job_accum[nj] = J.accum;
       W.job_scale[nj] = J.scale;
       W.job_rank[nj] = J.rank;
+      W.job_part[nj] = J.part;
       for (auto& p : J.segs) { W.seg_tok0[nseg] = p.first; W.seg_ntok[nseg] = p.second; ++nseg; }
       grid += wgrad_items_for_rank(J.rank, adapters->h_in, adapters->h_out);
-      adapter_in_launch[J.adapter] = 1;
+      if (J.part < 0) adapter_in_launch[J.adapter] = 1;
       done[j] = 1;
       --remaining;
       ++nj;
@@ -841,6 +949,28 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
     W.job_item0[nj] = grid;
     const hipError_t e = launch_wgrad(W, grid, strm);
     if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "weight-gradient launch failed: %s", hipGetErrorString(e));
+  }
+  if (!reds.empty()) {
+    WgradReducePlan R;
+    std::memset(&R, 0, sizeof(R));
+    R.part_base = reinterpret_cast<const float*>(wsb + L.wpart);
+    R.part_stride = L.wpart_stride;
+    R.dA_tab = dA_ptrs; R.dB_tab = dB_ptrs;
+    R.h_in = adapters->h_in; R.h_out = adapters->h_out;
+    R.accumulate = accumulate ? 1 : 0;
+    int grid = 0;
+    for (const Red& r : reds) {
+      const int j = R.n_red++;
+      R.red_item0[j] = grid;
+      R.red_adapter[j] = r.adapter;
+      R.red_rank[j] = adapters->ranks[r.adapter];
+      R.red_slot0[j] = r.slot0;
+      R.red_nparts[j] = r.nparts;
+      grid += (int)cdiv64((int64_t)(adapters->h_in + adapters->h_out) * R.red_rank[j], kReduceElems);
+    }
+    R.red_item0[R.n_red] = grid;
+    const hipError_t e = launch_wgrad_reduce(R, strm);
+    if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "weight-gradient reduce launch failed: %s", hipGetErrorString(e));
   }
   return LORA_OK;
 }

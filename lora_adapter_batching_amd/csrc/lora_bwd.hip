@@ -207,6 +207,9 @@ __device__ __forceinline__ void wgrad_item(const WgradPlan& P, int job, int kind
   const bool is_db = kind == 0;
   float* out = reinterpret_cast<float*>(is_db ? P.dB_tab[a] : P.dA_tab[a]);
   if (!out) return;  // whole workgroup: uniform
+  // a token-range part of a split job writes its own slot (summed later)
+  const int part = P.job_part[job];
+  if (part >= 0) out = P.part_base + (int64_t)part * P.part_stride + (is_db ? 0 : (int64_t)P.h_out * rank);
   const uint16_t* Z = is_db ? P.dy : P.x;
   const int64_t ldz = is_db ? P.lddy : P.ldx;
   const float* Q = is_db ? P.U : P.dU;
@@ -260,7 +263,7 @@ __device__ __forceinline__ void wgrad_item(const WgradPlan& P, int job, int kind
   }
   // lane holds C[m = 4g + i][n = cl] of block (q, kb): column c0 + QN*m + q
   // (the A-operand row m came from lane m's columns), rank 16kb + cl
-  const bool accum = P.job_accum[job] != 0;
+  const bool accum = part < 0 && P.job_accum[job] != 0;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int k = 16 * kb + cl;
@@ -324,6 +327,38 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_kernel(WgradPlan P) {
     case 4: wgrad_item<4, wgrad_qn(4), GATHER>(P, job, kind, chunk, Qt); break;
     default: wgrad_item<8, wgrad_qn(8), GATHER>(P, job, kind, chunk, Qt); break;
   }
+}
+
+// Sum of split jobs' parts: workgroup w of adapter j takes kReduceElems
+// consecutive floats of the adapter's flattened gradients (dB [h_out][r],
+// then dA [r][h_in]); both sizes are multiples of 8 floats, so a thread's 4
+// floats never straddle the two. The parts are added in slot order.
+__global__ __launch_bounds__(kThreads) void wgrad_reduce_kernel(WgradReducePlan R) {
+  __shared__ int red_of_item;
+  const int item = blockIdx.x;
+  {
+    const int j = min((int)threadIdx.x, kMaxJobs - 1);
+    if ((int)threadIdx.x < R.n_red && item >= R.red_item0[j] && item < R.red_item0[j + 1]) red_of_item = j;
+  }
+  __syncthreads();
+  const int j = __builtin_amdgcn_readfirstlane(red_of_item);
+  const int a = R.red_adapter[j], rank = R.red_rank[j];
+  const int64_t n_db = (int64_t)R.h_out * rank, n_all = n_db + (int64_t)R.h_in * rank;
+  const int64_t e = (int64_t)(item - R.red_item0[j]) * kReduceElems + 4 * threadIdx.x;
+  if (e >= n_all) return;
+  float* dst = reinterpret_cast<float*>(e < n_db ? R.dB_tab[a] : R.dA_tab[a]);
+  if (!dst) return;
+  dst += e < n_db ? e : e - n_db;
+  const float* src = R.part_base + (int64_t)R.red_slot0[j] * R.part_stride + e;
+  f32x4 sum = *reinterpret_cast<const f32x4*>(src);
+  for (int p = 1; p < R.red_nparts[j]; ++p) sum += *reinterpret_cast<const f32x4*>(src + p * R.part_stride);
+  if (R.accumulate) sum = *reinterpret_cast<const f32x4*>(dst) + sum;
+  *reinterpret_cast<f32x4*>(dst) = sum;
+}
+
+hipError_t launch_wgrad_reduce(const WgradReducePlan& R, hipStream_t stream) {
+  hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(R.red_item0[R.n_red]), dim3(kThreads), 0, stream, R);
+  return hipGetLastError();
 }
 
 int wgrad_items_for_rank(int rank, int h_in, int h_out) {

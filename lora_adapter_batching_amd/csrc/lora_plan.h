@@ -116,9 +116,33 @@ struct WgradPlan {
   int32_t job_accum[kMaxJobs];
   float job_scale[kMaxJobs];
   int32_t job_rank[kMaxJobs];
+  int32_t job_part[kMaxJobs];  // -1: write the adapter's gradients; else partial slot index
   int32_t seg_tok0[kMaxJobSeg];
   int32_t seg_ntok[kMaxJobSeg];
+  float* part_base;     // partial slots: slot s = dB part [h_out][r] then dA part [r][h_in]
+  int64_t part_stride;  // floats per slot
 };
+
+// Sum of the token-range parts of split weight-gradient jobs: for adapter
+// red_adapter[j], its gradients (dB then dA, flattened) become
+// (accumulate ? old : 0) + sum of slots red_slot0[j] .. red_slot0[j] + red_nparts[j] - 1,
+// added in slot order.
+struct WgradReducePlan {
+  const float* part_base;
+  int64_t part_stride;
+  const uint64_t* dA_tab;
+  const uint64_t* dB_tab;
+  int32_t h_in;
+  int32_t h_out;
+  int32_t n_red;
+  int32_t accumulate;
+  int32_t red_item0[kMaxJobs + 1];  // first workgroup of each adapter; [n_red] = grid
+  int32_t red_adapter[kMaxJobs];
+  int32_t red_rank[kMaxJobs];
+  int32_t red_slot0[kMaxJobs];
+  int32_t red_nparts[kMaxJobs];
+};
+constexpr int kReduceElems = 4 * kThreads;  // floats per reduce workgroup
 
 // Transposed copies of the adapter weights for the backward du/dx pass.
 struct TransposePlan {

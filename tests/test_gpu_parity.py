@@ -417,3 +417,82 @@ def test_train_qwen2p5_7b_full_size():
     ranks = prob.ranks
     pick = [int(np.argmin(ranks)), int(np.argmax(ranks)), 5, 17]
     _check_backward(gp, ob, dx, dA, dB, adapters=sorted(set(pick)))
+
+
+@pytest.mark.parametrize("flags,use_rows", [(0, False), (1, False), (0, True)])
+def test_backward_split_token_ranges(flags, use_rows):
+    """Few weight-gradient items for the GPU: the token ranges of the two
+    heavy adapters are cut into parts that run side by side and are summed
+    in a second pass (adapter 0 over three ragged segments, adapter 1 over
+    one). A zero entry in the dB table skips that gradient (its buffer keeps
+    its NaN fill) while its dA is still written."""
+    import torch
+    L = _L()
+    ranks = [64, 8, 0, 32]
+    lens = [700, 40, 900, 300, 63, 37]
+    ads = [0, 2, 1, 0, 3, 0]
+    prob = make_custom(31, 512, 384, ranks, scales="random", seg_lens=lens, seg_adapter=ads, with_dy=True)
+    gp = GpuProblem(prob, use_token_rows=use_rows)
+    ob = oracle_batch(prob)
+    if flags:
+        g = np.random.default_rng(32)
+        dA = [torch.tensor(g.standard_normal((r, prob.h_in)), dtype=torch.float32, device="cuda") for r in ranks]
+        dB = [torch.tensor(g.standard_normal((prob.h_out, r)), dtype=torch.float32, device="cuda") for r in ranks]
+        dA0 = [to_f64(t) for t in dA]
+        dB0 = [to_f64(t) for t in dB]
+    else:
+        dA, dB, _, _ = _grad_tables(prob)
+        dA0 = dB0 = None
+    pa = torch.tensor([t.data_ptr() if t.numel() else 0 for t in dA], dtype=torch.int64, device="cuda")
+    pb = torch.tensor([t.data_ptr() if t.numel() and i != 1 else 0 for i, t in enumerate(dB)],
+                      dtype=torch.int64, device="cuda")
+    dB1_before = to_f64(dB[1]).copy()
+    dx = torch.zeros((prob.T, prob.h_in), dtype=torch.bfloat16, device="cuda")
+    ws = L.new_workspace(L.OP_BACKWARD, gp.adapters, gp.segments)
+    _say(f"backward split token ranges flags={flags} token_rows={use_rows}")
+    for _ in range(2):  # the second call reuses the workspace's partial slots
+        if flags:
+            for t, t0 in zip(dA, dA0):
+                t.copy_(torch.from_numpy(t0).float())
+            for t, t0 in zip(dB, dB0):
+                t.copy_(torch.from_numpy(t0).float())
+        dx.zero_()
+        L.packed_backward(gp.x, gp.dy, None, gp.adapters, gp.segments, dx, pa, pb, flags, ws)
+        torch.cuda.synchronize()
+        du_ref, dx_ref, dA_ref, dB_ref = ob.backward()
+        e = rel_err(gp.sorted_rows(dx), dx_ref)
+        assert e <= BF16_TOL, f"dx rel err {e:.3e}"
+        for i in (0, 1, 3):
+            ra = dA_ref[i] + (dA0[i] if dA0 is not None else 0.0)
+            ea = rel_err(to_f64(dA[i]), ra)
+            assert ea <= FP32_TOL, f"dA[{i}] rel err {ea:.3e}"
+            if i == 1:
+                assert np.array_equal(np.isnan(to_f64(dB[1])), np.isnan(dB1_before))
+                assert np.array_equal(np.nan_to_num(to_f64(dB[1]), nan=7.0), np.nan_to_num(dB1_before, nan=7.0))
+                continue
+            rb = dB_ref[i] + (dB0[i] if dB0 is not None else 0.0)
+            eb = rel_err(to_f64(dB[i]), rb)
+            assert eb <= FP32_TOL, f"dB[{i}] rel err {eb:.3e}"
+
+
+def test_backward_split_is_deterministic():
+    """Split weight gradients are bit-identical from call to call (the parts
+    are added in a fixed order)."""
+    import torch
+    L = _L()
+    ranks = [16]
+    prob = make_custom(33, 256, 256, ranks, seg_lens=[3000], seg_adapter=[0], with_dy=True)
+    gp = GpuProblem(prob)
+    outs = []
+    ws = L.new_workspace(L.OP_BACKWARD, gp.adapters, gp.segments)
+    _say("backward split determinism")
+    for _ in range(3):
+        dA, dB, pa, pb = _grad_tables(prob)
+        L.packed_backward(gp.x, gp.dy, None, gp.adapters, gp.segments, None, pa, pb, 0, ws)
+        torch.cuda.synchronize()
+        outs.append((to_f64(dA[0]), to_f64(dB[0])))
+    for a, b in outs[1:]:
+        assert np.array_equal(a, outs[0][0]) and np.array_equal(b, outs[0][1])
+    ob = oracle_batch(prob)
+    _, _, dA_ref, dB_ref = ob.backward()
+    assert rel_err(outs[0][0], dA_ref[0]) <= FP32_TOL and rel_err(outs[0][1], dB_ref[0]) <= FP32_TOL

@@ -16,7 +16,7 @@ namespace lora {
 // Transposed copies: Bt_s = B_i^T [r, h_out]; At_s = A_i^T [h_in, round_up(r,8)]
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void transpose_kernel(TransposePlan P) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ alignas(16) uint16_t tile[64][64 + 8];
   const int per = P.tiles_b + P.tiles_a;
   const int s = blockIdx.x / per;
   const int w0 = blockIdx.x - s * per;
@@ -42,16 +42,44 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(TransposePlan P) {
   }
   const int r0 = (w / tcols) * 64, c0 = (w % tcols) * 64;
   if (r0 >= rows_pad || c0 >= cols) return;
-  for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
-    const int i = e >> 6, j = e & 63;
-    const int sr = r0 + i, sc = c0 + j;
-    tile[i][j] = (sr < rows && sc < cols) ? src[(int64_t)sr * lds + sc] : (uint16_t)0;
+  // loads: 16 bytes (8 elements of one row) per thread and pass when the
+  // source rows are 16-byte aligned (lds a multiple of 8; the base is by
+  // contract), else element by element
+  if ((lds & 7) == 0) {
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int e = threadIdx.x + kThreads * pass;  // 512 pieces of 8 elements
+      const int i = e >> 3, j = (e & 7) * 8;
+      const int sr = r0 + i, sc = c0 + j;
+      u32x4v v = {0u, 0u, 0u, 0u};
+      if (sr < rows && sc < cols)  // cols is a multiple of 8 here, so all 8 are in range
+        v = *reinterpret_cast<const u32x4v*>(src + (int64_t)sr * lds + sc);
+      *reinterpret_cast<u32x4v*>(&tile[i][j]) = v;
+    }
+  } else {
+    for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
+      const int i = e >> 6, j = e & 63;
+      const int sr = r0 + i, sc = c0 + j;
+      tile[i][j] = (sr < rows && sc < cols) ? src[(int64_t)sr * lds + sc] : (uint16_t)0;
+    }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
-    const int i = e >> 6, j = e & 63;
+  // stores: 16 bytes of one destination row per thread and pass (ldd and
+  // rows_pad are multiples of 8, so a piece is either whole or outside)
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int e = threadIdx.x + kThreads * pass;
+    const int i = e >> 3, j = (e & 7) * 8;  // destination row c0 + i, columns r0 + j .. + 7
     const int dr = c0 + i, dc = r0 + j;
-    if (dr < cols && dc < rows_pad) dst[(int64_t)dr * ldd + dc] = tile[j][i];
+    if (dr < cols && dc < rows_pad) {
+      uint32_t q[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        q[h] = (uint32_t)tile[j + 2 * h][i] | ((uint32_t)tile[j + 2 * h + 1][i] << 16);
+      typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+      *reinterpret_cast<u32x4v*>(dst + (int64_t)dr * ldd + dc) = u32x4v{q[0], q[1], q[2], q[3]};
+    }
   }
 }
 

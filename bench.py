@@ -132,11 +132,15 @@ def dev_bf16(bits):
 class DecodeStep:
     """Pre-marshalled C-ABI calls for one decode step over a rotation set."""
 
-    def __init__(self, projs, nsets):
+    def __init__(self, projs, nsets, request_order=False):
         import torch
         import lora_adapter_batching_amd as L
         from lora_adapter_batching_amd import binding as Bd
         self.lib = L.load()
+        # request_order: x and y stay in the order the tokens arrived; every
+        # step uploads its sorted-position -> row table (from the step's own
+        # bookkeeping) and the kernels gather x rows and scatter y rows
+        self.request_order = request_order
         self.Bd = Bd
         p0 = projs["q"]
         self.ids = np.ascontiguousarray(p0.token_ids, np.int32)
@@ -151,10 +155,19 @@ class DecodeStep:
         self.names = ["q", "o", "gate_up"]
         self.sets = []
         self.keep = []
+        if request_order:
+            # one pinned host table, device table and event per rotation set:
+            # a slot's host table is rewritten only after its last upload ended
+            self.rows_host = [torch.zeros(self.T, dtype=torch.int32).pin_memory() for _ in range(nsets)]
+            self.rows_dev = [torch.zeros(self.T, dtype=torch.int32, device="cuda") for _ in range(nsets)]
+            self.rows_ev = [None] * nsets
+            self.cseg_rows = [Bd.CSegments(self.T, self.N + 1, self.starts.ctypes.data, self.adap.ctypes.data,
+                                           r.data_ptr()) for r in self.rows_dev]
         dev_inputs = {}
         for name in self.names:
             p = projs[name]
-            dev_inputs[name] = (dev_bf16(p.x[perm]), [dev_bf16(a) for a in p.A], [dev_bf16(b) for b in p.B])
+            xs = p.x if request_order else p.x[perm]
+            dev_inputs[name] = (dev_bf16(xs), [dev_bf16(a) for a in p.A], [dev_bf16(b) for b in p.B])
         for s in range(nsets):
             calls = []
             for name in self.names:
@@ -180,12 +193,25 @@ class DecodeStep:
 
     def step(self, i, events=None):
         lib = self.lib
-        st = lib.lora_segments_from_ids(self.ids.ctypes.data, self.T, self.N, self.perm.ctypes.data,
+        k = i % len(self.sets)
+        perm_ptr = self.perm.ctypes.data
+        if self.request_order:
+            if self.rows_ev[k] is not None:
+                self.rows_ev[k].synchronize()
+            perm_ptr = self.rows_host[k].data_ptr()
+        st = lib.lora_segments_from_ids(self.ids.ctypes.data, self.T, self.N, perm_ptr,
                                         self.starts.ctypes.data, self.adap.ctypes.data)
         if st:
             raise RuntimeError(lib.lora_last_error().decode())
-        calls = self.sets[i % len(self.sets)]
+        calls = self.sets[k]
         segp = ctypes.byref(self.cseg)
+        if self.request_order:
+            import torch
+            self.rows_dev[k].copy_(self.rows_host[k], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record()
+            self.rows_ev[k] = ev
+            segp = ctypes.byref(self.cseg_rows[k])
         for j, (xp, ldx, adc, yp, ldy, wsp, wsb) in enumerate(calls):
             ev = events if events is not None and events[0] == j else None
             if ev is not None:
@@ -198,6 +224,26 @@ class DecodeStep:
 
 
 EVENT_EVERY = 8  # steps between the steps that carry a pair of timing events
+
+
+def bench_decode_request_order(steps=200, warmup=20, nsets=16):
+    """The decode step with x and y left in request order: the step's
+    bookkeeping writes the row table into pinned memory, it is uploaded, and
+    the kernels gather x rows and scatter y rows through it."""
+    import torch
+    from workloads import make_c2_projections
+    ds = DecodeStep(make_c2_projections(1), nsets, request_order=True)
+    for i in range(warmup):
+        ds.step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ds.step(warmup + i)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    return _entry("decode_request_order_token_rows_qwen3_4b_256tok_8x_r32", np.array([sec]),
+                  ds.bytes_per_step, ds.flops_per_step,
+                  {"note": "wall time per step incl. bookkeeping and the row-table upload"})
 
 
 def bench_decode(steps, warmup, nsets=16):
@@ -297,7 +343,8 @@ def bench_secondary(reps=20):
     import torch
     import lora_adapter_batching_amd as L
     from workloads import make_config
-    out = []
+    out = [bench_decode_request_order()]
+    torch.cuda.empty_cache()
     for cfg, nsets in (("prefill", 3), ("hetero", 2)):
         prob = make_config(cfg)
         sets = [_upload(prob, L) for _ in range(nsets)]

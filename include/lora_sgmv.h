@@ -37,7 +37,9 @@
  *    x/y/dx/dy (an in-kernel gather/scatter, so a request-order batch need
  *    not be permuted by the caller). u and du always use sorted positions.
  *  - Streams: `stream` is a hipStream_t (NULL = the null stream). Calls only
- *    enqueue work and never synchronise the device.
+ *    enqueue work and never synchronise the device. Calls must not be
+ *    captured into a HIP graph: each launch carries a fresh hand-off id in
+ *    its kernel argument, which a replayed graph would repeat.
  *  - Workspace: size it with lora_workspace_size(). It must be filled with
  *    zero bytes once before its first use; every call returns its counters
  *    to zero when its work completes. The hand-off stamps a call leaves in

@@ -223,7 +223,42 @@ class DecodeStep:
                 raise RuntimeError(lib.lora_last_error().decode())
 
 
-EVENT_EVERY = 8  # steps between the steps that carry a pair of timing events
+EVENT_EVERY = 8  # steps between the steps that carry a pair of timing events (breakdown pass)
+
+
+def bench_decode(steps, warmup, nsets=16):
+    import torch
+    from workloads import make_c2_projections
+    projs = make_c2_projections(1)
+    ds = DecodeStep(projs, nsets)
+    for i in range(warmup):
+        ds.step(i)
+    torch.cuda.synchronize()
+    # timed region: wall clock for value, and one pair of HIP events on the
+    # launch stream around the whole region for the mean launch duration
+    # (GPU time of the region / launches, so inter-launch gaps count against
+    # the kernel; no event sits between launches)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        ds.step(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gpu_per_launch = e0.elapsed_time(e1) * 1e-3 / (3 * steps)
+    # breakdown pass (not timed for value): an event pair around one launch
+    # of every EVENT_EVERY-th step, the projections in turn; each pair adds a
+    # few microseconds of its own
+    sampled = list(range(0, steps, EVENT_EVERY))
+    ev = {i: (k % 3, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for k, i in enumerate(sampled)}
+    for i in range(steps):
+        ds.step(warmup + steps + i, ev.get(i))
+    torch.cuda.synchronize()
+    per_launch = [np.array([a.elapsed_time(b) for (j, a, b) in ev.values() if j == jj]) * 1e-3 for jj in range(3)]
+    return ds, (t1 - t0) / steps, gpu_per_launch, per_launch  # seconds
 
 
 def bench_decode_request_order(steps=200, warmup=20, nsets=16):
@@ -244,31 +279,6 @@ def bench_decode_request_order(steps=200, warmup=20, nsets=16):
     return _entry("decode_request_order_token_rows_qwen3_4b_256tok_8x_r32", np.array([sec]),
                   ds.bytes_per_step, ds.flops_per_step,
                   {"note": "wall time per step incl. bookkeeping and the row-table upload"})
-
-
-def bench_decode(steps, warmup, nsets=16):
-    import torch
-    from workloads import make_c2_projections
-    projs = make_c2_projections(1)
-    ds = DecodeStep(projs, nsets)
-    for i in range(warmup):
-        ds.step(i)
-    torch.cuda.synchronize()
-    # timed region: wall clock for value; HIP events around one fused launch
-    # of every EVENT_EVERY-th step, taking the projections in turn (a timing
-    # event costs a few microseconds of GPU time, so recording them around
-    # every launch would slow the step itself)
-    sampled = list(range(0, steps, EVENT_EVERY))
-    ev = {i: (k % 3, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for k, i in enumerate(sampled)}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ds.step(warmup + i, ev.get(i))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    per_launch = [np.array([a.elapsed_time(b) for (j, a, b) in ev.values() if j == jj]) * 1e-3 for jj in range(3)]
-    return ds, (t1 - t0) / steps, per_launch  # seconds, per projection
 
 
 # ---------------------------------------------------------------------------
@@ -337,6 +347,29 @@ def copy_ceiling_gbs(nbytes=1 << 30, reps=10):
     sec = e0.elapsed_time(e1) * 1e-3 / reps
     del a, b
     return 2.0 * nbytes / sec / 1e9
+
+
+def copy_same_bytes_us(nbytes, nsets=16, reps=200):
+    """Mean time of a plain device-to-device copy that moves nbytes in all
+    (nbytes / 2 read, nbytes / 2 written), rotating over nsets buffer pairs so
+    that the Infinity Cache cannot serve it, launched back to back like the
+    decode launches: what a kernel of this size reaches at best."""
+    import torch
+    half = int(nbytes // 2) // 16 * 16
+    src = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+    dst = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+    for i in range(nsets):
+        dst[i].copy_(src[i])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        dst[i % nsets].copy_(src[i % nsets])
+    e1.record()
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del src, dst
+    return us
 
 
 def bench_secondary(reps=20):
@@ -565,23 +598,24 @@ def main():
     import lora_adapter_batching_amd as L
     L.load()
     log("decode step")
-    ds, sec_per_step, per_launch = bench_decode(args.steps, args.warmup)
+    ds, sec_per_step, avg_launch, per_launch = bench_decode(args.steps, args.warmup)
     value = ds.bytes_per_step / sec_per_step / 1e9
     # dominant kernel: the fused launch (sgmv_fwd_kernel), 3 launches per step
-    avg_launch = float(np.mean([pl.mean() for pl in per_launch]))
     bytes_per_launch = ds.bytes_per_step / 3.0
     achieved = bytes_per_launch / avg_launch / 1e9
     traffic = load_traffic(WORKLOAD)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": KERNEL, "avg_launch_us": round(avg_launch * 1e6, 3),
-            "launch_us": {n: round(float(np.median(per_launch[j])) * 1e6, 3)
-                          for j, n in enumerate(ds.names)},
+            "launch_us_event_pairs": {n: round(float(np.median(per_launch[j])) * 1e6, 3)
+                                      for j, n in enumerate(ds.names)},
             "algorithmic_bytes_per_launch": round(bytes_per_launch),
             "event_every_steps": EVENT_EVERY}
     gate = ds.work[2][0] / float(np.median(per_launch[2])) / 1e9
-    roof["gate_up_GBs"] = round(gate, 1)
+    roof["gate_up_GBs_event_pair"] = round(gate, 1)
     roof["copy_ceiling_GBs"] = round(copy_ceiling_gbs(), 1)
+    # the same bytes as one launch, moved by a plain copy (launch-latency floor)
+    roof["copy_same_bytes_us"] = {n: round(copy_same_bytes_us(ds.work[j][0]), 2) for j, n in enumerate(ds.names)}
     out = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec_per_step * 1e3, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

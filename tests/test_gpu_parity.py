@@ -7,7 +7,7 @@ import sys
 import numpy as np
 import pytest
 
-from helpers import BF16_TOL, FP32_TOL, GpuProblem, oracle_batch, rel_err, to_f64
+from helpers import BF16_TOL, FP32_TOL, GpuProblem, dev_bf16, oracle_batch, rel_err, to_f64
 from workloads import make_config, make_custom
 
 pytestmark = pytest.mark.gpu
@@ -223,6 +223,52 @@ def test_decode_qwen3_4b_projections_full():
         _say(f"decode {name} {prob.h_in}->{prob.h_out}")
         y, u = _run_fused(gp)
         _check_forward(gp, ob, y, u)
+
+
+def test_decode_request_order_token_rows_full():
+    """Decode projections at full size with x and y left in request order:
+    the kernels gather x rows and scatter y rows through token_rows."""
+    projs = make_config("decode")
+    for name, prob in projs.items():
+        gp = GpuProblem(prob, use_token_rows=True)
+        ob = oracle_batch(prob)
+        _say(f"decode request order {name} {prob.h_in}->{prob.h_out}")
+        y, u = _run_fused(gp)
+        _check_forward(gp, ob, y, u)
+
+
+def test_decode_changing_batches_one_workspace():
+    """Consecutive decode steps whose adapter ids change from step to step,
+    as in serving: each step groups its ids, uploads its row table into the
+    same device buffer and launches with the same workspace. Every step must
+    match the oracle on its own batch (no hand-off state of an earlier step
+    may leak into a later one)."""
+    import torch
+    L = _L()
+    ranks = [32] * 8
+    base = make_custom(41, 2560, 2560, ranks, ids=np.zeros(256, np.int32))
+    A = [dev_bf16(a) for a in base.A]
+    B = [dev_bf16(b) for b in base.B]
+    ad = L.Adapters(A, B, base.ranks, base.scales, base.h_in, base.h_out)
+    rows = torch.zeros(256, dtype=torch.int32, device="cuda")
+    ws = None
+    for step in range(4):
+        rng = np.random.default_rng(100 + step)
+        ids = rng.integers(-1 if step == 3 else 0, 8, size=256).astype(np.int32)
+        prob = make_custom(41, 2560, 2560, ranks, ids=ids)  # same weights (same seed and shapes), new ids
+        x = dev_bf16(prob.x)
+        perm, starts, adap = L.segments_from_ids(ids, 8)
+        rows.copy_(torch.from_numpy(perm))
+        sg = L.Segments(starts, adap, rows)
+        if ws is None:
+            ws = L.new_workspace(L.OP_FUSED, ad, sg)
+        y = torch.zeros((256, 2560), dtype=torch.bfloat16, device="cuda")
+        _say(f"decode step {step} with changing ids")
+        L.sgmv_fused(x, ad, sg, y, None, ws)
+        torch.cuda.synchronize()
+        y_ref, _ = oracle_batch(prob).forward()
+        e = rel_err(to_f64(y)[perm], y_ref)
+        assert e <= BF16_TOL, f"step {step}: y rel err {e:.3e}"
 
 
 def _sample_rows(gp, n=96, seed=0):

@@ -74,6 +74,20 @@ def fwd_work(h_in, h_out, ranks, seg_starts, seg_adapter, save_u=False):
     return bytes_, flops
 
 
+def shrink_work(h_in, ranks, seg_starts, seg_adapter):
+    """x read, A_i read once, fp32 u written (rank columns only)."""
+    tr = active_token_ranks(ranks, seg_starts, seg_adapter)
+    w = sum(int(ranks[a]) * h_in for a in used_adapters(ranks, seg_starts, seg_adapter))
+    return 2 * len(tr) * h_in + 2 * w + 4 * int(tr.sum()), 2 * h_in * int(tr.sum())
+
+
+def expand_work(h_out, ranks, seg_starts, seg_adapter):
+    """fp32 u read, B_i read once, y read and written."""
+    tr = active_token_ranks(ranks, seg_starts, seg_adapter)
+    w = sum(int(ranks[a]) * h_out for a in used_adapters(ranks, seg_starts, seg_adapter))
+    return 4 * int(tr.sum()) + 2 * w + 4 * len(tr) * h_out, 2 * h_out * int(tr.sum())
+
+
 def bwd_work(h_in, h_out, ranks, seg_starts, seg_adapter):
     tr = active_token_ranks(ranks, seg_starts, seg_adapter)
     T = len(tr)
@@ -317,6 +331,23 @@ def _time_calls(fn, reps, warm=3):
     return np.array([a.elapsed_time(b) for a, b in ts]) * 1e-3
 
 
+def _time_region(fn, reps, warm=8):
+    """Mean seconds per call of `reps` back-to-back calls between one pair of
+    HIP events. For launches shorter than the host's submission time a pair
+    of events around each call would time the host, not the kernel."""
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        fn(i)
+    b.record()
+    b.synchronize()
+    return np.array([a.elapsed_time(b) * 1e-3 / reps])
+
+
 def _entry(name, seconds, bytes_, flops, extra=None):
     med = float(np.median(seconds))
     gbs = bytes_ / med / 1e9
@@ -372,11 +403,45 @@ def copy_same_bytes_us(nbytes, nsets=16, reps=200):
     return us
 
 
+def bench_shrink_expand(reps=20):
+    """The separate shrink (x -> u) and expand (u -> y) entry points on the
+    prefill batch and on the decode gate_up projection (rotated inputs)."""
+    import torch
+    import lora_adapter_batching_amd as L
+    from workloads import make_c2_projections, make_config
+    out = []
+    cases = (("prefill_llama3_8b_8192tok_4096x4096_8x_r16", make_config("prefill"), 3),
+             ("decode_gate_up_2560x19456_256tok_8x_r32", make_c2_projections(1)["gate_up"], 16))
+    for name, prob, nsets in cases:
+        sets = [_upload(prob, L) for _ in range(nsets)]
+        rmax = int(prob.ranks.max())
+        us = [torch.zeros((prob.T, rmax), dtype=torch.float32, device="cuda") for _ in range(nsets)]
+        ws = L.new_workspace(L.OP_SHRINK, sets[0]["ad"], sets[0]["sg"])
+        st, ad = sets[0]["starts"], sets[0]["adap"]
+
+        def shr(i):
+            s = sets[i % nsets]
+            L.sgmv_shrink(s["x"], s["ad"], s["sg"], us[i % nsets], ws)
+
+        def exp(i):
+            s = sets[i % nsets]
+            L.sgmv_expand(us[i % nsets], s["ad"], s["sg"], s["y"], None)
+        b, f = shrink_work(prob.h_in, prob.ranks, st, ad)
+        out.append(_entry(name + "_shrink", _time_region(shr, 10 * reps), b, f, {"timing": "back-to-back calls"}))
+        b, f = expand_work(prob.h_out, prob.ranks, st, ad)
+        out.append(_entry(name + "_expand", _time_region(exp, 10 * reps), b, f, {"timing": "back-to-back calls"}))
+        del sets, us
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_secondary(reps=20):
     import torch
     import lora_adapter_batching_amd as L
     from workloads import make_config
     out = [bench_decode_request_order()]
+    torch.cuda.empty_cache()
+    out += bench_shrink_expand(reps)
     torch.cuda.empty_cache()
     for cfg, nsets in (("prefill", 3), ("hetero", 2)):
         prob = make_config(cfg)

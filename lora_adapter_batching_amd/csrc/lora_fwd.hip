@@ -863,6 +863,53 @@ __device__ __forceinline__ uint64_t load_stamp(const PT& P, int idx) {
   return ((uint64_t)v[1] << 32) | v[0];
 }
 
+// Sums tile t's ks parts in order q = 0, 1, ... into Pl (scaled), with the
+// loads of several parts in flight together; device_scope: the parts were
+// written with device-scope stores (read past the CU's L1 and a stale L2).
+template <int RB, typename PT>
+__device__ __forceinline__ void sum_parts_to_lds(const PT& P, const TileInfo& t, float* Pl, bool device_scope) {
+  const float ps = P.scale_in_shrink ? t.scale : 1.f;
+  constexpr int RC = 32 * RB;                  // rank columns of the P tile
+  constexpr int EPT = kTileM * RC / kThreads;  // elements per thread
+  // the loads of PD parts (all of them for the usual k split) are in flight
+  // together
+  const __amdgpu_buffer_rsrc_t r = mk_rsrc(partial_ptr(P, t.g, 0), (int64_t)P.ks * kTileM * P.rpad * 4);
+  const uint32_t part_bytes = (uint32_t)(kTileM * P.rpad * 4);
+  float s[EPT];
+  uint32_t off[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = threadIdx.x + kThreads * j;
+    const int n = e / RC, k = e - n * RC;
+    off[j] = (uint32_t)((n * P.rpad + k) * 4);
+    s[j] = 0.f;
+  }
+  constexpr int PD = 8 / RB;
+  for (int q0 = 0; q0 < P.ks; q0 += PD) {
+    float v[PD][EPT];
+#pragma unroll
+    for (int d = 0; d < PD; ++d)
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const uint32_t o = q0 + d < P.ks ? (uint32_t)(q0 + d) * part_bytes + off[j] : kOff;
+        v[d][j] = __builtin_bit_cast(float, device_scope ? __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, kAuxDev)
+                                                         : __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0));
+      }
+#pragma unroll
+    for (int d = 0; d < PD; ++d)
+#pragma unroll
+      for (int j = 0; j < EPT; ++j)
+        if (q0 + d < P.ks) s[j] = (q0 + d == 0) ? v[d][j] : s[j] + v[d][j];
+  }
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = threadIdx.x + kThreads * j;
+    const int n = e / RC, k = e - n * RC;
+    Pl[n * kLdp + k] = s[j] * ps;
+  }
+  lds_sync();
+}
+
 // kModeShrink / kModeFusedDep phase A: shrink over k-chunk c.
 template <int RB, typename PT>
 __device__ __forceinline__ void item_shrink(const PT& P, const Lds& L, const TileInfo& t, int c) {
@@ -902,29 +949,27 @@ __device__ __forceinline__ void item_shrink(const PT& P, const Lds& L, const Til
     }
     return;
   }
-  // kModeShrink, ks > 1: partials move with device-coherent atomic swaps
-  // whose returned values each thread waits for; the last arriving chunk
-  // (per-tile counter) sums all chunks in order and returns the counter to 0
-  float sink = 0.f;
+  // kModeShrink, ks > 1: each chunk stores its part with device-scope
+  // stores, waits until they are performed, and counts itself in the tile's
+  // arrival counter; the last arriving chunk sums all parts in order (the
+  // same ordered sum as the fused hand-off, several parts' loads in flight),
+  // writes u and returns the counter to 0
   reduce_waves<RB>(red, acc, wave, lane, [&](int k, int n, float v) __attribute__((always_inline)) {
-    sink += __hip_atomic_exchange(part + n * rpad + k, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(part + n * rpad + k, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   });
-  red[threadIdx.x] = sink;  // waits for every swap of this thread
+  asm volatile("" ::: "memory");
+  wait_vmcnt<0>();  // this thread's part stores have been performed
   int* ctr = P.counters + kCtrTiles + t.g;
-  __syncthreads();
+  __syncthreads();  // ... and every thread's
   if (threadIdx.x == 0) *L.flag = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (*L.flag != P.ks - 1) return;
-  for (int e = threadIdx.x; e < kTileM * t.rank; e += kThreads) {
-    const int n = e / t.rank, k = e - n * t.rank;
-    if (n >= t.cnt) continue;
-    float s = __hip_atomic_load(partial_ptr(P, t.g, 0) + n * rpad + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int q = 1; q < P.ks; ++q)
-      s += __hip_atomic_load(partial_ptr(P, t.g, q) + n * rpad + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    P.U[(int64_t)(t.p0 + n) * P.ldu + k] = s * ps;
-  }
+  float* Pl = L.Pl();
+  sum_parts_to_lds<RB>(P, t, Pl, true);
+  store_u_from_lds(P, t, Pl);
   if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
 
 // kModeFusedDep phase B: wait for the tile's parts, sum them in order,
 // expand n-chunk c. If the parts do not all arrive within spin_ticks (their
@@ -960,48 +1005,10 @@ __device__ __forceinline__ bool wait_and_sum_parts(const PT& P, const Lds& L, co
   }
   __syncthreads();
   if (!*L.flag) return false;
-  const float ps = P.scale_in_shrink ? t.scale : 1.f;
-  constexpr int RC = 32 * RB;                  // rank columns of the P tile
-  constexpr int EPT = kTileM * RC / kThreads;  // elements per thread
-  // the loads of PD parts (all of them for the usual k split) are in flight
-  // together
-  const __amdgpu_buffer_rsrc_t r = mk_rsrc(partial_ptr(P, t.g, 0), (int64_t)P.ks * kTileM * P.rpad * 4);
-  const uint32_t part_bytes = (uint32_t)(kTileM * P.rpad * 4);
-  float s[EPT];
-  uint32_t off[EPT];
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int e = threadIdx.x + kThreads * j;
-    const int n = e / RC, k = e - n * RC;
-    off[j] = (uint32_t)((n * P.rpad + k) * 4);
-    s[j] = 0.f;
-  }
-  constexpr int PD = 8 / RB;
-  for (int q0 = 0; q0 < P.ks; q0 += PD) {
-    float v[PD][EPT];
-#pragma unroll
-    for (int d = 0; d < PD; ++d)
-#pragma unroll
-      for (int j = 0; j < EPT; ++j) {
-        const uint32_t o = q0 + d < P.ks ? (uint32_t)(q0 + d) * part_bytes + off[j] : kOff;
-        v[d][j] = __builtin_bit_cast(float, P.xcd_local ? __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0)
-                                                        : __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, kAuxDev));
-      }
-#pragma unroll
-    for (int d = 0; d < PD; ++d)
-#pragma unroll
-      for (int j = 0; j < EPT; ++j)
-        if (q0 + d < P.ks) s[j] = (q0 + d == 0) ? v[d][j] : s[j] + v[d][j];
-  }
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int e = threadIdx.x + kThreads * j;
-    const int n = e / RC, k = e - n * RC;
-    Pl[n * kLdp + k] = s[j] * ps;
-  }
-  lds_sync();
+  sum_parts_to_lds<RB>(P, t, Pl, P.xcd_local == 0);
   return true;
 }
+
 
 template <int RB, typename PT>
 __device__ __forceinline__ void item_expand_wait(const PT& P, const Lds& L, const TileInfo& t, int c) {

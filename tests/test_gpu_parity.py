@@ -225,6 +225,30 @@ def test_decode_qwen3_4b_projections_full():
         _check_forward(gp, ob, y, u)
 
 
+@pytest.mark.parametrize("use_rows", [False, True])
+def test_decode_shrink_then_expand_split_k(use_rows):
+    """The separate shrink and expand calls on the decode projections: a
+    decode batch has few tiles, so the shrink splits h_in = 2560 into parts
+    whose last arriving workgroup sums them in order (per-tile counters that
+    must return to zero: the call is made twice on one workspace)."""
+    import torch
+    L = _L()
+    projs = make_config("decode")
+    for name in ("q", "gate_up"):
+        prob = projs[name]
+        gp = GpuProblem(prob, use_token_rows=use_rows)
+        ob = oracle_batch(prob)
+        u = gp.new_u()
+        ws = L.new_workspace(L.OP_SHRINK, gp.adapters, gp.segments)
+        _say(f"decode {name} shrink (split k) + expand token_rows={use_rows}")
+        for _ in range(2):
+            y = gp.new_y()
+            L.sgmv_shrink(gp.x, gp.adapters, gp.segments, u, ws)
+            L.sgmv_expand(u, gp.adapters, gp.segments, y, None)
+        torch.cuda.synchronize()
+        _check_forward(gp, ob, y, u)
+
+
 def test_decode_request_order_token_rows_full():
     """Decode projections at full size with x and y left in request order:
     the kernels gather x rows and scatter y rows through token_rows."""

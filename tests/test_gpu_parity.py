@@ -2,6 +2,7 @@
 the same seeded inputs. Element-by-element at oracle-friendly sizes, sampled
 rows (or whole adapters) at the full workload sizes.
 """
+import copy
 import sys
 
 import numpy as np
@@ -127,6 +128,47 @@ def test_weight_addresses_from_device_tables_and_host_copies():
                      for t in (y, u, y2, u2)])
     for a, b in zip(*outs):  # u starts as NaN: unwritten entries stay NaN in both
         assert np.array_equal(a, b, equal_nan=True)
+
+
+@pytest.mark.parametrize("host_tables", [True, False])
+def test_in_place_weight_update_and_table_swap(host_tables):
+    """Adapters stay registered while their weights change: (1) new values
+    written into the same A/B buffers between two calls (an optimizer step in
+    place) and (2) the pointer table entries of two adapters re-pointed to a
+    second set of buffers (double-buffered weights) are both picked up by the
+    next call, each checked against the oracle on the new weights."""
+    import torch
+    L = _L()
+    prob = _mixed_problem(6)
+    gp = GpuProblem(prob, host_tables=host_tables)
+    ws = L.new_workspace(L.OP_FUSED, gp.adapters, gp.segments)
+    _say(f"in-place weight update host_tables={host_tables}")
+    y, u = _run_fused(gp, ws=ws)
+    _check_forward(gp, ob=oracle_batch(prob), y=y, u=u)
+    # (1) in place: the same buffers, weights of another seed
+    prob2 = make_custom(prob.seed + 100, prob.h_in, prob.h_out, list(prob.ranks), ids=prob.token_ids)
+    for i in range(prob.N):
+        if gp.A[i] is not None:
+            gp.A[i].copy_(dev_bf16(prob2.A[i]))
+            gp.B[i].copy_(dev_bf16(prob2.B[i]))
+    upd = copy.copy(prob)  # same x, y0, ids and scales; the new weights
+    upd.A, upd.B = list(prob2.A), list(prob2.B)
+    y, u = _run_fused(gp, ws=ws)
+    _check_forward(gp, ob=oracle_batch(upd), y=y, u=u)
+    # (2) re-point adapters 0 and 4 to fresh buffers (device table, and the
+    # host copies when the call carries them)
+    prob3 = make_custom(prob.seed + 200, prob.h_in, prob.h_out, list(prob.ranks), ids=prob.token_ids)
+    keep = []
+    for i in (0, 4):
+        a, b = dev_bf16(prob3.A[i]), dev_bf16(prob3.B[i])
+        keep += [a, b]
+        gp.adapters.A_ptrs[i] = a.data_ptr()
+        gp.adapters.B_ptrs[i] = b.data_ptr()
+        gp.adapters.A_host[i] = a.data_ptr()
+        gp.adapters.B_host[i] = b.data_ptr()
+        upd.A[i], upd.B[i] = prob3.A[i], prob3.B[i]
+    y, u = _run_fused(gp, ws=ws)
+    _check_forward(gp, ob=oracle_batch(upd), y=y, u=u)
 
 
 @pytest.mark.parametrize("use_token_rows", [False, True])

@@ -435,6 +435,47 @@ def bench_shrink_expand(reps=20):
     return out
 
 
+def bench_host(reps=2000):
+    """Host-side costs: the token bookkeeping (request-order ids -> segments
+    and row table, a counting sort in the library) at decode and
+    packed-training sizes, and the host time of one fused decode call
+    (validation, planning and the launch itself) through the C ABI."""
+    import lora_adapter_batching_amd as L
+    lib = L.load()
+    out = []
+    rng = np.random.default_rng(7)
+    for T, N in ((256, 8), (65536, 32)):
+        ids = rng.integers(0, N, size=T).astype(np.int32)
+        perm = np.zeros(T, np.int32)
+        st = np.zeros(N + 2, np.int32)
+        ad = np.zeros(N + 1, np.int32)
+        n = reps if T <= 4096 else max(20, reps // 50)
+        t0 = time.perf_counter()
+        for _ in range(n):
+            lib.lora_segments_from_ids(ids.ctypes.data, T, N, perm.ctypes.data, st.ctypes.data, ad.ctypes.data)
+        us = (time.perf_counter() - t0) / n * 1e6
+        out.append({"workload": f"host_bookkeeping_{T}tok_{N}_adapters", "us": round(us, 3),
+                    "note": "lora_segments_from_ids through ctypes, host only"})
+    return out
+
+
+def bench_host_call(ds, reps=300):
+    """Host time of one fused decode call (q projection) through the C ABI,
+    issued while the GPU is kept busy so that launches never wait."""
+    import torch
+    lib = ds.lib
+    xp, ldx, adc, yp, ldy, wsp, wsb = ds.sets[0][0]
+    segp = ctypes.byref(ds.cseg)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        lib.lora_sgmv_fused(xp, ldx, adc, segp, yp, ldy, None, 0, wsp, wsb, ds.stream)
+    t1 = time.perf_counter()
+    torch.cuda.synchronize()
+    return {"workload": "host_cost_per_fused_decode_call", "us": round((t1 - t0) / reps * 1e6, 2),
+            "note": "validation + planning + launch, host side, through ctypes"}
+
+
 def bench_secondary(reps=20):
     import torch
     import lora_adapter_batching_amd as L
@@ -690,11 +731,12 @@ def main():
                       "bytes_per_step": int(ds.bytes_per_step), "flops_per_step": int(ds.flops_per_step),
                       "rotation_sets": len(ds.sets)},
            "roofline": roof}
+    host = bench_host() + [bench_host_call(ds)]
     if not args.no_secondary:
         log("secondary workloads")
         del ds
         torch.cuda.empty_cache()
-        out["secondary"] = bench_secondary()
+        out["secondary"] = host + bench_secondary()
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = bench_cpu(out["config"]["bytes_per_step"])

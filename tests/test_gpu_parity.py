@@ -291,6 +291,44 @@ def test_decode_shrink_then_expand_split_k(use_rows):
         _check_forward(gp, ob, y, u)
 
 
+def test_concurrent_calls_on_two_streams():
+    """Two decode-sized fused calls (split hand-off layout) and a backward
+    enqueued on two non-default streams at once, each with its own
+    workspace: every result matches the oracle (hand-off state lives in the
+    workspace and every launch has its own id)."""
+    import torch
+    L = _L()
+    projs = make_config("decode")
+    cases = []
+    for name in ("q", "o"):
+        prob = projs[name]
+        gp = GpuProblem(prob)
+        cases.append((gp, oracle_batch(prob), L.new_workspace(L.OP_FUSED, gp.adapters, gp.segments)))
+    bprob = make_custom(51, 512, 384, [16, 64], seg_lens=[900, 700], seg_adapter=[0, 1], with_dy=True)
+    bgp = GpuProblem(bprob)
+    bws = L.new_workspace(L.OP_BACKWARD, bgp.adapters, bgp.segments)
+    dA, dB, pa, pb = _grad_tables(bprob)
+    dx = torch.zeros((bprob.T, bprob.h_in), dtype=torch.bfloat16, device="cuda")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    _say("concurrent fused calls and a backward on two streams")
+    ys = [(k, cases[k][0].new_y()) for rep in range(3) for k in range(2)]
+    torch.cuda.synchronize()
+    # everything enqueued without a synchronisation in between: calls on one
+    # stream share its workspace in order, the two streams run side by side
+    for i, (k, y) in enumerate(ys):
+        gp, _, ws = cases[k]
+        L.sgmv_fused(gp.x, gp.adapters, gp.segments, y, None, ws, stream=streams[k])
+        if i == 1:
+            L.packed_backward(bgp.x, bgp.dy, None, bgp.adapters, bgp.segments, dx, pa, pb, 0, bws,
+                              stream=streams[1])
+    torch.cuda.synchronize()
+    for k, y in ys:
+        gp, ob, _ = cases[k]
+        _check_forward(gp, ob, y)
+    _check_backward(bgp, oracle_batch(bprob), dx, dA, dB)
+
+
 def test_decode_request_order_token_rows_full():
     """Decode projections at full size with x and y left in request order:
     the kernels gather x rows and scatter y rows through token_rows."""

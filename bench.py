@@ -14,6 +14,7 @@ with HIP events (GB/s, TFLOP/s, fractions of the MI355X peaks).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu]
        python bench.py --sweep-adapters   (packed vs one-adapter-at-a-time calls, N = 1..32)
+       python bench.py --only prefill|hetero|train [--reps R]   (one workload alone, for counter runs)
 """
 from __future__ import annotations
 
@@ -647,6 +648,44 @@ def bench_adapter_sweep(reps=20):
             "train_fwd_bwd_3584x3584_2048tok_per_adapter": _sweep_train(L, (1, 2, 4, 8, 16, 32), reps // 2)}
 
 
+def bench_only(name, reps=5):
+    """One secondary workload alone (for counter runs): 'prefill' and
+    'hetero' run the fused forward, 'train' the fused forward saving u and
+    then the packed backward, each `reps` times on rotated inputs."""
+    import torch
+    import lora_adapter_batching_amd as L
+    from workloads import make_config
+    prob = make_config(name)
+    nsets = 1 if name == "train" else 2
+    sets = [_upload(prob, L) for _ in range(nsets)]
+    s0 = sets[0]
+    out = {"only": name, "reps": reps}
+    if name != "train":
+        ws = L.new_workspace(L.OP_FUSED, s0["ad"], s0["sg"])
+        sec = _time_calls(lambda i: L.sgmv_fused(sets[i % nsets]["x"], sets[i % nsets]["ad"], sets[i % nsets]["sg"],
+                                                 sets[i % nsets]["y"], None, ws), reps, warm=1)
+        b, f = fwd_work(prob.h_in, prob.h_out, prob.ranks, s0["starts"], s0["adap"])
+        out["fwd"] = _entry(name, sec, b, f)
+    else:
+        dy = dev_bf16(prob.dy)
+        u = torch.zeros((prob.T, int(prob.ranks.max())), dtype=torch.float32, device="cuda")
+        dx = torch.zeros((prob.T, prob.h_in), dtype=torch.bfloat16, device="cuda")
+        dA = [torch.zeros((int(r), prob.h_in), dtype=torch.float32, device="cuda") for r in prob.ranks]
+        dB = [torch.zeros((prob.h_out, int(r)), dtype=torch.float32, device="cuda") for r in prob.ranks]
+        pa = torch.tensor([t.data_ptr() for t in dA], dtype=torch.int64, device="cuda")
+        pb = torch.tensor([t.data_ptr() for t in dB], dtype=torch.int64, device="cuda")
+        wsf = L.new_workspace(L.OP_FUSED, s0["ad"], s0["sg"])
+        wsb = L.new_workspace(L.OP_BACKWARD, s0["ad"], s0["sg"])
+        sf = _time_calls(lambda i: L.sgmv_fused(s0["x"], s0["ad"], s0["sg"], s0["y"], u, wsf), reps, warm=1)
+        sb = _time_calls(lambda i: L.packed_backward(s0["x"], dy, u, s0["ad"], s0["sg"], dx, pa, pb, 0, wsb),
+                         reps, warm=1)
+        bf, ff = fwd_work(prob.h_in, prob.h_out, prob.ranks, s0["starts"], s0["adap"], save_u=True)
+        bb, fb = bwd_work(prob.h_in, prob.h_out, prob.ranks, s0["starts"], s0["adap"])
+        out["fwd"] = _entry(name + "_fwd", sf, bf, ff)
+        out["bwd"] = _entry(name + "_bwd", sb, bb, fb)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on the host cores
 # ---------------------------------------------------------------------------
@@ -679,6 +718,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "hetero", "train"],
+                    help="run one secondary workload alone (counter runs)")
+    ap.add_argument("--reps", type=int, default=5, help="repetitions for --only")
     ap.add_argument("--sweep-adapters", action="store_true",
                     help="only time N packed adapters in one call against N one-adapter calls")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -697,6 +739,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": a.numel()}))
+        return
+    if args.only:
+        print(json.dumps(bench_only(args.only, args.reps)), flush=True)
         return
     if args.sweep_adapters:
         print(json.dumps(bench_adapter_sweep()), flush=True)

@@ -177,6 +177,28 @@ int lora_sgmv_fused(const void* x, int64_t ldx, const lora_adapters_t* adapters,
                     int64_t ldu, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Several LoRA-wrapped projections that read the same x (for example the q,
+ * k and v projections of one attention layer, each with its own set of
+ * adapters) in ONE kernel launch: the one-launch-per-decode-step design
+ * ("Trajectory presenta C-LoRA" (vivodigitale.it), "Come funziona
+ * l'architettura") carried over to the projections of a step that share
+ * their input, so that the launch latency is paid once.
+ *   y[p][row(pos)] += s_p,i B_p,i (A_p,i x[row(pos)])   for p < num_proj
+ * adapters[p]: HOST array of num_proj pointers; every projection has the
+ * same num_adapters and h_in (the segments' adapter ids index all of them),
+ * its own h_out, ranks, scales and weight tables. y[p] / ldy[p]: HOST arrays
+ * of num_proj DEVICE output addresses and row strides (bf16 [*, h_out_p]);
+ * the outputs must not overlap each other or x. 1 <= num_proj <= 4. No u is
+ * saved. The workspace is sized by lora_workspace_size_multi() and follows
+ * the rules of the other calls. Errors as for lora_sgmv_fused().
+ */
+int lora_workspace_size_multi(int32_t num_proj, const lora_adapters_t* const* adapters,
+                              const lora_segments_t* segments, size_t* bytes);
+int lora_sgmv_fused_multi(const void* x, int64_t ldx, int32_t num_proj,
+                          const lora_adapters_t* const* adapters, const lora_segments_t* segments,
+                          void* const* y, const int64_t* ldy, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Packed backward over all adapters of the batch ("Technische Samenvatting: PLoRA" (gist.science), "LoRA
  * Execution Engine": forward and backward cases tiled along the sequence or
  * hidden dimension):

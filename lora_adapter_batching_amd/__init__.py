@@ -16,11 +16,14 @@ from .binding import (  # noqa: F401
     OP_SHRINK,
     load,
     new_workspace,
+    new_workspace_multi,
     packed_backward,
     segments_from_ids,
     sgmv_expand,
     sgmv_fused,
+    sgmv_fused_multi,
     sgmv_shrink,
     version,
     workspace_size,
+    workspace_size_multi,
 )

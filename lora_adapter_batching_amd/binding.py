@@ -47,8 +47,8 @@ class CSegments(ctypes.Structure):
 
 
 EXPORTS = ["lora_segments_from_ids", "lora_workspace_size", "lora_sgmv_shrink", "lora_sgmv_expand",
-           "lora_sgmv_fused", "lora_packed_backward", "lora_status_string", "lora_last_error",
-           "lora_version"]
+           "lora_sgmv_fused", "lora_packed_backward", "lora_workspace_size_multi",
+           "lora_sgmv_fused_multi", "lora_status_string", "lora_last_error", "lora_version"]
 
 _lib = None
 
@@ -75,6 +75,10 @@ def load(path: str = LIB_PATH):
     lib.lora_packed_backward.argtypes = [P, I64, P, I64, P, I64, ctypes.POINTER(CAdapters),
                                          ctypes.POINTER(CSegments), P, I64, P, P, ctypes.c_uint32,
                                          P, ctypes.c_size_t, P]
+    lib.lora_workspace_size_multi.argtypes = [ctypes.c_int32, P, ctypes.POINTER(CSegments),
+                                              ctypes.POINTER(ctypes.c_size_t)]
+    lib.lora_sgmv_fused_multi.argtypes = [P, I64, ctypes.c_int32, P, ctypes.POINTER(CSegments), P, P,
+                                          P, ctypes.c_size_t, P]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_last_error.restype = ctypes.c_char_p
@@ -237,6 +241,40 @@ def packed_backward(x, dy, u, adapters: Adapters, segments: Segments, dx, dA_ptr
         _ptr(u), u.stride(0) if u is not None else 0, adapters.c, segments.c, _ptr(dx),
         dx.stride(0) if dx is not None else 0, _ptr(dA_ptrs), _ptr(dB_ptrs), int(flags), wp, wb,
         _stream_handle(stream)))
+
+
+def _multi_tables(adapters: Sequence[Adapters]):
+    """C array of lora_adapters_t pointers (kept alive by the caller)."""
+    arr = (ctypes.POINTER(CAdapters) * len(adapters))(*[ctypes.pointer(a._c) for a in adapters])
+    return arr
+
+
+def workspace_size_multi(adapters: Sequence[Adapters], segments: Segments) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    arr = _multi_tables(adapters)
+    _check(lib.lora_workspace_size_multi(len(adapters), ctypes.cast(arr, ctypes.c_void_p), segments.c,
+                                         ctypes.byref(n)))
+    return int(n.value)
+
+
+def new_workspace_multi(adapters: Sequence[Adapters], segments: Segments, device="cuda"):
+    """A zero-filled workspace tensor for sgmv_fused_multi."""
+    import torch
+    return torch.zeros(max(workspace_size_multi(adapters, segments), 256), dtype=torch.uint8, device=device)
+
+
+def sgmv_fused_multi(x, adapters: Sequence[Adapters], segments: Segments, ys: Sequence, ws=None, stream=None):
+    """One launch for several projections over the same x: ys[p] +=
+    s B_p,i (A_p,i x) with projection p's adapters."""
+    lib = load()
+    wp, wb = _ws(ws)
+    arr = _multi_tables(adapters)
+    yp = (ctypes.c_void_p * len(ys))(*[_ptr(y) for y in ys])
+    ld = (ctypes.c_int64 * len(ys))(*[y.stride(0) for y in ys])
+    _check(lib.lora_sgmv_fused_multi(_ptr(x), x.stride(0), len(adapters), ctypes.cast(arr, ctypes.c_void_p),
+                                     segments.c, ctypes.cast(yp, ctypes.c_void_p),
+                                     ctypes.cast(ld, ctypes.c_void_p), wp, wb, _stream_handle(stream)))
 
 
 def version() -> int:

@@ -95,6 +95,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct ActiveSeg {
   int tok0, ntok, adapter, rank;
   float scale;
+  int proj = 0;  // projection of a multi-projection call
 };
 
 // ---------------------------------------------------------------------------
@@ -284,6 +285,16 @@ struct FwdCall {
   float* partials;
   int32_t* counters;
   int rmax;  // largest rank of the adapters (partials row length)
+  // multi-projection calls: projections 1 .. n_proj-1 (projection 0 is Y,
+  // ldy, N, Wtab, Vtab and their host copies above)
+  int n_proj;
+  uint16_t* proj_Y[kMaxProj];
+  int64_t proj_ldy[kMaxProj];
+  int proj_N[kMaxProj];
+  const uint64_t* proj_Wtab[kMaxProj];
+  const uint64_t* proj_Vtab[kMaxProj];
+  const uint64_t* proj_Wtab_host[kMaxProj];
+  const uint64_t* proj_Vtab_host[kMaxProj];
 };
 
 // Optional planner override for tuning, read once from LORA_SGMV_FORCE:
@@ -367,6 +378,10 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
     P.K = c.K; P.N = c.N; P.v_round = c.v_round; P.scale_in_shrink = c.scale_in_shrink;
     P.write_u = c.write_u ? 1 : 0;
     P.rpad = rpad_for(c.rmax);
+    for (int q = 1; q < std::max(1, c.n_proj); ++q) {
+      P.proj_Y[q] = c.proj_Y[q]; P.proj_ldy[q] = c.proj_ldy[q]; P.proj_N[q] = c.proj_N[q];
+      P.proj_Wtab[q] = c.proj_Wtab[q]; P.proj_Vtab[q] = c.proj_Vtab[q];
+    }
     int tiles = 0;
     for (int i = 0; i < ns; ++i) {
       const ActiveSeg& s = segs[base + i];
@@ -377,11 +392,17 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
       P.seg_scale[i] = s.scale;
       P.seg_rank[i] = (uint8_t)s.rank;
       P.seg_slot[i] = (uint8_t)(slot_of.empty() ? 0 : slot_of[s.adapter]);
+      P.seg_proj[i] = (uint8_t)s.proj;
       tiles += cdiv(s.ntok, kTileM);
     }
     P.n_seg = ns;
     P.n_tiles = tiles;
-    const int nblocks = cdiv(c.N, 32);
+    // column blocks of the widest projection: the item count per tile is
+    // chosen for it, and every projection splits its own width into as many
+    // items (some of a narrow projection's may be empty)
+    int n_widest = c.N;
+    for (int q = 1; q < c.n_proj; ++q) n_widest = std::max(n_widest, c.proj_N[q]);
+    const int nblocks = cdiv(n_widest, 32);
     const int slots = 2 * cus;  // resident workgroups at the kernels' occupancy
     // split of a shrink-only call's reduction: none when the tiles alone fill
     // the GPU, otherwise chunks of about kShrinkChunk elements
@@ -502,6 +523,10 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
       }
     }
     if (P.grid <= 0) continue;
+    if (c.n_proj > 1) {
+      P.nblk = cdiv(cdiv(c.N, 32), P.nc);
+      for (int q = 1; q < c.n_proj; ++q) P.proj_nblk[q] = cdiv(cdiv(c.proj_N[q], 32), P.nc);
+    }
     int rmax_launch = 0;
     for (int i = 0; i < ns; ++i) rmax_launch = std::max(rmax_launch, (int)P.seg_rank[i]);
     const int rbmax = rmax_launch <= 32 ? 1 : (rmax_launch <= 64 ? 2 : 4);
@@ -509,12 +534,17 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
     // tables (when the call uses tables and has the copies of those it uses)
     uint64_t wq[kSmallSeg], vq[kSmallSeg];
     const bool need_w = c.mode_op != LORA_OP_EXPAND, need_v = c.mode_op != LORA_OP_SHRINK;
-    if (ns <= kSmallSeg && (c.Wtab || c.Vtab) && (!need_w || (c.Wtab && c.Wtab_host)) &&
-        (!need_v || (c.Vtab && c.Vtab_host))) {
+    bool host_tabs = (c.Wtab || c.Vtab) && (!need_w || (c.Wtab && c.Wtab_host)) &&
+                     (!need_v || (c.Vtab && c.Vtab_host));
+    for (int q = 1; q < c.n_proj; ++q)
+      host_tabs = host_tabs && c.proj_Wtab_host[q] && c.proj_Vtab_host[q];
+    if (ns <= kSmallSeg && host_tabs) {
       for (int i = 0; i < ns; ++i) {
-        const int a = segs[base + i].adapter;
-        wq[i] = need_w ? c.Wtab_host[a] : 0;
-        vq[i] = need_v ? c.Vtab_host[a] : 0;
+        const ActiveSeg& sg = segs[base + i];
+        const uint64_t* wt = sg.proj ? c.proj_Wtab_host[sg.proj] : c.Wtab_host;
+        const uint64_t* vt = sg.proj ? c.proj_Vtab_host[sg.proj] : c.Vtab_host;
+        wq[i] = need_w ? wt[sg.adapter] : 0;
+        vq[i] = need_v ? vt[sg.adapter] : 0;
       }
       P.ptrs_in_plan = 1;
     }
@@ -682,6 +712,99 @@ int lora_sgmv_fused(const void* x, int64_t ldx, const lora_adapters_t* adapters,
   c.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
   c.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.counters);
   c.rmax = max_rank_all(adapters);
+  return run_fwd(c, segs, {}, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// Several projections over one x in one launch
+// ---------------------------------------------------------------------------
+// Checks shared by the multi-projection calls; on success *rmax is the
+// largest rank over every projection's adapters.
+static int multi_checks(int32_t num_proj, const lora_adapters_t* const* adapters,
+                        const lora_segments_t* segments, int* rmax) {
+  if (num_proj < 1 || num_proj > kMaxProj)
+    return fail(LORA_INVALID_ARGUMENT, "num_proj must be in [1, %d], got %d", kMaxProj, num_proj);
+  if (!adapters) return fail(LORA_INVALID_ARGUMENT, "adapters is NULL");
+  *rmax = 0;
+  for (int p = 0; p < num_proj; ++p) {
+    if (!adapters[p]) return fail(LORA_INVALID_ARGUMENT, "adapters[%d] is NULL", p);
+    int st = common_checks(adapters[p], segments);
+    if (st) return st;
+    if (adapters[p]->num_adapters != adapters[0]->num_adapters || adapters[p]->h_in != adapters[0]->h_in)
+      return fail(LORA_INVALID_ARGUMENT, "adapters[%d]: every projection needs the same num_adapters and h_in", p);
+    *rmax = std::max(*rmax, max_rank_all(adapters[p]));
+  }
+  return LORA_OK;
+}
+
+// Hand-off words and split-shrink partials of a multi-projection launch:
+// the tiles of every projection share one part budget.
+static size_t multi_ws_bytes(int32_t num_proj, int rmax, const lora_segments_t* s) {
+  const int64_t tiles = (int64_t)cdiv(s->num_tokens, kTileM) + s->num_segments;
+  const int64_t parts = std::max<int64_t>(1, std::min<int64_t>(kMaxPartials, num_proj * tiles * kMaxKs));
+  const size_t part_off = (kCounterBytes + 255) / 256 * 256;
+  return part_off + (size_t)parts * kTileM * rpad_for(rmax) * sizeof(float);
+}
+
+int lora_workspace_size_multi(int32_t num_proj, const lora_adapters_t* const* adapters,
+                              const lora_segments_t* segments, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(LORA_INVALID_ARGUMENT, "bytes is NULL");
+  int rmax = 0;
+  int st = multi_checks(num_proj, adapters, segments, &rmax);
+  if (st) return st;
+  *bytes = multi_ws_bytes(num_proj, rmax, segments);
+  return LORA_OK;
+}
+
+int lora_sgmv_fused_multi(const void* x, int64_t ldx, int32_t num_proj,
+                          const lora_adapters_t* const* adapters, const lora_segments_t* segments,
+                          void* const* y, const int64_t* ldy, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int rmax = 0;
+  int st = multi_checks(num_proj, adapters, segments, &rmax);
+  if (st) return st;
+  if (!y || !ldy) return fail(LORA_INVALID_ARGUMENT, "y / ldy is NULL");
+  std::vector<ActiveSeg> segs;
+  for (int p = 0; p < num_proj; ++p) {
+    auto v = active_segments(adapters[p], segments);
+    if (v.empty()) continue;
+    char name[16];
+    std::snprintf(name, sizeof(name), "y[%d]", p);
+    if ((st = check_rows(y[p], ldy[p], adapters[p]->h_out, name, true))) return st;
+    if (!adapters[p]->A_ptrs || !adapters[p]->B_ptrs)
+      return fail(LORA_INVALID_ARGUMENT, "adapters[%d]: A_ptrs/B_ptrs is NULL", p);
+    for (auto& a : v) a.proj = p;
+    segs.insert(segs.end(), v.begin(), v.end());
+  }
+  if (segs.empty()) return LORA_OK;
+  if ((st = check_rows(x, ldx, adapters[0]->h_in, "x", true))) return st;
+  if ((st = check_ws(ws, ws_bytes, multi_ws_bytes(num_proj, rmax, segments)))) return st;
+  FwdCall c{};
+  c.mode_op = LORA_OP_FUSED;
+  c.X = static_cast<const uint16_t*>(x); c.ldx = ldx;
+  c.Y = static_cast<uint16_t*>(y[0]); c.ldy = ldy[0];
+  c.Wtab = adapters[0]->A_ptrs; c.Vtab = adapters[0]->B_ptrs; c.v_round = 1;
+  if (adapters[0]->A_ptrs_host && adapters[0]->B_ptrs_host) {
+    c.Wtab_host = adapters[0]->A_ptrs_host;
+    c.Vtab_host = adapters[0]->B_ptrs_host;
+  }
+  c.K = adapters[0]->h_in; c.N = adapters[0]->h_out;
+  c.n_proj = num_proj;
+  for (int p = 1; p < num_proj; ++p) {
+    c.proj_Y[p] = static_cast<uint16_t*>(y[p]); c.proj_ldy[p] = ldy[p];
+    c.proj_N[p] = adapters[p]->h_out;
+    c.proj_Wtab[p] = adapters[p]->A_ptrs; c.proj_Vtab[p] = adapters[p]->B_ptrs;
+    if (adapters[p]->A_ptrs_host && adapters[p]->B_ptrs_host) {
+      c.proj_Wtab_host[p] = adapters[p]->A_ptrs_host;
+      c.proj_Vtab_host[p] = adapters[p]->B_ptrs_host;
+    }
+  }
+  c.token_rows = segments->token_rows;
+  const size_t part_off = (kCounterBytes + 255) / 256 * 256;
+  c.counters = reinterpret_cast<int32_t*>(ws);
+  c.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + part_off);
+  c.rmax = rmax;
   return run_fwd(c, segs, {}, static_cast<hipStream_t>(stream));
 }
 

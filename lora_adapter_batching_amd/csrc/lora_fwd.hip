@@ -31,6 +31,7 @@ struct TileInfo {
   int adapter;
   int rank;
   int slot;
+  int proj;  // projection (multi-projection launches; else 0)
   float scale;
   uint64_t wptr, vptr;  // small plans with ptrs_in_plan: the segment's weight addresses
 };
@@ -70,6 +71,7 @@ __device__ __forceinline__ TileInfo tile_info(const PT& P, int g, TileInfo* lds)
     t.adapter = P.seg_adapter[sel];
     t.rank = P.seg_rank[sel];
     t.slot = P.seg_slot[sel];
+    t.proj = P.seg_proj[sel];
     t.scale = P.seg_scale[sel];
     // one scalar load each from the kernel-argument segment at the selected
     // entry (indexing the arrays by value would hold all of them in SGPRs)
@@ -89,6 +91,7 @@ __device__ __forceinline__ TileInfo tile_info(const PT& P, int g, TileInfo* lds)
   const int t1n = P.seg_tile0[min(i + 1, PlanCap<PT>::v - 1)];
   const int tok0 = P.seg_tok0[i], ntok = P.seg_ntok[i];
   const int adapter = P.seg_adapter[i], rank = P.seg_rank[i], slot = P.seg_slot[i];
+  const int proj = P.seg_proj[i];
   const float scale = P.seg_scale[i];
   if (threadIdx.x < P.n_seg) {
     const int t1 = (i + 1 < P.n_seg) ? t1n : P.n_tiles;
@@ -101,6 +104,7 @@ __device__ __forceinline__ TileInfo tile_info(const PT& P, int g, TileInfo* lds)
       t.adapter = adapter;
       t.rank = rank;
       t.slot = slot;
+      t.proj = proj;
       t.scale = scale;
       *lds = t;
     }
@@ -113,22 +117,46 @@ __device__ __forceinline__ TileInfo tile_info(const PT& P, int g, TileInfo* lds)
   t.adapter = __builtin_amdgcn_readfirstlane(t.adapter);
   t.rank = __builtin_amdgcn_readfirstlane(t.rank);
   t.slot = __builtin_amdgcn_readfirstlane(t.slot);
+  t.proj = __builtin_amdgcn_readfirstlane(t.proj);
   t.scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t.scale)));
   return t;
+}
+
+// The output side of a tile's projection: rows, row stride, width, column
+// blocks per expand item, and the weight tables (projection 0 is the plan's
+// own fields; the others come from the plan's projection arrays, read with
+// constant indices so that they stay scalar kernel-argument loads).
+struct ProjView {
+  uint16_t* Y;
+  int64_t ldy;
+  const uint64_t* Wtab;
+  const uint64_t* Vtab;
+  int N;
+  int nblk;
+};
+template <typename PT>
+__device__ __forceinline__ ProjView proj_view(const PT& P, int p) {
+  ProjView v{P.Y, P.ldy, P.Wtab, P.Vtab, P.N, P.nblk};
+#pragma unroll
+  for (int q = 1; q < kMaxProj; ++q)
+    if (p == q) v = ProjView{P.proj_Y[q], P.proj_ldy[q], P.proj_Wtab[q], P.proj_Vtab[q], P.proj_N[q], P.proj_nblk[q]};
+  return v;
 }
 
 template <typename PT>
 __device__ __forceinline__ const uint16_t* w_ptr(const PT& P, const TileInfo& t) {
   if constexpr (PlanCap<PT>::v <= kSmallSeg)
     if (P.ptrs_in_plan) return reinterpret_cast<const uint16_t*>(t.wptr);
-  if (P.Wtab) return reinterpret_cast<const uint16_t*>(P.Wtab[t.adapter]);
+  const uint64_t* tab = proj_view(P, t.proj).Wtab;
+  if (tab) return reinterpret_cast<const uint16_t*>(tab[t.adapter]);
   return P.Wslots + (int64_t)t.slot * P.w_slot_elems;
 }
 template <typename PT>
 __device__ __forceinline__ const uint16_t* v_ptr(const PT& P, const TileInfo& t) {
   if constexpr (PlanCap<PT>::v <= kSmallSeg)
     if (P.ptrs_in_plan) return reinterpret_cast<const uint16_t*>(t.vptr);
-  if (P.Vtab) return reinterpret_cast<const uint16_t*>(P.Vtab[t.adapter]);
+  const uint64_t* tab = proj_view(P, t.proj).Vtab;
+  if (tab) return reinterpret_cast<const uint16_t*>(tab[t.adapter]);
   return P.Vslots + (int64_t)t.slot * P.v_slot_elems;
 }
 
@@ -543,14 +571,15 @@ __device__ __forceinline__ StgCtx<RB> stg_ctx(const PT& P, const TileInfo& t, in
   constexpr int YPR = G::CW / 8;
   constexpr int RPJ = kThreads / YPR;
   StgCtx<RB> C;
-  const TileRows yt = tile_rows(P.Y, P.ldy, P.N, P, t);
+  const ProjView pv = proj_view(P, t.proj);
+  const TileRows yt = tile_rows(pv.Y, pv.ldy, pv.N, P, t);
   C.yr = yt.r;
   const int r0 = threadIdx.x / YPR;
 #pragma unroll
   for (int j = 0; j < G::YV; ++j) C.yoff[j] = row_off(P, t, yt, r0 + RPJ * j);
   C.ldv = ((t.rank + P.v_round - 1) / P.v_round) * P.v_round;
   C.vec16 = (C.ldv & 7) == 0;
-  C.vr = mk_rsrc(v_ptr(P, t), (int64_t)P.N * C.ldv * 2);
+  C.vr = mk_rsrc(v_ptr(P, t), (int64_t)pv.N * C.ldv * 2);
   C.rank = t.rank;
   C.kbn = (t.rank + 15) >> 4;
   const int rv = (int)(C.ldv >> 3);  // vectors per V row (vec16)
@@ -564,10 +593,10 @@ __device__ __forceinline__ StgCtx<RB> stg_ctx(const PT& P, const TileInfo& t, in
     C.vrow[j] = (uint16_t)row;
     C.vlds[j] = (uint16_t)(row * G::RP + 8 * (f - row * rv));
   }
-  const int nblocks = (P.N + 31) >> 5;
-  const int cb0 = c * P.nblk;
+  const int nblocks = (pv.N + 31) >> 5;
+  const int cb0 = c * pv.nblk;
   C.c0 = 32 * cb0;
-  C.c1 = min(P.N, 32 * min(nblocks, cb0 + P.nblk));
+  C.c1 = min(pv.N, 32 * min(nblocks, cb0 + pv.nblk));
   C.oscale = P.scale_in_shrink ? 1.f : t.scale;
   return C;
 }
@@ -721,18 +750,19 @@ __device__ __forceinline__ void exp_block(const ExpCtx<RB>& C, const PFrags<RB>&
 template <int RB, typename PT>
 __device__ __forceinline__ ExpCtx<RB> exp_ctx(const PT& P, const TileInfo& t, int c) {
   ExpCtx<RB> C;
-  const TileRows yt = tile_rows(P.Y, P.ldy, P.N, P, t);
+  const ProjView pv = proj_view(P, t.proj);
+  const TileRows yt = tile_rows(pv.Y, pv.ldy, pv.N, P, t);
   C.yr = yt.r;
   C.yrow = row_off(P, t, yt, threadIdx.x & 31);
   C.ldv = ((t.rank + P.v_round - 1) / P.v_round) * P.v_round;
   C.vec16 = (C.ldv & 7) == 0;
-  C.vr = mk_rsrc(v_ptr(P, t), (int64_t)P.N * C.ldv * 2);
+  C.vr = mk_rsrc(v_ptr(P, t), (int64_t)pv.N * C.ldv * 2);
   C.rank = t.rank;
   C.kbn = (t.rank + 15) >> 4;
-  const int nblocks = (P.N + 31) >> 5;
-  const int cb0 = c * P.nblk;
+  const int nblocks = (pv.N + 31) >> 5;
+  const int cb0 = c * pv.nblk;
   C.c0 = 32 * cb0;
-  C.c1 = min(P.N, 32 * min(nblocks, cb0 + P.nblk));
+  C.c1 = min(pv.N, 32 * min(nblocks, cb0 + pv.nblk));
   C.nb = (C.c1 - C.c0 + 31) >> 5;
   C.oscale = P.scale_in_shrink ? 1.f : t.scale;
   return C;
@@ -780,12 +810,14 @@ __device__ __forceinline__ void store_u_from_lds(const PT& P, const TileInfo& t,
 // stores cover whole rows.
 template <int RB>
 __device__ __forceinline__ bool direct_expand(int nblk) { return nblk <= 4; }
+template <typename PT>
+__device__ __forceinline__ int item_nblk(const PT& P, const TileInfo& t) { return proj_view(P, t.proj).nblk; }
 
 template <int RB, typename PT>
 __device__ __forceinline__ void expand_from_lds(const PT& P, const TileInfo& t, int c, const float* Pl,
                                                 uint8_t* stage) {
   PFrags<RB> F;
-  if (direct_expand<RB>(P.nblk)) {
+  if (direct_expand<RB>(item_nblk(P, t))) {
     const ExpCtx<RB> C = exp_ctx<RB>(P, t, c);
     constexpr int NE = ExpDepth<RB>::v;
     BlkRegs<RB> R[NE];
@@ -1017,7 +1049,7 @@ __device__ __forceinline__ void item_expand_wait(const PT& P, const Lds& L, cons
   // y rows and expand weights do not depend on the shrink: the first loads
   // are issued before waiting
   bool done = false;
-  if (direct_expand<RB>(P.nblk)) {
+  if (direct_expand<RB>(item_nblk(P, t))) {
     const ExpCtx<RB> C = exp_ctx<RB>(P, t, c);
     constexpr int NE = ExpDepth<RB>::v;
     BlkRegs<RB> R[NE];
@@ -1162,6 +1194,7 @@ hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream, const uin
       Q.seg_scale[i] = P.seg_scale[i];
       Q.seg_rank[i] = P.seg_rank[i];
       Q.seg_slot[i] = P.seg_slot[i];
+      Q.seg_proj[i] = P.seg_proj[i];
     }
     return launch_fwd_t(Q, rbmax, stream);
   }

@@ -15,6 +15,7 @@ constexpr int kMaxSeg = 128;   // segments per forward launch
 constexpr int kMaxJobs = 64;   // adapter jobs per weight-gradient launch
 constexpr int kMaxJobSeg = 128;
 constexpr int kMaxPartials = 2048;  // (tile, k-chunk) parts in split modes (bounds the workspace)
+constexpr int kMaxProj = 4;         // projections over one x in one fused launch
 
 // Forward-style launch modes (also used for the backward du/dx pass).
 enum FwdMode : int32_t {
@@ -69,6 +70,15 @@ struct FwdHeader {
   int32_t grid;         // launched workgroups
   int32_t spin_ticks;   // wall-clock ticks an expand waits before computing the shrink itself
   int32_t ptrs_in_plan; // small plans: weight addresses are in seg_wptr / seg_vptr
+  // Projections 1 .. kMaxProj-1 of a multi-projection launch (several
+  // LoRA-wrapped projections over the same x); projection 0 uses Y, ldy, N,
+  // nblk, Wtab and Vtab above, and entry 0 of these arrays is unused.
+  uint16_t* proj_Y[kMaxProj];
+  int64_t proj_ldy[kMaxProj];
+  const uint64_t* proj_Wtab[kMaxProj];
+  const uint64_t* proj_Vtab[kMaxProj];
+  int32_t proj_N[kMaxProj];
+  int32_t proj_nblk[kMaxProj];
 };
 
 constexpr int kSmallSeg = 16;  // capacity of the small plan (decode batches)
@@ -88,6 +98,7 @@ struct FwdPlanT : FwdHeader {
   float seg_scale[CAP];
   uint8_t seg_rank[CAP];
   uint8_t seg_slot[CAP];
+  uint8_t seg_proj[CAP];  // projection of the segment (0 unless multi-projection)
 };
 using FwdPlan = FwdPlanT<kMaxSeg>;
 

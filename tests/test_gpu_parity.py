@@ -646,3 +646,54 @@ def test_backward_split_is_deterministic():
     ob = oracle_batch(prob)
     _, _, dA_ref, dB_ref = ob.backward()
     assert rel_err(outs[0][0], dA_ref[0]) <= FP32_TOL and rel_err(outs[0][1], dB_ref[0]) <= FP32_TOL
+
+
+# ---------------------------------------------------------------------------
+# Several projections over one x in one launch
+# ---------------------------------------------------------------------------
+MULTI_CASES = [
+    # (T, h_in, outputs, adapters, rank choices, token_rows, host_tables)
+    (256, 2560, (4096, 1024, 1024), 8, (32,), False, True),      # q/k/v-like decode, plan in device tables
+    (256, 2560, (4096, 1024, 1024), 4, (8, 16, 32), True, True),  # small plan: weight addresses in the launch
+    (100, 264, (72, 520), 3, (0, 1, 12, 40, 64), False, False),   # ragged widths, rank 0 in some projections
+    (3000, 1032, (1032, 200, 3080, 8), 6, (8, 16, 24, 128), True, True),  # medium batch, four projections
+    (18000, 264, (200, 264), 5, (8, 16, 32), False, True),        # large batch (one on-chip item per tile)
+]
+
+
+@pytest.mark.parametrize("case", range(len(MULTI_CASES)))
+def test_fused_multi_projection(case):
+    """lora_sgmv_fused_multi: every projection's y matches the oracle of that
+    projection alone (same x and ids, its own adapters)."""
+    import torch
+    L = _L()
+    T, h_in, outs, N, choices, use_rows, host_tables = MULTI_CASES[case]
+    rng = np.random.default_rng(700 + case)
+    ids = rng.integers(-1, N, size=T).astype(np.int32)
+    probs = []
+    for p, h_out in enumerate(outs):
+        ranks = [int(r) for r in rng.choice(choices, size=N)]
+        pr = make_custom(710 + 10 * case + p, h_in, h_out, ranks, scales="random", ids=ids, y0=(p % 2 == 1))
+        if probs:
+            pr = copy.copy(pr)
+            pr.x = probs[0].x  # one x for every projection
+        probs.append(pr)
+    gps = [GpuProblem(pr, use_token_rows=use_rows, host_tables=host_tables) for pr in probs]
+    ys = [g.new_y() for g in gps]
+    ads = [g.adapters for g in gps]
+    ws = L.new_workspace_multi(ads, gps[0].segments)
+    _say(f"multi-projection case {case}: T={T} {h_in}->{outs} N={N} rows={use_rows}")
+    for _ in range(2):  # the second call reuses the workspace (y accumulates twice)
+        L.sgmv_fused_multi(gps[0].x, ads, gps[0].segments, ys, ws)
+    torch.cuda.synchronize()
+    for p, (g, pr, y) in enumerate(zip(gps, probs, ys)):
+        ob = oracle_batch(pr)
+        y_ref, _ = ob.forward()
+        # two calls: y = y0 + 2 * delta
+        y0 = to_f64(g.y_init)
+        y0 = y0[g.perm] if g.use_token_rows else y0
+        ref = y0 + 2.0 * (y_ref - y0)
+        got = g.sorted_rows(y)
+        if T:
+            e = rel_err(got, ref)
+            assert e <= BF16_TOL, f"projection {p}: y rel err {e:.3e}"

@@ -188,3 +188,50 @@ def test_workspace_size_bounds():
     assert sizes[(16, B.OP_BACKWARD)] < sizes[(65536, B.OP_BACKWARD)]
     n = ctypes.c_size_t(0)
     assert lib.lora_workspace_size(7, ctypes.byref(ad), ctypes.byref(sg), ctypes.byref(n)) != 0
+
+
+def test_multi_projection_validation():
+    """lora_sgmv_fused_multi / lora_workspace_size_multi reject malformed
+    requests on the host mirrors before any GPU call."""
+    lib = L.load()
+    a0, k0 = _adapters(ranks=(8, 16), h_in=64, h_out=32)
+    a1, k1 = _adapters(ranks=(4, 0), h_in=64, h_out=48)
+    a_hin, k2 = _adapters(ranks=(8, 16), h_in=72, h_out=32)
+    a_n, k3 = _adapters(ranks=(8, 16, 8), h_in=64, h_out=32)
+    sg, ks = _segments([0, 3, 5], [0, 1])
+
+    def arr(*ads):
+        return (ctypes.POINTER(B.CAdapters) * len(ads))(*[ctypes.pointer(a) for a in ads])
+
+    def call(ads, n=None, ys=None, lds=None, ws=FAKE, wsb=1 << 30):
+        n = len(ads) if n is None else n
+        ys = ys if ys is not None else [FAKE] * len(ads)
+        lds = lds if lds is not None else [32, 48, 32, 32][:len(ads)]
+        yp = (ctypes.c_void_p * len(ys))(*ys)
+        ld = (ctypes.c_int64 * len(lds))(*lds)
+        return lib.lora_sgmv_fused_multi(FAKE, 64, n, ctypes.cast(arr(*ads), ctypes.c_void_p), ctypes.byref(sg),
+                                         ctypes.cast(yp, ctypes.c_void_p), ctypes.cast(ld, ctypes.c_void_p),
+                                         ws, wsb, 0)
+
+    assert call([a0, a1], n=0) == B.LORA_INVALID_ARGUMENT
+    assert call([a0, a1], n=5) == B.LORA_INVALID_ARGUMENT
+    assert call([a0, a_hin]) == B.LORA_INVALID_ARGUMENT
+    assert "same num_adapters and h_in" in lib.lora_last_error().decode()
+    assert call([a0, a_n]) == B.LORA_INVALID_ARGUMENT
+    assert call([a0, a1], ys=[FAKE, 0]) == B.LORA_INVALID_ARGUMENT  # projection 1 has work (adapter 0)
+    assert call([a0, a1], lds=[32, 40]) == B.LORA_INVALID_ARGUMENT  # row stride below h_out 48
+    n = ctypes.c_size_t(0)
+    assert lib.lora_workspace_size_multi(2, ctypes.cast(arr(a0, a1), ctypes.c_void_p), ctypes.byref(sg),
+                                         ctypes.byref(n)) == 0
+    n1 = ctypes.c_size_t(0)
+    assert lib.lora_workspace_size_multi(1, ctypes.cast(arr(a0), ctypes.c_void_p), ctypes.byref(sg),
+                                         ctypes.byref(n1)) == 0
+    assert n.value >= n1.value > 0
+    assert call([a0, a1], wsb=n.value - 1) == B.LORA_WORKSPACE_TOO_SMALL
+    # nothing to do: every segment skipped -> OK without touching the GPU
+    sg_skip, k4 = _segments([0, 3, 5], [-1, -1])
+    yp = (ctypes.c_void_p * 2)(0, 0)
+    ld = (ctypes.c_int64 * 2)(32, 48)
+    assert lib.lora_sgmv_fused_multi(0, 64, 2, ctypes.cast(arr(a0, a1), ctypes.c_void_p), ctypes.byref(sg_skip),
+                                     ctypes.cast(yp, ctypes.c_void_p), ctypes.cast(ld, ctypes.c_void_p),
+                                     0, 0, 0) == B.LORA_OK

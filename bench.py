@@ -477,11 +477,60 @@ def bench_host_call(ds, reps=300):
             "note": "validation + planning + launch, host side, through ctypes"}
 
 
+def bench_multi_projection(reps=200, nsets=16):
+    """q/k/v-shaped decode over one x (Qwen3-4B-like widths: 2560->4096,
+    2560->1024, 2560->1024; 8 adapters of rank 32 per projection; the
+    256-token decode batch): one multi-projection launch against one fused
+    launch per projection, back-to-back calls on rotated inputs."""
+    import torch
+    import lora_adapter_batching_amd as L
+    from workloads import make_c2_projections, make_custom
+    base = make_c2_projections(1)["q"]
+    ids = np.asarray(base.token_ids, np.int32)
+    perm, starts, adap = L.segments_from_ids(ids, base.N)
+    sg = L.Segments(starts, adap)
+    outs = (4096, 1024, 1024)
+    probs = [make_custom(20 + p, base.h_in, h, list(base.ranks), ids=ids) for p, h in enumerate(outs)]
+    sets = []
+    for _ in range(nsets):
+        x = dev_bf16(base.x[perm])
+        ads, ys = [], []
+        for pr in probs:
+            A = [dev_bf16(a) for a in pr.A]
+            B = [dev_bf16(b) for b in pr.B]
+            ads.append(L.Adapters(A, B, pr.ranks, pr.scales, pr.h_in, pr.h_out))
+            ys.append(torch.zeros((pr.T, pr.h_out), dtype=torch.bfloat16, device="cuda"))
+        sets.append((x, ads, ys))
+    wsm = L.new_workspace_multi(sets[0][1], sg)
+    wss = [L.new_workspace(L.OP_FUSED, a, sg) for a in sets[0][1]]
+
+    def multi(i):
+        x, ads, ys = sets[i % nsets]
+        L.sgmv_fused_multi(x, ads, sg, ys, wsm)
+
+    def single(i):
+        x, ads, ys = sets[i % nsets]
+        for a, y, w in zip(ads, ys, wss):
+            L.sgmv_fused(x, a, sg, y, None, w)
+    tm = float(_time_region(multi, reps)[0])
+    ts = float(_time_region(single, reps)[0])
+    # algorithmic bytes: each projection's, with x counted once (it is shared)
+    n_active = len(active_token_ranks(probs[0].ranks, starts, adap))
+    b = sum(fwd_work(pr.h_in, pr.h_out, pr.ranks, starts, adap)[0] for pr in probs)
+    b -= (len(probs) - 1) * 2 * n_active * base.h_in
+    f = sum(fwd_work(pr.h_in, pr.h_out, pr.ranks, starts, adap)[1] for pr in probs)
+    return [_entry("decode_qkv_multi_projection_one_launch_256tok_8x_r32", np.array([tm]), b, f,
+                   {"timing": "back-to-back calls", "three_launches_us": round(ts * 1e6, 2),
+                    "speedup_vs_three_launches": round(ts / tm, 3)})]
+
+
 def bench_secondary(reps=20):
     import torch
     import lora_adapter_batching_amd as L
     from workloads import make_config
     out = [bench_decode_request_order()]
+    torch.cuda.empty_cache()
+    out += bench_multi_projection()
     torch.cuda.empty_cache()
     out += bench_shrink_expand(reps)
     torch.cuda.empty_cache()

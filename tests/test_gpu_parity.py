@@ -697,3 +697,31 @@ def test_fused_multi_projection(case):
         if T:
             e = rel_err(got, ref)
             assert e <= BF16_TOL, f"projection {p}: y rel err {e:.3e}"
+
+
+def test_workspace_sized_once_serves_smaller_batches():
+    """One fused and one backward workspace, sized for the largest batch,
+    serve later batches with fewer tokens and segments and other shapes of
+    work (the layouts of small and medium batches use split hand-offs whose
+    state lives in the workspace)."""
+    import torch
+    L = _L()
+    ranks = [8, 32, 16, 64, 0, 24]
+    big_ids = np.random.default_rng(60).integers(-1, len(ranks), size=3000).astype(np.int32)
+    big = make_custom(61, 1032, 520, ranks, scales="random", ids=big_ids, with_dy=True)
+    gbig = GpuProblem(big)
+    wsf = L.new_workspace(L.OP_FUSED, gbig.adapters, gbig.segments)
+    wsb = L.new_workspace(L.OP_BACKWARD, gbig.adapters, gbig.segments)
+    for k, T in enumerate((3000, 257, 1, 900)):
+        ids = np.random.default_rng(62 + k).integers(-1, len(ranks), size=T).astype(np.int32)
+        prob = make_custom(61, 1032, 520, ranks, scales="random", ids=ids, with_dy=True)
+        gp = GpuProblem(prob, use_token_rows=bool(k % 2))
+        ob = oracle_batch(prob)
+        _say(f"shared workspaces, batch {k}: T={T}")
+        y, u = _run_fused(gp, ws=wsf)
+        _check_forward(gp, ob, y, u)
+        dA, dB, pa, pb = _grad_tables(prob)
+        dx = torch.zeros((T, prob.h_in), dtype=torch.bfloat16, device="cuda")
+        L.packed_backward(gp.x, gp.dy, u, gp.adapters, gp.segments, dx, pa, pb, 0, wsb)
+        torch.cuda.synchronize()
+        _check_backward(gp, ob, dx, dA, dB)

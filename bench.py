@@ -332,10 +332,13 @@ def _time_calls(fn, reps, warm=3):
     return np.array([a.elapsed_time(b) for a, b in ts]) * 1e-3
 
 
-def _time_region(fn, reps, warm=8):
+def _time_region(fn, reps, warm=64):
     """Mean seconds per call of `reps` back-to-back calls between one pair of
     HIP events. For launches shorter than the host's submission time a pair
-    of events around each call would time the host, not the kernel."""
+    of events around each call would time the host, not the kernel. The
+    warm-up is long because the first few hundred launches of a fresh process
+    can include one multi-millisecond stall of the runtime (seen once, about
+    40 ms, between kernels of normal duration in a kernel trace)."""
     import torch
     for i in range(warm):
         fn(i)

@@ -353,12 +353,16 @@ def _time_region(fn, reps, warm=64):
 
 
 def _entry(name, seconds, bytes_, flops, extra=None):
+    seconds = np.asarray(seconds, np.float64)
     med = float(np.median(seconds))
     gbs = bytes_ / med / 1e9
     tfl = flops / med / 1e12
     d = {"workload": name, "us": round(med * 1e6, 2), "GB/s": round(gbs, 1),
          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "TFLOP/s": round(tfl, 2),
          "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 5), "bytes": int(bytes_), "flops": int(flops)}
+    if seconds.size > 1:  # per-call samples: their spread too
+        d["p10_us"] = round(float(np.percentile(seconds, 10)) * 1e6, 2)
+        d["p90_us"] = round(float(np.percentile(seconds, 90)) * 1e6, 2)
     if extra:
         d.update(extra)
     return d

@@ -122,12 +122,23 @@ typedef struct lora_segments_t {
   const int32_t* seg_starts;  /* HOST [S+1]: [0] = 0, non-decreasing, [S] = T */
   const int32_t* seg_adapter; /* HOST [S]: -1 (no adapter) or 0..N-1 */
   const int32_t* token_rows;  /* DEVICE [T] or NULL: row of x/y/dx/dy used by position p.
-                                 Rows must be distinct for the writing calls, and
-                                 row * ld * 2 bytes must stay below 2 GiB (rows past
-                                 that read as zero and are not written). */
+                                 Rows must be distinct for the writing calls. With a
+                                 table, every matrix the call touches is addressed
+                                 through one 2 GiB - 16 byte window from its base:
+                                 the call is refused (LORA_INVALID_ARGUMENT) when
+                                 T rows of its stride cannot fit in the window, and
+                                 a row that is negative or does not lie wholly
+                                 inside it is treated as absent (it reads as zero
+                                 and is never written; the offset is computed in
+                                 64 bits, so it cannot wrap onto another row). */
 } lora_segments_t;
 
 /*
+ * Token bookkeeping for a mixed-adapter batch. A decode batch arrives with
+ * the tokens of many tenants' adapters interleaved in request order
+ * ("Trajectory presenta C-LoRA" (vivodigitale.it), "Come funziona
+ * l'architettura": one batch mixes tokens of different adapters); the
+ * segmented kernels want each adapter's tokens as one contiguous run.
  * Groups request-order adapter ids into segments (HOST only, no GPU):
  * segment a (0 <= a < N) holds the tokens with id a in request order, and a
  * final segment N holds the tokens with id -1. perm[p] is the request index
@@ -140,8 +151,14 @@ int lora_segments_from_ids(const int32_t* ids, int32_t num_tokens, int32_t num_a
                            int32_t* perm, int32_t* seg_starts, int32_t* seg_adapter);
 
 /*
- * Bytes of device workspace needed by `op` (LORA_OP_*) for these adapters
- * and this batch. The value depends only on T, S, N, h_in, h_out and the
+ * Device scratch of the one-launch calls: the cross-workgroup hand-off of a
+ * shrink that is split along h_in before the expand of the same launch
+ * ("Trajectory presenta C-LoRA" (vivodigitale.it), "Come funziona
+ * l'architettura": the per-adapter work of a decode step runs as one launch),
+ * and for the backward the du / transposed-weight buffers of the packed
+ * kernels ("Technische Samenvatting: PLoRA" (gist.science), "Packed LoRA
+ * Kernels"). Bytes of device workspace needed by `op` (LORA_OP_*) for these
+ * adapters and this batch. The value depends only on T, S, N, h_in, h_out and the
  * largest rank in `adapters`, so one workspace serves every later batch with
  * no more tokens and segments.
  */
@@ -149,17 +166,27 @@ int lora_workspace_size(int op, const lora_adapters_t* adapters, const lora_segm
                         size_t* bytes);
 
 /*
- * Shrink: u[p][k] = sum_d A_i[k][d] x[row(p)][d] for k < r_i (fp32), for every
+ * Shrink, the first of the two products of a LoRA-wrapped projection (the
+ * low-rank factor A_i of the adapter, "Trajectory presenta C-LoRA"
+ * (vivodigitale.it), "Cos'e C-LoRA e perche serve"), for all adapters of the
+ * batch in one launch, tiled along tokens and h_in rather than the rank
+ * ("Technische Samenvatting: PLoRA" (gist.science), "Kernelontwerp"):
+ * u[p][k] = sum_d A_i[k][d] x[row(p)][d] for k < r_i (fp32), for every
  * position p of an active segment. Columns k >= r_i of u are not written.
  * x: DEVICE bf16 [*, ldx]; u: DEVICE fp32 [T, ldu], ldu >= max rank used.
+ * Errors as for every call; ws may be NULL when lora_workspace_size() gives 0.
  */
 int lora_sgmv_shrink(const void* x, int64_t ldx, const lora_adapters_t* adapters,
                      const lora_segments_t* segments, float* u, int64_t ldu, void* ws,
                      size_t ws_bytes, void* stream);
 
 /*
- * Expand: y[row(p)][j] += s_i sum_k B_i[j][k] u[p][k] for j < h_out,
- * rounded to bf16. u: DEVICE fp32 [T, ldu]; y: DEVICE bf16 [*, ldy].
+ * Expand, the second product (the factor B_i back to h_out, scaled by the
+ * adapter's scaling factor: "Technische Samenvatting: PLoRA" (gist.science),
+ * "Resultaten", rank and scaling factor per adapter), for all adapters of
+ * the batch in one launch, tiled along tokens and h_out ("Kernelontwerp"):
+ * y[row(p)][j] += s_i sum_k B_i[j][k] u[p][k] for j < h_out, rounded to bf16.
+ * u: DEVICE fp32 [T, ldu]; y: DEVICE bf16 [*, ldy]. Needs no workspace.
  */
 int lora_sgmv_expand(const float* u, int64_t ldu, const lora_adapters_t* adapters,
                      const lora_segments_t* segments, void* y, int64_t ldy, void* ws,
@@ -188,7 +215,9 @@ int lora_sgmv_fused(const void* x, int64_t ldx, const lora_adapters_t* adapters,
  * same num_adapters and h_in (the segments' adapter ids index all of them),
  * its own h_out, ranks, scales and weight tables. y[p] / ldy[p]: HOST arrays
  * of num_proj DEVICE output addresses and row strides (bf16 [*, h_out_p]);
- * the outputs must not overlap each other or x. 1 <= num_proj <= 4. No u is
+ * the outputs must not overlap each other or x (an output that starts at x,
+ * or two that start at the same address, are refused with
+ * LORA_INVALID_ARGUMENT). 1 <= num_proj <= 4. No u is
  * saved. The workspace is sized by lora_workspace_size_multi() and follows
  * the rules of the other calls. Errors as for lora_sgmv_fused().
  */

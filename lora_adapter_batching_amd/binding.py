@@ -267,6 +267,12 @@ def new_workspace_multi(adapters: Sequence[Adapters], segments: Segments, device
 def sgmv_fused_multi(x, adapters: Sequence[Adapters], segments: Segments, ys: Sequence, ws=None, stream=None):
     """One launch for several projections over the same x: ys[p] +=
     s B_p,i (A_p,i x) with projection p's adapters."""
+    import torch
+    if len(ys) != len(adapters):
+        raise ValueError(f"sgmv_fused_multi: {len(adapters)} adapter sets but {len(ys)} outputs")
+    for p, y in enumerate(ys):
+        if y.dtype != torch.bfloat16 or y.dim() != 2 or y.stride(1) != 1:
+            raise ValueError(f"sgmv_fused_multi: ys[{p}] must be a 2-D bfloat16 tensor with unit column stride")
     lib = load()
     wp, wb = _ws(ws)
     arr = _multi_tables(adapters)
@@ -275,6 +281,51 @@ def sgmv_fused_multi(x, adapters: Sequence[Adapters], segments: Segments, ys: Se
     _check(lib.lora_sgmv_fused_multi(_ptr(x), x.stride(0), len(adapters), ctypes.cast(arr, ctypes.c_void_p),
                                      segments.c, ctypes.cast(yp, ctypes.c_void_p),
                                      ctypes.cast(ld, ctypes.c_void_p), wp, wb, _stream_handle(stream)))
+
+
+class CPlanItem(ctypes.Structure):
+    """lora_plan_item_t of the internal inspection entry (csrc/lora_inspect.h)."""
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("launch", "phase", "block", "grid", "mode", "kind", "tile", "adapter", "proj", "rank",
+                 "tok0", "ntok", "lo", "hi", "part", "aux")]
+
+
+INSPECT_WITH_U, INSPECT_WITH_DX, INSPECT_ACCUMULATE = 1, 2, 4
+PHASE_FWD, PHASE_WGRAD, PHASE_REDUCE, PHASE_TRANSPOSE = 0, 1, 2, 3
+
+
+def inspect_plan(op: int, adapters, segments: Segments, options: int = 0, cus: int = 256, xccs: int = 8):
+    """Host-only listing of every workgroup the call `op` would launch
+    (no GPU involved). adapters: one Adapters-like object, or a sequence of
+    them for a multi-projection fused call. Returns (items, ranges): a numpy
+    structured array with the lora_plan_item_t fields, and an int32 [n, 2]
+    array of (first position, count) token ranges of weight-gradient jobs."""
+    lib = load()
+    fn = lib.lora_inspect_plan
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(CSegments), ctypes.c_uint32,
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.POINTER(ctypes.c_int64)]
+    ads = list(adapters) if isinstance(adapters, (list, tuple)) else [adapters]
+    arr = _multi_tables(ads)
+    n_items = ctypes.c_int64(0)
+    n_ranges = ctypes.c_int64(0)
+    cap, rcap = 1 << 14, 1 << 12
+    while True:
+        items = (CPlanItem * cap)()
+        ranges = (ctypes.c_int32 * (2 * rcap))()
+        _check(fn(op, len(ads), ctypes.cast(arr, ctypes.c_void_p), segments.c, options, cus, xccs,
+                  ctypes.cast(items, ctypes.c_void_p), cap, ctypes.byref(n_items),
+                  ctypes.cast(ranges, ctypes.c_void_p), rcap, ctypes.byref(n_ranges)))
+        if n_items.value <= cap and n_ranges.value <= rcap:
+            break
+        cap = max(cap, int(n_items.value))
+        rcap = max(rcap, int(n_ranges.value))
+    dt = np.dtype([(f, np.int32) for f, _ in CPlanItem._fields_])
+    out = np.frombuffer(bytes(items), dtype=dt, count=int(n_items.value)).copy()
+    rg = np.frombuffer(bytes(ranges), dtype=np.int32, count=2 * int(n_ranges.value)).reshape(-1, 2).copy()
+    return out, rg
 
 
 def version() -> int:

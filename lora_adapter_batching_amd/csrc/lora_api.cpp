@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "../../include/lora_sgmv.h"
+#include "lora_inspect.h"
 #include "lora_plan.h"
 
 namespace lora {
@@ -81,6 +82,30 @@ DeviceInfo device_info() {
   }
   return cache[dev];
 }
+
+// Where the launches of a call go: the HIP stream, or (for the host-only
+// plan inspection entry) a recorder that keeps the plans and launches
+// nothing. Every planning decision is taken by the same code either way.
+struct Launcher {
+  virtual ~Launcher() = default;
+  virtual DeviceInfo dev() = 0;
+  virtual hipError_t fwd(const FwdPlan& P, int rbmax, const uint64_t* wptr, const uint64_t* vptr) = 0;
+  virtual hipError_t transpose(const TransposePlan& P) = 0;
+  virtual hipError_t wgrad(const WgradPlan& P, int grid) = 0;
+  virtual hipError_t reduce(const WgradReducePlan& R) = 0;
+};
+
+struct HipLauncher final : Launcher {
+  hipStream_t stream;
+  explicit HipLauncher(void* s) : stream(static_cast<hipStream_t>(s)) {}
+  DeviceInfo dev() override { return device_info(); }
+  hipError_t fwd(const FwdPlan& P, int rbmax, const uint64_t* wptr, const uint64_t* vptr) override {
+    return launch_fwd(P, rbmax, stream, wptr, vptr);
+  }
+  hipError_t transpose(const TransposePlan& P) override { return launch_transpose(P, stream); }
+  hipError_t wgrad(const WgradPlan& P, int grid) override { return launch_wgrad(P, grid, stream); }
+  hipError_t reduce(const WgradReducePlan& R) override { return launch_wgrad_reduce(R, stream); }
+};
 
 int round_up(int a, int b) { return (a + b - 1) / b * b; }
 // Row length of a split-K partial tile: the kernels write 32 * RB rows with
@@ -161,6 +186,21 @@ int check_rows(const void* p, int64_t ld, int width, const char* name, bool need
                               (long long)ld, width);
   if (ld & 7) return fail(LORA_INVALID_ARGUMENT, "row stride of %s (%lld) is not a multiple of 8", name,
                           (long long)ld);
+  return LORA_OK;
+}
+
+// With a token-row table the kernels address a whole matrix from its base
+// through one buffer resource of kGatherSpan bytes. The rows of a batch are
+// distinct, so its largest row is at least T - 1: a batch whose T rows cannot
+// fit in that span is refused here (a row past the span would be read as
+// zero and not written).
+int check_gather(const lora_segments_t* s, int64_t ld, int width, const char* name, bool needed) {
+  if (!needed || !s->token_rows || s->num_tokens == 0) return LORA_OK;
+  const int64_t span = ((int64_t)(s->num_tokens - 1) * ld + width) * 2;
+  if (span > kGatherSpan)
+    return fail(LORA_INVALID_ARGUMENT,
+                "%s: with token_rows, %d rows of stride %lld span %lld bytes, above the %lld-byte gather limit",
+                name, s->num_tokens, (long long)ld, (long long)span, (long long)kGatherSpan);
   return LORA_OK;
 }
 
@@ -252,14 +292,44 @@ WsLayout ws_layout(int op, const lora_adapters_t* a, const lora_segments_t* s) {
 // ---------------------------------------------------------------------------
 // Planner: forward-style launches
 // ---------------------------------------------------------------------------
-// Orders segments so that heavy work is dispatched first (longest first),
-// which lets the in-order workgroup dispatcher balance ranks and lengths.
-void order_by_cost(std::vector<ActiveSeg>& v, int K, int N) {
-  std::stable_sort(v.begin(), v.end(), [&](const ActiveSeg& x, const ActiveSeg& y) {
-    const double cx = (double)cdiv(x.ntok, kTileM) * (2.0 * K + 4.0 * N + 2.0 * x.rank * (K + N) / 8.0);
-    const double cy = (double)cdiv(y.ntok, kTileM) * (2.0 * K + 4.0 * N + 2.0 * y.rank * (K + N) / 8.0);
-    return cx > cy;
-  });
+// Orders segments so that heavy work items are dispatched first. Workgroups
+// are handed out in launch order to whichever CU frees up first, so the
+// order is a longest-processing-time-first list schedule when it runs by
+// the cost of one ITEM (a 32-token tile's share of x or y plus its adapter's
+// weights, larger for larger ranks), not by a segment's total: a long
+// segment of a small-rank adapter must not hold back a short one of a
+// large rank. With room in the plan, the ragged last tile of a segment
+// becomes an entry of its own, so that these lighter items go to the end
+// of the order too.
+void order_by_cost(std::vector<ActiveSeg>& v, int K, int N, bool split_ragged) {
+  if (split_ragged) {
+    size_t extra = 0;
+    for (const auto& s : v) extra += (s.ntok > kTileM && s.ntok % kTileM) ? 1 : 0;
+    if (v.size() + extra <= (size_t)kMaxSeg) {
+      std::vector<ActiveSeg> w;
+      w.reserve(v.size() + extra);
+      for (const auto& s : v) {
+        const int full = s.ntok / kTileM * kTileM;
+        if (s.ntok > kTileM && full < s.ntok) {
+          ActiveSeg a = s, b = s;
+          a.ntok = full;
+          b.tok0 = s.tok0 + full;
+          b.ntok = s.ntok - full;
+          w.push_back(a);
+          w.push_back(b);
+        } else {
+          w.push_back(s);
+        }
+      }
+      v.swap(w);
+    }
+  }
+  auto item_cost = [&](const ActiveSeg& s) {
+    const double rows = std::min(s.ntok, kTileM);
+    return rows * (2.0 * K + 4.0 * N) + 2.0 * s.rank * (double)(K + N);
+  };
+  std::stable_sort(v.begin(), v.end(),
+                   [&](const ActiveSeg& x, const ActiveSeg& y) { return item_cost(x) > item_cost(y); });
 }
 
 struct FwdCall {
@@ -359,11 +429,15 @@ int local_grid(int tiles, int ks, int nc) {
 }
 
 int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int>& slot_of,
-            hipStream_t stream) {
+            Launcher& launcher) {
   if (segs.empty()) return LORA_OK;
-  const DeviceInfo dev = device_info();
+  const DeviceInfo dev = launcher.dev();
   const int cus = dev.cus;
-  order_by_cost(segs, c.K, c.N);
+  {
+    int tiles_all = 0;
+    for (const auto& sg : segs) tiles_all += cdiv(sg.ntok, kTileM);
+    order_by_cost(segs, c.K, c.N, 4 * tiles_all > dev.cus);
+  }
   // split into launches of at most kMaxSeg segments
   for (size_t base = 0; base < segs.size(); base += kMaxSeg) {
     const int ns = (int)std::min<size_t>(kMaxSeg, segs.size() - base);
@@ -548,8 +622,7 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
       }
       P.ptrs_in_plan = 1;
     }
-    const hipError_t e = P.ptrs_in_plan ? launch_fwd(P, rbmax, stream, wq, vq)
-                                        : launch_fwd(P, rbmax, stream, nullptr, nullptr);
+    const hipError_t e = P.ptrs_in_plan ? launcher.fwd(P, rbmax, wq, vq) : launcher.fwd(P, rbmax, nullptr, nullptr);
     if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
   }
   return LORA_OK;
@@ -631,15 +704,15 @@ static int common_checks(const lora_adapters_t* adapters, const lora_segments_t*
   return check_segments(segments, adapters->num_adapters);
 }
 
-int lora_sgmv_shrink(const void* x, int64_t ldx, const lora_adapters_t* adapters,
-                     const lora_segments_t* segments, float* u, int64_t ldu, void* ws,
-                     size_t ws_bytes, void* stream) {
-  g_last_error.clear();
+static int sgmv_shrink_impl(const void* x, int64_t ldx, const lora_adapters_t* adapters,
+                            const lora_segments_t* segments, float* u, int64_t ldu, void* ws,
+                            size_t ws_bytes, Launcher& launcher) {
   int st = common_checks(adapters, segments);
   if (st) return st;
   const auto segs = active_segments(adapters, segments);
   if (segs.empty()) return LORA_OK;
   if ((st = check_rows(x, ldx, adapters->h_in, "x", true))) return st;
+  if ((st = check_gather(segments, ldx, adapters->h_in, "x", true))) return st;
   if ((st = check_u(u, ldu, max_rank_used(segs), "u"))) return st;
   if (!adapters->A_ptrs) return fail(LORA_INVALID_ARGUMENT, "A_ptrs is NULL");
   const WsLayout L = ws_layout(LORA_OP_SHRINK, adapters, segments);
@@ -655,22 +728,19 @@ int lora_sgmv_shrink(const void* x, int64_t ldx, const lora_adapters_t* adapters
   c.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
   c.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.counters);
   c.rmax = max_rank_all(adapters);
-  return run_fwd(c, segs, {}, static_cast<hipStream_t>(stream));
+  return run_fwd(c, segs, {}, launcher);
 }
 
-int lora_sgmv_expand(const float* u, int64_t ldu, const lora_adapters_t* adapters,
-                     const lora_segments_t* segments, void* y, int64_t ldy, void* ws,
-                     size_t ws_bytes, void* stream) {
-  g_last_error.clear();
+static int sgmv_expand_impl(const float* u, int64_t ldu, const lora_adapters_t* adapters,
+                            const lora_segments_t* segments, void* y, int64_t ldy, Launcher& launcher) {
   int st = common_checks(adapters, segments);
   if (st) return st;
   const auto segs = active_segments(adapters, segments);
   if (segs.empty()) return LORA_OK;
   if ((st = check_rows(y, ldy, adapters->h_out, "y", true))) return st;
+  if ((st = check_gather(segments, ldy, adapters->h_out, "y", true))) return st;
   if ((st = check_u(u, ldu, max_rank_used(segs), "u"))) return st;
   if (!adapters->B_ptrs) return fail(LORA_INVALID_ARGUMENT, "B_ptrs is NULL");
-  (void)ws;
-  (void)ws_bytes;
   FwdCall c{};
   c.mode_op = LORA_OP_EXPAND;
   c.Y = static_cast<uint16_t*>(y); c.ldy = ldy;
@@ -680,19 +750,20 @@ int lora_sgmv_expand(const float* u, int64_t ldu, const lora_adapters_t* adapter
   c.K = adapters->h_in; c.N = adapters->h_out;
   c.token_rows = segments->token_rows;
   c.rmax = max_rank_all(adapters);
-  return run_fwd(c, segs, {}, static_cast<hipStream_t>(stream));
+  return run_fwd(c, segs, {}, launcher);
 }
 
-int lora_sgmv_fused(const void* x, int64_t ldx, const lora_adapters_t* adapters,
-                    const lora_segments_t* segments, void* y, int64_t ldy, float* u_save,
-                    int64_t ldu, void* ws, size_t ws_bytes, void* stream) {
-  g_last_error.clear();
+static int sgmv_fused_impl(const void* x, int64_t ldx, const lora_adapters_t* adapters,
+                           const lora_segments_t* segments, void* y, int64_t ldy, float* u_save,
+                           int64_t ldu, void* ws, size_t ws_bytes, Launcher& launcher) {
   int st = common_checks(adapters, segments);
   if (st) return st;
   const auto segs = active_segments(adapters, segments);
   if (segs.empty()) return LORA_OK;
   if ((st = check_rows(x, ldx, adapters->h_in, "x", true))) return st;
   if ((st = check_rows(y, ldy, adapters->h_out, "y", true))) return st;
+  if ((st = check_gather(segments, ldx, adapters->h_in, "x", true))) return st;
+  if ((st = check_gather(segments, ldy, adapters->h_out, "y", true))) return st;
   if (u_save && (st = check_u(u_save, ldu, max_rank_used(segs), "u_save"))) return st;
   if (!adapters->A_ptrs || !adapters->B_ptrs) return fail(LORA_INVALID_ARGUMENT, "A_ptrs/B_ptrs is NULL");
   const WsLayout L = ws_layout(LORA_OP_FUSED, adapters, segments);
@@ -712,7 +783,33 @@ int lora_sgmv_fused(const void* x, int64_t ldx, const lora_adapters_t* adapters,
   c.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
   c.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.counters);
   c.rmax = max_rank_all(adapters);
-  return run_fwd(c, segs, {}, static_cast<hipStream_t>(stream));
+  return run_fwd(c, segs, {}, launcher);
+}
+
+int lora_sgmv_shrink(const void* x, int64_t ldx, const lora_adapters_t* adapters,
+                     const lora_segments_t* segments, float* u, int64_t ldu, void* ws,
+                     size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  HipLauncher launcher(stream);
+  return sgmv_shrink_impl(x, ldx, adapters, segments, u, ldu, ws, ws_bytes, launcher);
+}
+
+int lora_sgmv_expand(const float* u, int64_t ldu, const lora_adapters_t* adapters,
+                     const lora_segments_t* segments, void* y, int64_t ldy, void* ws,
+                     size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  (void)ws;
+  (void)ws_bytes;
+  HipLauncher launcher(stream);
+  return sgmv_expand_impl(u, ldu, adapters, segments, y, ldy, launcher);
+}
+
+int lora_sgmv_fused(const void* x, int64_t ldx, const lora_adapters_t* adapters,
+                    const lora_segments_t* segments, void* y, int64_t ldy, float* u_save,
+                    int64_t ldu, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  HipLauncher launcher(stream);
+  return sgmv_fused_impl(x, ldx, adapters, segments, y, ldy, u_save, ldu, ws, ws_bytes, launcher);
 }
 
 // ---------------------------------------------------------------------------
@@ -757,10 +854,10 @@ int lora_workspace_size_multi(int32_t num_proj, const lora_adapters_t* const* ad
   return LORA_OK;
 }
 
-int lora_sgmv_fused_multi(const void* x, int64_t ldx, int32_t num_proj,
-                          const lora_adapters_t* const* adapters, const lora_segments_t* segments,
-                          void* const* y, const int64_t* ldy, void* ws, size_t ws_bytes, void* stream) {
-  g_last_error.clear();
+static int sgmv_fused_multi_impl(const void* x, int64_t ldx, int32_t num_proj,
+                                 const lora_adapters_t* const* adapters, const lora_segments_t* segments,
+                                 void* const* y, const int64_t* ldy, void* ws, size_t ws_bytes,
+                                 Launcher& launcher) {
   int rmax = 0;
   int st = multi_checks(num_proj, adapters, segments, &rmax);
   if (st) return st;
@@ -772,6 +869,7 @@ int lora_sgmv_fused_multi(const void* x, int64_t ldx, int32_t num_proj,
     char name[16];
     std::snprintf(name, sizeof(name), "y[%d]", p);
     if ((st = check_rows(y[p], ldy[p], adapters[p]->h_out, name, true))) return st;
+    if ((st = check_gather(segments, ldy[p], adapters[p]->h_out, name, true))) return st;
     if (!adapters[p]->A_ptrs || !adapters[p]->B_ptrs)
       return fail(LORA_INVALID_ARGUMENT, "adapters[%d]: A_ptrs/B_ptrs is NULL", p);
     for (auto& a : v) a.proj = p;
@@ -779,6 +877,13 @@ int lora_sgmv_fused_multi(const void* x, int64_t ldx, int32_t num_proj,
   }
   if (segs.empty()) return LORA_OK;
   if ((st = check_rows(x, ldx, adapters[0]->h_in, "x", true))) return st;
+  if ((st = check_gather(segments, ldx, adapters[0]->h_in, "x", true))) return st;
+  // every output is written: no two may share a base address, and none may be x
+  for (int p = 0; p < num_proj; ++p) {
+    if (y[p] == x) return fail(LORA_INVALID_ARGUMENT, "y[%d] is x: outputs must not overlap x", p);
+    for (int q = 0; q < p; ++q)
+      if (y[p] == y[q]) return fail(LORA_INVALID_ARGUMENT, "y[%d] and y[%d] are the same buffer", q, p);
+  }
   if ((st = check_ws(ws, ws_bytes, multi_ws_bytes(num_proj, rmax, segments)))) return st;
   FwdCall c{};
   c.mode_op = LORA_OP_FUSED;
@@ -805,15 +910,22 @@ int lora_sgmv_fused_multi(const void* x, int64_t ldx, int32_t num_proj,
   c.counters = reinterpret_cast<int32_t*>(ws);
   c.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + part_off);
   c.rmax = rmax;
-  return run_fwd(c, segs, {}, static_cast<hipStream_t>(stream));
+  return run_fwd(c, segs, {}, launcher);
 }
 
-int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t lddy, const float* u,
-                         int64_t ldu, const lora_adapters_t* adapters,
-                         const lora_segments_t* segments, void* dx, int64_t lddx,
-                         const uint64_t* dA_ptrs, const uint64_t* dB_ptrs, uint32_t flags,
-                         void* ws, size_t ws_bytes, void* stream) {
+int lora_sgmv_fused_multi(const void* x, int64_t ldx, int32_t num_proj,
+                          const lora_adapters_t* const* adapters, const lora_segments_t* segments,
+                          void* const* y, const int64_t* ldy, void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
+  HipLauncher launcher(stream);
+  return sgmv_fused_multi_impl(x, ldx, num_proj, adapters, segments, y, ldy, ws, ws_bytes, launcher);
+}
+
+static int packed_backward_impl(const void* x, int64_t ldx, const void* dy, int64_t lddy, const float* u,
+                                int64_t ldu, const lora_adapters_t* adapters,
+                                const lora_segments_t* segments, void* dx, int64_t lddx,
+                                const uint64_t* dA_ptrs, const uint64_t* dB_ptrs, uint32_t flags,
+                                void* ws, size_t ws_bytes, Launcher& launcher) {
   int st = common_checks(adapters, segments);
   if (st) return st;
   if (flags & ~LORA_GRAD_ACCUMULATE) return fail(LORA_INVALID_ARGUMENT, "unknown flags 0x%x", flags);
@@ -833,13 +945,15 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
     if ((st = check_rows(x, ldx, adapters->h_in, "x", true))) return st;
     if ((st = check_rows(dy, lddy, adapters->h_out, "dy", true))) return st;
     if ((st = check_rows(dx, lddx, adapters->h_in, "dx", dx != nullptr))) return st;
+    if ((st = check_gather(segments, ldx, adapters->h_in, "x", true))) return st;
+    if ((st = check_gather(segments, lddy, adapters->h_out, "dy", true))) return st;
+    if ((st = check_gather(segments, lddx, adapters->h_in, "dx", dx != nullptr))) return st;
     if (u && (st = check_u(u, ldu, max_rank_used(segs), "u"))) return st;
     if (!adapters->A_ptrs || !adapters->B_ptrs) return fail(LORA_INVALID_ARGUMENT, "A_ptrs/B_ptrs is NULL");
   }
   const WsLayout L = ws_layout(LORA_OP_BACKWARD, adapters, segments);
   if ((st = check_ws(ws, ws_bytes, L.total))) return st;
 
-  hipStream_t strm = static_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(ws);
   float* partials = reinterpret_cast<float*>(wsb + L.partials);
   int32_t* counters = reinterpret_cast<int32_t*>(wsb + L.counters);
@@ -859,7 +973,7 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
     c.K = adapters->h_in; c.N = adapters->h_out;
     c.token_rows = segments->token_rows;
     c.partials = partials; c.counters = counters; c.rmax = rmax;
-    if ((st = run_fwd(c, segs, {}, strm))) return st;
+    if ((st = run_fwd(c, segs, {}, launcher))) return st;
     Uuse = c.U;
     lduse = L.lddu;
   }
@@ -896,7 +1010,7 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
     T.tiles_b = cdiv(adapters->h_out, 64) * T.tb_cols;
     T.ta_cols = cdiv(adapters->h_in, 64);
     T.tiles_a = cdiv(round_up(grmax, 8), 64) * T.ta_cols;
-    hipError_t e = launch_transpose(T, strm);
+    hipError_t e = launcher.transpose(T);
     if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "transpose launch failed: %s", hipGetErrorString(e));
 
     std::vector<ActiveSeg> gsegs;
@@ -914,7 +1028,7 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
     c.K = adapters->h_out; c.N = adapters->h_in;
     c.token_rows = segments->token_rows;
     c.partials = partials; c.counters = counters; c.rmax = rmax;
-    if ((st = run_fwd(c, gsegs, slot_of, strm))) return st;
+    if ((st = run_fwd(c, gsegs, slot_of, launcher))) return st;
   }
 
   // weight gradients: one job per adapter (several chained jobs if it has
@@ -940,7 +1054,7 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
   // unsplit adapter as long as before only adds traffic).
   std::vector<int> nparts(N, 1);
   {
-    const int slots_gpu = 2 * device_info().cus;
+    const int slots_gpu = 2 * launcher.dev().cus;
     int64_t items = 0;
     std::vector<int> steps(N, 0), it(N, 0);
     for (int a = 0; a < N; ++a) {
@@ -1075,7 +1189,7 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
     if (nj == 0) return fail(LORA_DEVICE_ERROR, "internal planner error (no weight-gradient job placed)");
     W.n_jobs = nj;
     W.job_item0[nj] = grid;
-    const hipError_t e = launch_wgrad(W, grid, strm);
+    const hipError_t e = launcher.wgrad(W, grid);
     if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "weight-gradient launch failed: %s", hipGetErrorString(e));
   }
   if (!reds.empty()) {
@@ -1097,10 +1211,190 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
       grid += (int)cdiv64((int64_t)(adapters->h_in + adapters->h_out) * R.red_rank[j], kReduceElems);
     }
     R.red_item0[R.n_red] = grid;
-    const hipError_t e = launch_wgrad_reduce(R, strm);
+    const hipError_t e = launcher.reduce(R);
     if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "weight-gradient reduce launch failed: %s", hipGetErrorString(e));
   }
   return LORA_OK;
+}
+
+int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t lddy, const float* u,
+                         int64_t ldu, const lora_adapters_t* adapters,
+                         const lora_segments_t* segments, void* dx, int64_t lddx,
+                         const uint64_t* dA_ptrs, const uint64_t* dB_ptrs, uint32_t flags,
+                         void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  HipLauncher launcher(stream);
+  return packed_backward_impl(x, ldx, dy, lddy, u, ldu, adapters, segments, dx, lddx, dA_ptrs, dB_ptrs, flags,
+                              ws, ws_bytes, launcher);
+}
+
+// ---------------------------------------------------------------------------
+// Host-only plan inspection (lora_inspect.h)
+// ---------------------------------------------------------------------------
+namespace {
+
+// Lists the workgroups of every launch instead of launching anything.
+struct Recorder final : Launcher {
+  DeviceInfo d;
+  lora_plan_item_t* items;
+  int64_t cap, n = 0;
+  int32_t* ranges;
+  int64_t rcap, nr = 0;
+  int launches = 0;
+  void put(const lora_plan_item_t& r) {
+    if (n < cap) items[n] = r;
+    ++n;
+  }
+  DeviceInfo dev() override { return d; }
+  hipError_t fwd(const FwdPlan& P, int rbmax, const uint64_t*, const uint64_t*) override {
+    (void)rbmax;
+    const int launch = launches++;
+    for (int b = 0; b < P.grid; ++b) {
+      lora_plan_item_t r{};
+      r.launch = launch; r.phase = LORA_PHASE_FWD; r.block = b; r.grid = P.grid; r.mode = P.mode;
+      r.part = P.ks; r.aux = P.nc;
+      const FwdItem it = fwd_item(P, b);
+      if (it.g < 0 || it.g >= P.n_tiles) {
+        r.kind = -1; r.tile = -1; r.adapter = -1;
+        put(r);
+        continue;
+      }
+      int sel = 0;
+      for (int i = 1; i < P.n_seg; ++i)
+        if (it.g >= P.seg_tile0[i]) sel = i;
+      const int tt = it.g - P.seg_tile0[sel];
+      r.kind = it.kind; r.tile = it.g;
+      r.adapter = P.seg_adapter[sel]; r.proj = P.seg_proj[sel]; r.rank = P.seg_rank[sel];
+      r.tok0 = P.seg_tok0[sel] + tt * kTileM;
+      r.ntok = std::min(kTileM, P.seg_ntok[sel] - tt * kTileM);
+      if (it.kind == kItemShrink) {
+        shrink_range(P.K, P.kchunk, it.c, r.lo, r.hi);
+      } else {
+        const int p = r.proj;
+        expand_cols(p == 0 ? P.N : P.proj_N[p], p == 0 ? P.nblk : P.proj_nblk[p], it.c, r.lo, r.hi);
+      }
+      put(r);
+    }
+    return hipSuccess;
+  }
+  hipError_t transpose(const TransposePlan& P) override {
+    const int launch = launches++;
+    for (int k = 0; k < P.n_slots; ++k) {
+      lora_plan_item_t r{};
+      r.launch = launch; r.phase = LORA_PHASE_TRANSPOSE; r.block = -1;
+      r.grid = P.n_slots * (P.tiles_b + P.tiles_a); r.kind = 0; r.tile = k;
+      r.adapter = P.slot_adapter[k]; r.rank = P.slot_rank[k];
+      put(r);
+    }
+    return hipSuccess;
+  }
+  hipError_t wgrad(const WgradPlan& P, int grid) override {
+    const int launch = launches++;
+    std::vector<int64_t> first(P.n_jobs);
+    for (int j = 0; j < P.n_jobs; ++j) {
+      first[j] = nr;
+      for (int q = 0; q < P.job_nseg[j]; ++q) {
+        if (nr < rcap) {
+          ranges[2 * nr] = P.seg_tok0[P.job_seg0[j] + q];
+          ranges[2 * nr + 1] = P.seg_ntok[P.job_seg0[j] + q];
+        }
+        ++nr;
+      }
+    }
+    for (int b = 0; b < grid; ++b) {
+      int j = 0;
+      while (j + 1 < P.n_jobs && b >= P.job_item0[j + 1]) ++j;
+      const int rank = P.job_rank[j];
+      const int cw = wgrad_cw(rank);
+      const int nb_db = cdiv(P.h_out, cw);
+      const int local = b - P.job_item0[j];
+      lora_plan_item_t r{};
+      r.launch = launch; r.phase = LORA_PHASE_WGRAD; r.block = b; r.grid = grid;
+      r.kind = local < nb_db ? 0 : 1;
+      r.tile = j; r.adapter = P.job_adapter[j]; r.rank = rank;
+      r.tok0 = (int32_t)first[j]; r.ntok = P.job_nseg[j];
+      const int chunk = r.kind == 0 ? local : local - nb_db;
+      const int ncols = r.kind == 0 ? P.h_out : P.h_in;
+      r.lo = chunk * cw;
+      r.hi = std::min(ncols, r.lo + cw);
+      r.part = P.job_part[j]; r.aux = P.job_accum[j];
+      put(r);
+    }
+    return hipSuccess;
+  }
+  hipError_t reduce(const WgradReducePlan& R) override {
+    const int launch = launches++;
+    const int grid = R.red_item0[R.n_red];
+    for (int b = 0; b < grid; ++b) {
+      int j = 0;
+      while (j + 1 < R.n_red && b >= R.red_item0[j + 1]) ++j;
+      const int64_t n_all = (int64_t)(R.h_in + R.h_out) * R.red_rank[j];
+      lora_plan_item_t r{};
+      r.launch = launch; r.phase = LORA_PHASE_REDUCE; r.block = b; r.grid = grid; r.tile = j;
+      r.adapter = R.red_adapter[j]; r.rank = R.red_rank[j];
+      const int64_t e0 = (int64_t)(b - R.red_item0[j]) * kReduceElems;
+      r.lo = (int32_t)std::min(e0, n_all);
+      r.hi = (int32_t)std::min(e0 + kReduceElems, n_all);
+      r.part = R.red_slot0[j]; r.aux = R.red_nparts[j];
+      put(r);
+    }
+    return hipSuccess;
+  }
+};
+
+}  // namespace
+
+extern "C" int lora_inspect_plan(int op, int32_t num_proj, const lora_adapters_t* const* adapters,
+                                 const lora_segments_t* segments, uint32_t options, int32_t cus, int32_t xccs,
+                                 lora_plan_item_t* items, int64_t items_cap, int64_t* n_items, int32_t* ranges,
+                                 int64_t ranges_cap, int64_t* n_ranges) {
+  g_last_error.clear();
+  if (!adapters || !n_items || !n_ranges || (items_cap > 0 && !items) || (ranges_cap > 0 && !ranges))
+    return fail(LORA_INVALID_ARGUMENT, "NULL argument");
+  if (cus < 8 || xccs < 1) return fail(LORA_INVALID_ARGUMENT, "cus must be >= 8 and xccs >= 1");
+  Recorder rec;
+  rec.d = DeviceInfo{cus, 100000, xccs};
+  rec.items = items; rec.cap = items_cap; rec.ranges = ranges; rec.rcap = ranges_cap;
+  // stand-in device addresses (16-byte aligned, distinct, never dereferenced)
+  char* const base = reinterpret_cast<char*>((uintptr_t)1 << 40);
+  void* x = base;
+  void* y = base + ((uintptr_t)1 << 36);
+  float* u = reinterpret_cast<float*>(base + ((uintptr_t)2 << 36));
+  void* ws = base + ((uintptr_t)3 << 36);
+  const size_t ws_bytes = (size_t)1 << 35;
+  void* dxp = base + ((uintptr_t)4 << 36);
+  const uint64_t* tabs = reinterpret_cast<const uint64_t*>(base + ((uintptr_t)5 << 36));
+  int st = LORA_OK;
+  if (!adapters[0]) return fail(LORA_INVALID_ARGUMENT, "adapters[0] is NULL");
+  const lora_adapters_t* a = adapters[0];
+  const int64_t ldx = a->h_in, ldy = a->h_out, ldu = LORA_MAX_RANK;
+  if (op == LORA_OP_FUSED && num_proj > 1) {
+    void* ys[kMaxProj];
+    int64_t lds[kMaxProj];
+    for (int p = 0; p < std::min<int32_t>(num_proj, kMaxProj); ++p) {
+      ys[p] = base + ((uintptr_t)(8 + p) << 36);
+      lds[p] = adapters[p] ? adapters[p]->h_out : 8;
+    }
+    st = sgmv_fused_multi_impl(x, ldx, num_proj, adapters, segments, ys, lds, ws, ws_bytes, rec);
+  } else if (num_proj != 1) {
+    st = fail(LORA_INVALID_ARGUMENT, "num_proj must be 1 for this op");
+  } else if (op == LORA_OP_SHRINK) {
+    st = sgmv_shrink_impl(x, ldx, a, segments, u, ldu, ws, ws_bytes, rec);
+  } else if (op == LORA_OP_EXPAND) {
+    st = sgmv_expand_impl(u, ldu, a, segments, y, ldy, rec);
+  } else if (op == LORA_OP_FUSED) {
+    st = sgmv_fused_impl(x, ldx, a, segments, y, ldy, (options & LORA_INSPECT_WITH_U) ? u : nullptr, ldu, ws,
+                         ws_bytes, rec);
+  } else if (op == LORA_OP_BACKWARD) {
+    st = packed_backward_impl(x, ldx, y, ldy, (options & LORA_INSPECT_WITH_U) ? u : nullptr, ldu, a, segments,
+                              (options & LORA_INSPECT_WITH_DX) ? dxp : nullptr, ldx, tabs, tabs + 1024,
+                              (options & LORA_INSPECT_ACCUMULATE) ? LORA_GRAD_ACCUMULATE : 0u, ws, ws_bytes, rec);
+  } else {
+    st = fail(LORA_INVALID_ARGUMENT, "unknown op %d", op);
+  }
+  *n_items = rec.n;
+  *n_ranges = rec.nr;
+  return st;
 }
 
 }  // extern "C"

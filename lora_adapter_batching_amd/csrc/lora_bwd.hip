@@ -101,13 +101,8 @@ hipError_t launch_transpose(const TransposePlan& P, hipStream_t stream) {
 // B = Q (32 tokens x 16 ranks, fp32 split into bf16 hi + lo, staged through
 // LDS transposed). The loads of the next kWgDepth-1 steps are in flight while
 // a step is computed.
-// Columns per lane QN and rank blocks of 16 (KB) for a rank.
-__host__ __device__ constexpr int wgrad_qn(int kb) { return kb <= 4 ? 4 : 2; }
-__host__ __device__ inline int wgrad_kb(int rank) {
-  const int k = (rank + 15) >> 4;
-  return k <= 1 ? 1 : (k <= 2 ? 2 : (k <= 4 ? 4 : 8));
-}
-__host__ __device__ inline int wgrad_cw(int rank) { return 4 * 16 * wgrad_qn(wgrad_kb(rank)); }
+// Columns per lane QN and rank blocks of 16 (KB) for a rank: wgrad_qn,
+// wgrad_kb, wgrad_cw (shared with the host planner).
 
 constexpr int kQtLd = 36;    // LDS row length (floats) of the transposed Q tile
 constexpr int kWgDepth = 3;  // steps whose loads are in flight (and LDS Q buffers)
@@ -144,10 +139,11 @@ __device__ __forceinline__ void wg_load(const WgradPlan& P, const uint16_t* Z, i
   const bool live = c.seg < seg_end;
   const int cnt = live ? min(32, c.tend - c.t0) : 0;  // valid tokens of the step (uniform)
   // Z: a resource over the step's rows (contiguous positions) or over the
-  // whole matrix (token_rows gather; row * ldz * 2 < 2 GiB)
+  // whole matrix (token_rows gather: a row is read only if it lies wholly
+  // inside the resource, with its offset kept in 64 bits)
   __amdgpu_buffer_rsrc_t zr, rr;
   if constexpr (GATHER) {
-    zr = mk_rsrc(Z, cnt > 0 ? (int64_t)0x7ffffff0 : 0);
+    zr = mk_rsrc(Z, cnt > 0 ? kGatherSpan : 0);
     rr = mk_rsrc(P.token_rows + (live ? c.t0 : 0), (int64_t)cnt * 4);
   } else {
     zr = mk_rsrc(Z + (int64_t)(live ? c.t0 : 0) * ldz, cnt > 0 ? ((int64_t)(cnt - 1) * ldz + ncols) * 2 : 0);
@@ -156,9 +152,14 @@ __device__ __forceinline__ void wg_load(const WgradPlan& P, const uint16_t* Z, i
   for (int e = 0; e < 8; ++e) {
     const int r = 8 * g + e;
     const bool ok = col_ok && r < cnt;
-    int64_t row = r;
-    if constexpr (GATHER) row = (int64_t)__builtin_amdgcn_raw_buffer_load_b32(rr, ok ? 4 * r : (int)kOff, 0, 0);
-    const uint32_t off = ok ? (uint32_t)(row * ldz * 2 + (int64_t)ccol * 2) : kOff;
+    bool in = ok;
+    int64_t row_bytes = (int64_t)r * ldz * 2;
+    if constexpr (GATHER) {
+      const int32_t row = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rr, ok ? 4 * r : (int)kOff, 0, 0);
+      row_bytes = (int64_t)row * ldz * 2;
+      in = ok && row_bytes >= 0 && row_bytes <= kGatherSpan - (int64_t)ncols * 2;
+    }
+    const uint32_t off = in ? (uint32_t)(row_bytes + (int64_t)ccol * 2) : kOff;
     if constexpr (QN == 4) {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(zr, (int)off, 0, 0);

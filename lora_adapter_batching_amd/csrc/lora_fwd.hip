@@ -225,6 +225,7 @@ struct Lds {
 struct TileRows {
   __amdgpu_buffer_rsrc_t r;
   int64_t ld2;  // row stride in bytes
+  int64_t lim;  // gather: largest row offset (bytes) whose whole row lies in the resource
   bool gather;
 };
 template <typename PT>
@@ -233,18 +234,23 @@ __device__ __forceinline__ TileRows tile_rows(const uint16_t* base, int64_t ld, 
   TileRows tr;
   tr.gather = P.token_rows != nullptr;
   tr.ld2 = ld * 2;
+  tr.lim = kGatherSpan - (int64_t)width * 2;
   if (tr.gather)
-    tr.r = mk_rsrc(base, (int64_t)0x7ffffff0);
+    tr.r = mk_rsrc(base, kGatherSpan);
   else
     tr.r = mk_rsrc(base + (int64_t)t.p0 * ld, ((int64_t)(t.cnt - 1) * ld + width) * 2);
   return tr;
 }
-// Byte offset of tile row n in the resource (kOff if not a valid token).
+// Byte offset of tile row n in the resource (kOff if not a valid token). A
+// gathered row is computed in 64 bits and is absent (kOff: reads zero, its
+// stores are dropped) unless the whole row lies inside the resource, so a
+// row index far past the matrix can never wrap onto another row.
 template <typename PT>
 __device__ __forceinline__ uint32_t row_off(const PT& P, const TileInfo& t, const TileRows& tr, int n) {
   if (n >= t.cnt) return kOff;
-  const int64_t row = tr.gather ? (int64_t)P.token_rows[t.p0 + n] : (int64_t)n;
-  return (uint32_t)(row * tr.ld2);
+  if (!tr.gather) return (uint32_t)((int64_t)n * tr.ld2);
+  const int64_t off = (int64_t)P.token_rows[t.p0 + n] * tr.ld2;
+  return (off < 0 || off > tr.lim) ? kOff : (uint32_t)off;
 }
 
 // ---------------------------------------------------------------------------
@@ -335,7 +341,7 @@ __device__ __forceinline__ void shrink_lds(const PT& P, const TileInfo& t, int k
   ShrinkCtx<RB> C;
   const TileRows xt = tile_rows(P.X, P.ldx, P.K, P, t);
   if (xt.gather)
-    C.xr = mk_rsrc_words(P.X, (int64_t)0x7ffffff0);
+    C.xr = mk_rsrc_words(P.X, kGatherSpan);
   else
     C.xr = mk_rsrc_words(P.X + (int64_t)t.p0 * P.ldx, ((int64_t)(t.cnt - 1) * P.ldx + P.K) * 2);
   const uint32_t ldw2 = 2u * (uint32_t)P.K;
@@ -593,10 +599,7 @@ __device__ __forceinline__ StgCtx<RB> stg_ctx(const PT& P, const TileInfo& t, in
     C.vrow[j] = (uint16_t)row;
     C.vlds[j] = (uint16_t)(row * G::RP + 8 * (f - row * rv));
   }
-  const int nblocks = (pv.N + 31) >> 5;
-  const int cb0 = c * pv.nblk;
-  C.c0 = 32 * cb0;
-  C.c1 = min(pv.N, 32 * min(nblocks, cb0 + pv.nblk));
+  expand_cols(pv.N, pv.nblk, c, C.c0, C.c1);
   C.oscale = P.scale_in_shrink ? 1.f : t.scale;
   return C;
 }
@@ -759,10 +762,7 @@ __device__ __forceinline__ ExpCtx<RB> exp_ctx(const PT& P, const TileInfo& t, in
   C.vr = mk_rsrc(v_ptr(P, t), (int64_t)pv.N * C.ldv * 2);
   C.rank = t.rank;
   C.kbn = (t.rank + 15) >> 4;
-  const int nblocks = (pv.N + 31) >> 5;
-  const int cb0 = c * pv.nblk;
-  C.c0 = 32 * cb0;
-  C.c1 = min(pv.N, 32 * min(nblocks, cb0 + pv.nblk));
+  expand_cols(pv.N, pv.nblk, c, C.c0, C.c1);
   C.nb = (C.c1 - C.c0 + 31) >> 5;
   C.oscale = P.scale_in_shrink ? 1.f : t.scale;
   return C;
@@ -946,8 +946,8 @@ __device__ __forceinline__ void sum_parts_to_lds(const PT& P, const TileInfo& t,
 template <int RB, typename PT>
 __device__ __forceinline__ void item_shrink(const PT& P, const Lds& L, const TileInfo& t, int c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kb = c * P.kchunk;
-  const int ke = min(P.K, kb + P.kchunk);
+  int kb, ke;
+  shrink_range(P.K, P.kchunk, c, kb, ke);
   f32x16 acc[RB];
   shrink_lds<RB>(P, t, kb, ke, L, acc);
   float* red = L.red();
@@ -1084,8 +1084,8 @@ __device__ __forceinline__ void item_expand_wait(const PT& P, const Lds& L, cons
   const float ps = P.scale_in_shrink ? t.scale : 1.f;
   float run[4 * RB];
   for (int q = 0; q < P.ks; ++q) {
-    const int kb = q * P.kchunk;
-    const int ke = min(P.K, kb + P.kchunk);
+    int kb, ke;
+    shrink_range(P.K, P.kchunk, q, kb, ke);
     f32x16 acc[RB];
     shrink_lds<RB>(P, t, kb, ke, L, acc);
     int idx = 0;
@@ -1105,9 +1105,9 @@ __device__ __forceinline__ void item_expand_wait(const PT& P, const Lds& L, cons
 template <int RB, typename PT>
 __device__ __forceinline__ void run_item(const PT& P, const Lds& L, const TileInfo& t, int kind, int c) {
   switch (kind) {
-    case 0: item_shrink<RB>(P, L, t, c); break;
-    case 1: item_expand<RB>(P, L, t, c); break;
-    case 2: item_fused_tile<RB>(P, L, t, c); break;
+    case kItemShrink: item_shrink<RB>(P, L, t, c); break;
+    case kItemExpand: item_expand<RB>(P, L, t, c); break;
+    case kItemFusedTile: item_fused_tile<RB>(P, L, t, c); break;
     default: item_expand_wait<RB>(P, L, t, c); break;
   }
 }
@@ -1126,36 +1126,8 @@ __global__ __launch_bounds__(kThreads, 2) void sgmv_fwd_kernel(PT P) {
   asm volatile("" ::"s"(P.mode), "s"(P.xcd_local), "s"(P.xcd_remap), "s"(P.n_tiles), "s"(P.ks),
                "s"(P.nc), "s"(P.n_items_a), "s"(P.n_items_b), "s"(P.grid), "s"(P.n_seg),
                "s"(P.ptrs_in_plan), "s"(P.seg_tile0[0]), "s"(P.seg_tok0[0]), "s"(P.seg_ntok[0]));
-  int g = -1, c = 0, kind = 0;
-  if (P.mode == kModeFusedDep) {
-    if (P.xcd_local) {
-      // XCD x = b % 8 runs tiles x, x + 8, ...: their shrink parts first, then
-      // their expands (workgroup b runs on XCD b % 8)
-      const int x = b & 7, j = b >> 3;
-      const int tx = (P.n_tiles - x + 7) >> 3;
-      if (j < tx * P.ks) {
-        const int i = j / P.ks;
-        g = x + 8 * i; c = j - i * P.ks; kind = 0;
-      } else if (j < tx * (P.ks + P.nc)) {
-        const int j2 = j - tx * P.ks, i = j2 / P.nc;
-        g = x + 8 * i; c = j2 - i * P.nc; kind = 3;
-      }
-    } else if (b < P.n_items_a) {
-      g = b / P.ks; c = b - g * P.ks; kind = 0;
-    } else if (b < P.n_items_a + P.n_items_b) {
-      const int it = b - P.n_items_a;
-      g = it / P.nc; c = it - g * P.nc; kind = 3;
-    }
-  } else {
-    int it = b;
-    if (P.xcd_remap) {
-      const int q = P.grid >> 3;
-      it = (b & 7) * q + (b >> 3);
-    }
-    const int per = P.mode == kModeShrink ? P.ks : P.nc;
-    if (it < P.n_items_a) { g = it / per; c = it - g * per; }
-    kind = P.mode == kModeShrink ? 0 : (P.mode == kModeExpand ? 1 : 2);
-  }
+  const FwdItem it = fwd_item(P, b);
+  const int g = it.g, c = it.c, kind = it.kind;
   if (g >= 0) {
     const TileInfo t = tile_info(P, g, L.ti);
     if (RBMAX == 1 || t.rank <= 32) run_item<1>(P, L, t, kind, c);

@@ -5,6 +5,7 @@
 // host-to-device copy of metadata: segment tables live in the kernel-argument
 // segment and are read with scalar loads.
 #pragma once
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace lora {
@@ -16,6 +17,11 @@ constexpr int kMaxJobs = 64;   // adapter jobs per weight-gradient launch
 constexpr int kMaxJobSeg = 128;
 constexpr int kMaxPartials = 2048;  // (tile, k-chunk) parts in split modes (bounds the workspace)
 constexpr int kMaxProj = 4;         // projections over one x in one fused launch
+// Span (bytes) of the buffer resource over a whole matrix whose rows are
+// gathered through a token-row table: a row whose bytes would end past it is
+// treated as absent by the kernels, and the host rejects batches whose T
+// rows cannot fit in it.
+constexpr int64_t kGatherSpan = 0x7ffffff0;
 
 // Forward-style launch modes (also used for the backward du/dx pass).
 enum FwdMode : int32_t {
@@ -101,6 +107,86 @@ struct FwdPlanT : FwdHeader {
   uint8_t seg_proj[CAP];  // projection of the segment (0 unless multi-projection)
 };
 using FwdPlan = FwdPlanT<kMaxSeg>;
+
+// ---------------------------------------------------------------------------
+// Item geometry of a forward-style launch, shared by the kernel (which runs
+// it) and the host planner's inspection entry (which lists it for tests).
+// ---------------------------------------------------------------------------
+enum ItemKind : int32_t {
+  kItemShrink = 0,      // shrink over k-chunk c of tile g
+  kItemExpand = 1,      // expand column chunk c of tile g, U from memory
+  kItemFusedTile = 2,   // tile g's whole shrink on chip, then column chunk c
+  kItemExpandWait = 3,  // column chunk c of tile g after its shrink parts
+};
+struct FwdItem {
+  int g;     // tile (-1: the workgroup has nothing to do)
+  int c;     // k-chunk (shrink) or column chunk (expand kinds)
+  int kind;  // ItemKind
+};
+
+// Item of workgroup b.
+__host__ __device__ __forceinline__ FwdItem fwd_item(const FwdHeader& P, int b) {
+  FwdItem it{-1, 0, kItemShrink};
+  if (P.mode == kModeFusedDep) {
+    if (P.xcd_local) {
+      // XCD x = b % 8 runs tiles x, x + 8, ...: their shrink parts first,
+      // then their expands (workgroup b runs on XCD b % 8)
+      const int x = b & 7, j = b >> 3;
+      const int tx = (P.n_tiles - x + 7) >> 3;
+      if (j < tx * P.ks) {
+        const int i = j / P.ks;
+        it = FwdItem{x + 8 * i, j - i * P.ks, kItemShrink};
+      } else if (j < tx * (P.ks + P.nc)) {
+        const int j2 = j - tx * P.ks, i = j2 / P.nc;
+        it = FwdItem{x + 8 * i, j2 - i * P.nc, kItemExpandWait};
+      }
+    } else if (b < P.n_items_a) {
+      const int g = b / P.ks;
+      it = FwdItem{g, b - g * P.ks, kItemShrink};
+    } else if (b < P.n_items_a + P.n_items_b) {
+      const int i = b - P.n_items_a, g = i / P.nc;
+      it = FwdItem{g, i - g * P.nc, kItemExpandWait};
+    }
+    return it;
+  }
+  int i = b;
+  if (P.xcd_remap) {
+    const int q = P.grid >> 3;
+    i = (b & 7) * q + (b >> 3);
+  }
+  const int per = P.mode == kModeShrink ? P.ks : P.nc;
+  const int kind = P.mode == kModeShrink ? kItemShrink : (P.mode == kModeExpand ? kItemExpand : kItemFusedTile);
+  if (i < P.n_items_a) {
+    const int g = i / per;
+    it = FwdItem{g, i - g * per, kind};
+  }
+  return it;
+}
+
+// k range [kb, ke) of shrink part c.
+__host__ __device__ __forceinline__ void shrink_range(int K, int kchunk, int c, int& kb, int& ke) {
+  kb = c * kchunk;
+  ke = K < kb + kchunk ? K : kb + kchunk;
+}
+
+// Column range [c0, c1) of expand chunk c of an output n columns wide that
+// is cut into chunks of nblk 32-column blocks.
+__host__ __device__ __forceinline__ void expand_cols(int n, int nblk, int c, int& c0, int& c1) {
+  const int nblocks = (n + 31) >> 5;
+  const int cb0 = c * nblk;
+  const int cb1 = nblocks < cb0 + nblk ? nblocks : cb0 + nblk;
+  c0 = 32 * cb0;
+  c1 = n < 32 * cb1 ? n : 32 * cb1;
+}
+
+// Weight-gradient items: columns per lane QN and 16-wide rank blocks KB of a
+// rank, and the hidden columns one item owns.
+__host__ __device__ constexpr int wgrad_qn(int kb) { return kb <= 4 ? 4 : 2; }
+__host__ __device__ inline int wgrad_kb(int rank) {
+  const int k = (rank + 15) >> 4;
+  return k <= 1 ? 1 : (k <= 2 ? 2 : (k <= 4 ? 4 : 8));
+}
+__host__ __device__ inline int wgrad_cw(int rank) { return 4 * 16 * wgrad_qn(wgrad_kb(rank)); }
 
 // Weight-gradient launch: items are (job, kind, column chunk); a job is one
 // adapter (or part of its segments) whose token reduction the item owns.

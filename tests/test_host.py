@@ -91,11 +91,12 @@ def _adapters(ranks=(8, 16), scales=None, h_in=64, h_out=32, A=FAKE, Bp=FAKE):
     return c, (ranks, scales)
 
 
-def _segments(starts, adapter, T=None):
+def _segments(starts, adapter, T=None, token_rows=0):
     starts = np.ascontiguousarray(starts, np.int32)
     adapter = np.ascontiguousarray(adapter, np.int32)
     T = int(starts[-1]) if T is None else T
-    c = B.CSegments(T, len(adapter), starts.ctypes.data, adapter.ctypes.data if len(adapter) else 0, 0)
+    c = B.CSegments(T, len(adapter), starts.ctypes.data, adapter.ctypes.data if len(adapter) else 0,
+                    token_rows)
     return c, (starts, adapter)
 
 
@@ -205,7 +206,7 @@ def test_multi_projection_validation():
 
     def call(ads, n=None, ys=None, lds=None, ws=FAKE, wsb=1 << 30):
         n = len(ads) if n is None else n
-        ys = ys if ys is not None else [FAKE] * len(ads)
+        ys = ys if ys is not None else [FAKE + (1 << 24) * (p + 1) for p in range(len(ads))]
         lds = lds if lds is not None else [32, 48, 32, 32][:len(ads)]
         yp = (ctypes.c_void_p * len(ys))(*ys)
         ld = (ctypes.c_int64 * len(lds))(*lds)
@@ -220,6 +221,11 @@ def test_multi_projection_validation():
     assert call([a0, a_n]) == B.LORA_INVALID_ARGUMENT
     assert call([a0, a1], ys=[FAKE, 0]) == B.LORA_INVALID_ARGUMENT  # projection 1 has work (adapter 0)
     assert call([a0, a1], lds=[32, 40]) == B.LORA_INVALID_ARGUMENT  # row stride below h_out 48
+    # outputs that alias each other or x are refused
+    assert call([a0, a1], ys=[FAKE + 4096, FAKE + 4096]) == B.LORA_INVALID_ARGUMENT
+    assert "same buffer" in lib.lora_last_error().decode()
+    assert call([a0, a1], ys=[FAKE + 4096, FAKE]) == B.LORA_INVALID_ARGUMENT
+    assert "overlap x" in lib.lora_last_error().decode()
     n = ctypes.c_size_t(0)
     assert lib.lora_workspace_size_multi(2, ctypes.cast(arr(a0, a1), ctypes.c_void_p), ctypes.byref(sg),
                                          ctypes.byref(n)) == 0
@@ -235,3 +241,41 @@ def test_multi_projection_validation():
     assert lib.lora_sgmv_fused_multi(0, 64, 2, ctypes.cast(arr(a0, a1), ctypes.c_void_p), ctypes.byref(sg_skip),
                                      ctypes.cast(yp, ctypes.c_void_p), ctypes.cast(ld, ctypes.c_void_p),
                                      0, 0, 0) == B.LORA_OK
+
+
+def test_token_rows_gather_span_is_checked_on_the_host():
+    """With a token-row table the kernels reach every row through one window
+    of 2 GiB - 16 bytes from the matrix base; a batch whose T distinct rows
+    cannot fit in it is refused before any GPU call, for every matrix the
+    call touches (x, y, dx, dy)."""
+    lib = L.load()
+    span = 0x7FFFFFF0
+    h = 19456  # gate_up-like output width: rows of 38912 bytes
+    T_fit = (span // 2 - h) // h + 1       # largest T whose rows fit
+    for T, ok in ((T_fit, True), (T_fit + 1, False)):
+        ad, ka = _adapters(ranks=(16, 8), h_in=64, h_out=h)
+        sg, ks = _segments([0, T], [0], token_rows=FAKE)
+        # a zero-byte workspace stops a call that passes every argument check
+        # at the workspace check, which runs after the gather check and
+        # before anything reaches the GPU
+        st = _fused(ad, sg, ldx=64, ldy=h, wsb=0)
+        if ok:
+            assert st == B.LORA_WORKSPACE_TOO_SMALL, lib.lora_last_error().decode()
+        else:
+            assert st == B.LORA_INVALID_ARGUMENT
+            assert "gather limit" in lib.lora_last_error().decode()
+    # the same rows without a table address x/y per tile: no such limit
+    ad, ka = _adapters(ranks=(16, 8), h_in=64, h_out=h)
+    sg, ks = _segments([0, T_fit + 1], [0])
+    assert _fused(ad, sg, ldx=64, ldy=h, wsb=0) == B.LORA_WORKSPACE_TOO_SMALL
+    # an input-side stride alone can trip it too (x in a shrink, dy in a backward)
+    T = 1 << 16
+    ad, ka = _adapters(ranks=(16, 8), h_in=16384, h_out=32)
+    sg, ks = _segments([0, T], [0], token_rows=FAKE)
+    u = FAKE
+    st = lib.lora_sgmv_shrink(FAKE, 16384, ctypes.byref(ad), ctypes.byref(sg), u, 16, FAKE, 0, 0)
+    assert st == B.LORA_INVALID_ARGUMENT and "x: with token_rows" in lib.lora_last_error().decode()
+    ad, ka = _adapters(ranks=(16, 8), h_in=64, h_out=16384)
+    st = lib.lora_packed_backward(FAKE, 64, FAKE, 16384, 0, 0, ctypes.byref(ad), ctypes.byref(sg), 0, 0,
+                                  FAKE, FAKE, 0, FAKE, 0, 0)
+    assert st == B.LORA_INVALID_ARGUMENT and "dy: with token_rows" in lib.lora_last_error().decode()

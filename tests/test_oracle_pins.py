@@ -392,3 +392,79 @@ def test_workload_custom_is_deterministic():
     a = make_custom(5, 64, 48, [8, 16], ids=np.array([0, 1, 1, -1, 0], np.int32))
     b = make_custom(5, 64, 48, [8, 16], ids=np.array([0, 1, 1, -1, 0], np.int32))
     assert np.array_equal(a.x, b.x) and all(np.array_equal(p, q) for p, q in zip(a.A, b.A))
+
+
+# --------------------------------------------------------------------------
+# The Python helpers that feed the oracle: bf16 widening and the row /
+# adapter restrictions that build the references of the large parity checks
+# --------------------------------------------------------------------------
+def test_widen_matches_torch_on_every_bf16_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):  # float32 -> float64 of signalling NaN patterns
+        ours = oracle.widen(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    # 2 * (2^7 - 1) NaN payloads per sign: exponent all ones, mantissa non-zero
+    assert int(nan.sum()) == 2 * 127
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # the sign bit survives on zeros, and the extremes are what IEEE fixes
+    assert ours[0x0000] == 0.0 and not np.signbit(ours[0x0000])
+    assert ours[0x8000] == 0.0 and np.signbit(ours[0x8000])
+    assert ours[0x7F80] == np.inf and ours[0xFF80] == -np.inf
+    assert ours[0x3F80] == 1.0 and ours[0xC000] == -2.0
+    assert ours[0x0001] == 2.0 ** -133          # smallest subnormal
+    assert ours[0x007F] == 127 * 2.0 ** -133    # largest subnormal
+    assert ours[0x0080] == 2.0 ** -126          # smallest normal
+    assert ours[0x7F7F] == (2 - 2.0 ** -7) * 2.0 ** 127  # largest finite
+    # a 2-D array keeps its shape and row order
+    m = bits[:12].reshape(3, 4)
+    assert np.array_equal(oracle.widen(m), ours[:12].reshape(3, 4))
+
+
+def _helper_problem():
+    # request-order ids over 5 adapters (one of rank 0), with -1 tokens, an
+    # upstream gradient and a non-zero initial y
+    rng = np.random.default_rng(77)
+    ids = rng.integers(-1, 5, size=53).astype(np.int32)
+    return make_custom(11, 40, 24, [3, 8, 0, 5, 16], scales="random", ids=ids, with_dy=True, y0=True)
+
+
+def _nan_equal(a, b):
+    return np.array_equal(np.asarray(a), np.asarray(b), equal_nan=True)
+
+
+def test_batch_forward_tokens_equals_rows_of_forward():
+    p = _helper_problem()
+    ob = oracle.Batch(p)
+    y, u = ob.forward()
+    rng = np.random.default_rng(3)
+    for rows in (np.arange(p.T), rng.permutation(p.T)[:17], np.array([p.T - 1, 0, 5, 5])):
+        yr, ur = ob.forward_tokens(rows)
+        # each token is computed on its own in the same order: bit-identical
+        assert _nan_equal(yr, y[rows])
+        assert _nan_equal(ur, u[rows][:, :ur.shape[1]])
+    # an id -1 token keeps its initial row and leaves u unwritten
+    a = ob.token_adapter()
+    r = np.nonzero(a < 0)[0]
+    assert r.size > 0
+    yr, ur = ob.forward_tokens(r)
+    assert np.array_equal(yr, ob.y0[r]) and np.all(np.isnan(ur))
+
+
+def test_batch_backward_adapters_equals_full_backward():
+    p = _helper_problem()
+    ob = oracle.Batch(p)
+    du, dx, dA, dB = ob.backward()
+    a = ob.token_adapter()
+    for subset in ([0], [3, 1], [4, 0, 1, 3], [2]):
+        rows, dus, dxs, dAs, dBs = ob.backward_adapters(subset)
+        assert np.array_equal(rows, np.nonzero(np.isin(a, subset))[0])
+        # the token sums run over the same tokens in the same ascending order
+        for i in subset:
+            assert np.array_equal(dAs[i], dA[i]) and np.array_equal(dBs[i], dB[i])
+        # adapters outside the subset get no contribution
+        for i in set(range(p.N)) - set(subset):
+            assert not np.any(dAs[i]) and not np.any(dBs[i])
+        assert _nan_equal(dus, du[rows][:, :dus.shape[1]])
+        assert np.array_equal(dxs, dx[rows])

@@ -6,10 +6,13 @@ patterns. It holds none of the LoRA arithmetic: the CPU oracle and the HIP
 library both consume what it produces, and neither imports the other.
 """
 from .gen import (  # noqa: F401
+    Meta,
     Problem,
     CONFIG_NAMES,
+    DECODE_PROJECTIONS,
     bf16_bits_from_f32,
     make_config,
     make_custom,
     make_c2_projections,
+    make_meta,
 )

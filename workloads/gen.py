@@ -134,12 +134,49 @@ def _seg_problem(name, seed, rng, seg_lens, seg_adapter, h_in, h_out, ranks, sca
 CONFIG_NAMES = ["tiny", "decode", "prefill", "hetero", "train"]
 
 
+@dataclasses.dataclass
+class Meta:
+    """The batch structure of a workload without its tensors: widths, ranks,
+    scales and either request-order ids or an explicit segmentation. Drawn
+    with the same generator calls, in the same order, as the full workload,
+    so it matches the Problem of the same name and seed."""
+
+    name: str
+    T: int
+    h_in: int
+    h_out: int
+    ranks: np.ndarray
+    scales: np.ndarray
+    token_ids: np.ndarray
+    seg_lens: Optional[np.ndarray] = None
+    seg_adapter: Optional[np.ndarray] = None
+
+    @property
+    def N(self) -> int:
+        return int(len(self.ranks))
+
+    @property
+    def segmented(self) -> bool:
+        return self.seg_lens is not None
+
+
+def _tiny_meta(rng):
+    return rng.integers(0, 4, size=16).astype(np.int32)
+
+
 def make_tiny(seed: int = 0) -> Problem:
     """16 decode tokens, 256->256, 4 adapters of rank 8, scale 2.0, ids
     uniform in [0, 4) in request order."""
     rng = np.random.default_rng(seed)
-    ids = rng.integers(0, 4, size=16).astype(np.int32)
+    ids = _tiny_meta(rng)
     return _ids_problem("tiny", seed, rng, ids, 256, 256, [8] * 4, [2.0] * 4)
+
+
+def _decode_meta(rng):
+    return rng.integers(0, 8, size=256).astype(np.int32)
+
+
+DECODE_PROJECTIONS = (("q", 2560), ("o", 2560), ("gate_up", 19456))
 
 
 def make_c2_projections(seed: int = 1) -> Dict[str, Problem]:
@@ -148,9 +185,9 @@ def make_c2_projections(seed: int = 1) -> Dict[str, Problem]:
     scale 2.0, separate weights per projection. Three calls share the batch:
     q (2560->2560), o (2560->2560) and gate_up (2560->19456)."""
     rng = np.random.default_rng(seed)
-    ids = rng.integers(0, 8, size=256).astype(np.int32)
+    ids = _decode_meta(rng)
     out = {}
-    for proj, h_out in (("q", 2560), ("o", 2560), ("gate_up", 19456)):
+    for proj, h_out in DECODE_PROJECTIONS:
         out[proj] = _ids_problem(f"decode_{proj}", seed, rng, ids, 2560, h_out,
                                  [32] * 8, [2.0] * 8)
     return out
@@ -172,12 +209,17 @@ def prefill_segment_lengths(rng: np.random.Generator, total: int = 8192,
     return np.asarray(lens, dtype=np.int32)
 
 
+def _prefill_meta(rng):
+    lens = prefill_segment_lengths(rng)
+    seg_adapter = rng.integers(0, 8, size=len(lens)).astype(np.int32)
+    return lens, seg_adapter
+
+
 def make_prefill(seed: int = 2) -> Problem:
     """Chunked prefill, LLaMA-3-8B-like 4096->4096: 8 adapters of rank 16,
     8192 tokens in lognormal-length segments, adapter per segment uniform."""
     rng = np.random.default_rng(seed)
-    lens = prefill_segment_lengths(rng)
-    seg_adapter = rng.integers(0, 8, size=len(lens)).astype(np.int32)
+    lens, seg_adapter = _prefill_meta(rng)
     return _seg_problem("prefill", seed, rng, lens, seg_adapter, 4096, 4096,
                         [16] * 8, [2.0] * 8)
 
@@ -197,11 +239,15 @@ def make_hetero(seed: int = 3) -> Problem:
     {8,16,32,64,128}, scale 2.0, 4096 tokens, Zipf(1.1) popularity with the
     4 least popular adapters unused (empty segments)."""
     rng = np.random.default_rng(seed)
+    ranks, ids = _hetero_meta(rng)
+    return _ids_problem("hetero", seed, rng, ids, 4096, 14336, ranks, [2.0] * 32)
+
+
+def _hetero_meta(rng):
     ranks = rng.choice(np.array([8, 16, 32, 64, 128]), size=32).astype(np.int32)
     perm = rng.permutation(32).astype(np.int32)
     pop = rng.choice(32, size=4096, p=zipf_popularity())
-    ids = perm[pop].astype(np.int32)
-    return _ids_problem("hetero", seed, rng, ids, 4096, 14336, ranks, [2.0] * 32)
+    return ranks, perm[pop].astype(np.int32)
 
 
 def make_train(seed: int = 4) -> Problem:
@@ -209,11 +255,40 @@ def make_train(seed: int = 4) -> Problem:
     uniform from {8,16,32,64}, scale 2.0, each 4 sequences x 512 tokens,
     adapter-major; random upstream gradient dy."""
     rng = np.random.default_rng(seed)
+    ranks, lens, seg_adapter = _train_meta(rng)
+    return _seg_problem("train", seed, rng, lens, seg_adapter, 3584, 3584, ranks,
+                        [2.0] * 32, with_dy=True)
+
+
+def _train_meta(rng):
     ranks = rng.choice(np.array([8, 16, 32, 64]), size=32).astype(np.int32)
     seg_adapter = np.repeat(np.arange(32, dtype=np.int32), 4)
     lens = np.full(128, 512, dtype=np.int32)
-    return _seg_problem("train", seed, rng, lens, seg_adapter, 3584, 3584, ranks,
-                        [2.0] * 32, with_dy=True)
+    return ranks, lens, seg_adapter
+
+
+def make_meta(name: str, seed: Optional[int] = None, proj: str = "gate_up") -> Meta:
+    """Batch structure of the named workload (no tensors drawn). For
+    'decode', `proj` picks the projection width (q, o or gate_up)."""
+    idx = CONFIG_NAMES.index(name)
+    rng = np.random.default_rng(idx if seed is None else seed)
+    if name == "tiny":
+        ids = _tiny_meta(rng)
+        return Meta(name, 16, 256, 256, np.full(4, 8, np.int32), np.full(4, 2.0, np.float32), ids)
+    if name == "decode":
+        ids = _decode_meta(rng)
+        h_out = dict(DECODE_PROJECTIONS)[proj]
+        return Meta(f"decode_{proj}", 256, 2560, h_out, np.full(8, 32, np.int32), np.full(8, 2.0, np.float32), ids)
+    if name == "prefill":
+        lens, sa = _prefill_meta(rng)
+        return Meta(name, int(lens.sum()), 4096, 4096, np.full(8, 16, np.int32), np.full(8, 2.0, np.float32),
+                    np.repeat(sa, lens).astype(np.int32), lens, sa)
+    if name == "hetero":
+        ranks, ids = _hetero_meta(rng)
+        return Meta(name, 4096, 4096, 14336, ranks, np.full(32, 2.0, np.float32), ids)
+    ranks, lens, sa = _train_meta(rng)
+    return Meta(name, int(lens.sum()), 3584, 3584, ranks, np.full(32, 2.0, np.float32),
+                np.repeat(sa, lens).astype(np.int32), lens, sa)
 
 
 def make_config(name: str, seed: Optional[int] = None):

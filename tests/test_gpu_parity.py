@@ -350,13 +350,21 @@ def test_token_rows_far_row_is_absent_not_wrapped():
     other row changes (a 32-bit offset would have wrapped onto row 3)."""
     import torch
     L = _L()
-    T, h_in, h_out = 64, 256, 19456
+    T, h_in, h_out = 64, 1024, 19456
     rng = np.random.default_rng(9)
     ids = rng.integers(0, 3, size=T).astype(np.int32)
     prob = make_custom(12, h_in, h_out, [16, 8, 32], ids=ids, with_dy=True, y0=True)
     gp = GpuProblem(prob, use_token_rows=True, y0=True)
     far = 3 + (1 << 21)
-    assert (far * h_out * 2) % (1 << 32) == 3 * h_out * 2 and far * h_out * 2 >= 1 << 32
+    # the far row must lie past the gather window of EVERY matrix the calls
+    # touch (x and dx: h_in wide, y and dy: h_out wide): a row inside the
+    # window is a real row, and one past the end of a small matrix would be
+    # an access outside its allocation
+    span = 0x7FFFFFF0
+    for width in (h_in, h_out):
+        off = far * width * 2
+        assert off > span - 2 * width and off >= 1 << 32
+        assert off % (1 << 32) == 3 * width * 2  # a 32-bit offset would land on row 3
     p_far = int(np.nonzero(gp.perm != 3)[0][5])  # a sorted position whose row is not row 3
     r_lost = int(gp.perm[p_far])
     rows = gp.perm.copy()

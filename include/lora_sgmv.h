@@ -228,6 +228,25 @@ int lora_sgmv_fused_multi(const void* x, int64_t ldx, int32_t num_proj,
                           void* const* y, const int64_t* ldy, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * lora_sgmv_fused without a workspace, for callers that cannot allocate
+ * device memory or hand one over (code that must not call hipMalloc in its
+ * loop, serving loops and harnesses that forbid allocation). Arguments,
+ * results and errors are those of lora_sgmv_fused() minus ws / ws_bytes.
+ * The hand-off scratch is a static device array of
+ * LORA_NOALLOC_SCRATCH_BYTES per GPU, created with the library and held
+ * until the process ends; the call allocates nothing. A batch whose
+ * workspace (lora_workspace_size(LORA_OP_FUSED, ...)) exceeds it is refused
+ * with LORA_UNSUPPORTED before any HIP call. Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (different streams or
+ * threads) race, so they must be ordered. Not capturable into a HIP graph
+ * (each launch carries a fresh hand-off id, as for lora_sgmv_fused).
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int lora_sgmv_fused_noalloc(const void* x, int64_t ldx, const lora_adapters_t* adapters,
+                            const lora_segments_t* segments, void* y, int64_t ldy, float* u_save,
+                            int64_t ldu, void* stream);
+
+/*
  * Packed backward over all adapters of the batch ("Technische Samenvatting: PLoRA" (gist.science), "LoRA
  * Execution Engine": forward and backward cases tiled along the sequence or
  * hidden dimension):

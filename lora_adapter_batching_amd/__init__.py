@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     sgmv_expand,
     sgmv_fused,
     sgmv_fused_multi,
+    sgmv_fused_noalloc,
     sgmv_shrink,
     version,
     workspace_size,

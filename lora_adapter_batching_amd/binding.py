@@ -48,7 +48,9 @@ class CSegments(ctypes.Structure):
 
 EXPORTS = ["lora_segments_from_ids", "lora_workspace_size", "lora_sgmv_shrink", "lora_sgmv_expand",
            "lora_sgmv_fused", "lora_packed_backward", "lora_workspace_size_multi",
-           "lora_sgmv_fused_multi", "lora_status_string", "lora_last_error", "lora_version"]
+           "lora_sgmv_fused_multi", "lora_sgmv_fused_noalloc", "lora_status_string", "lora_last_error",
+           "lora_version"]
+NOALLOC_SCRATCH_BYTES = 16 << 20  # LORA_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -60,6 +62,10 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m lora_adapter_batching_amd.build`")
+    # torch (which provides the device memory and streams) brings its own HIP
+    # runtime; loading it first makes the library bind to that same runtime,
+    # so that one HIP runtime serves the process
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
@@ -79,6 +85,8 @@ def load(path: str = LIB_PATH):
                                               ctypes.POINTER(ctypes.c_size_t)]
     lib.lora_sgmv_fused_multi.argtypes = [P, I64, ctypes.c_int32, P, ctypes.POINTER(CSegments), P, P,
                                           P, ctypes.c_size_t, P]
+    lib.lora_sgmv_fused_noalloc.argtypes = [P, I64, ctypes.POINTER(CAdapters), ctypes.POINTER(CSegments),
+                                            P, I64, P, I64, P]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_last_error.restype = ctypes.c_char_p
@@ -241,6 +249,15 @@ def packed_backward(x, dy, u, adapters: Adapters, segments: Segments, dx, dA_ptr
         _ptr(u), u.stride(0) if u is not None else 0, adapters.c, segments.c, _ptr(dx),
         dx.stride(0) if dx is not None else 0, _ptr(dA_ptrs), _ptr(dB_ptrs), int(flags), wp, wb,
         _stream_handle(stream)))
+
+
+def sgmv_fused_noalloc(x, adapters: Adapters, segments: Segments, y, u_save=None, stream=None):
+    """lora_sgmv_fused_noalloc: the fused call with the library's static
+    device scratch instead of a workspace."""
+    lib = load()
+    ldu = u_save.stride(0) if u_save is not None else 0
+    _check(lib.lora_sgmv_fused_noalloc(_ptr(x), x.stride(0), adapters.c, segments.c, _ptr(y), y.stride(0),
+                                       _ptr(u_save), ldu, _stream_handle(stream)))
 
 
 def _multi_tables(adapters: Sequence[Adapters]):

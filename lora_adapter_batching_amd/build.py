@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblora_sgmv.so")
-SOURCES = ["lora_api.cpp", "lora_fwd.hip", "lora_bwd.hip"]
+SOURCES = ["lora_api.cpp", "lora_fwd.hip", "lora_bwd.hip", "lora_noalloc.hip"]
 ARCH = os.environ.get("LORA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -18,6 +18,7 @@
 
 #include "../../include/lora_sgmv.h"
 #include "lora_inspect.h"
+#include "lora_internal.h"
 #include "lora_plan.h"
 
 namespace lora {
@@ -639,6 +640,18 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 }  // namespace
 
+namespace lora {
+int set_error(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+}  // namespace lora
+
 // ===========================================================================
 // C ABI
 // ===========================================================================
@@ -755,7 +768,8 @@ static int sgmv_expand_impl(const float* u, int64_t ldu, const lora_adapters_t* 
 
 static int sgmv_fused_impl(const void* x, int64_t ldx, const lora_adapters_t* adapters,
                            const lora_segments_t* segments, void* y, int64_t ldy, float* u_save,
-                           int64_t ldu, void* ws, size_t ws_bytes, Launcher& launcher) {
+                           int64_t ldu, void* ws, size_t ws_bytes, Launcher& launcher,
+                           WsSource* src = nullptr) {
   int st = common_checks(adapters, segments);
   if (st) return st;
   const auto segs = active_segments(adapters, segments);
@@ -767,6 +781,16 @@ static int sgmv_fused_impl(const void* x, int64_t ldx, const lora_adapters_t* ad
   if (u_save && (st = check_u(u_save, ldu, max_rank_used(segs), "u_save"))) return st;
   if (!adapters->A_ptrs || !adapters->B_ptrs) return fail(LORA_INVALID_ARGUMENT, "A_ptrs/B_ptrs is NULL");
   const WsLayout L = ws_layout(LORA_OP_FUSED, adapters, segments);
+  if (src) {
+    if (L.total > src->cap)
+      return fail(LORA_UNSUPPORTED,
+                  "this batch needs %zu bytes of hand-off scratch and the library's static scratch holds %zu "
+                  "(call lora_sgmv_fused with a workspace instead)",
+                  L.total, src->cap);
+    ws = src->get();
+    if (!ws) return LORA_DEVICE_ERROR;
+    ws_bytes = src->cap;
+  }
   if ((st = check_ws(ws, ws_bytes, L.total))) return st;
   FwdCall c{};
   c.mode_op = LORA_OP_FUSED;
@@ -1398,3 +1422,10 @@ extern "C" int lora_inspect_plan(int op, int32_t num_proj, const lora_adapters_t
 }
 
 }  // extern "C"
+
+int lora::sgmv_fused_from(const void* x, int64_t ldx, const lora_adapters_t* adapters,
+                          const lora_segments_t* segments, void* y, int64_t ldy, float* u_save, int64_t ldu,
+                          WsSource& src, void* stream) {
+  HipLauncher launcher(stream);
+  return sgmv_fused_impl(x, ldx, adapters, segments, y, ldy, u_save, ldu, nullptr, 0, launcher, &src);
+}

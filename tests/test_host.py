@@ -279,3 +279,23 @@ def test_token_rows_gather_span_is_checked_on_the_host():
     st = lib.lora_packed_backward(FAKE, 64, FAKE, 16384, 0, 0, ctypes.byref(ad), ctypes.byref(sg), 0, 0,
                                   FAKE, FAKE, 0, FAKE, 0, 0)
     assert st == B.LORA_INVALID_ARGUMENT and "dy: with token_rows" in lib.lora_last_error().decode()
+
+
+def test_noalloc_refuses_batches_beyond_its_static_scratch():
+    """lora_sgmv_fused_noalloc checks the batch's workspace need against its
+    static scratch before any HIP call (so this runs without a GPU)."""
+    lib = L.load()
+    assert B.NOALLOC_SCRATCH_BYTES == 16 << 20
+    T = 65536
+    ad, ka = _adapters(ranks=(128, 8), h_in=4096, h_out=4096)
+    sg, ks = _segments([0, T], [0])
+    need = ctypes.c_size_t(0)
+    assert lib.lora_workspace_size(B.OP_FUSED, ctypes.byref(ad), ctypes.byref(sg), ctypes.byref(need)) == 0
+    assert need.value > B.NOALLOC_SCRATCH_BYTES
+    st = lib.lora_sgmv_fused_noalloc(FAKE, 4096, ctypes.byref(ad), ctypes.byref(sg), FAKE + (1 << 30), 4096,
+                                     0, 0, 0)
+    assert st == B.LORA_UNSUPPORTED
+    assert "static scratch" in lib.lora_last_error().decode()
+    # argument errors come first, as for lora_sgmv_fused
+    assert lib.lora_sgmv_fused_noalloc(0, 4096, ctypes.byref(ad), ctypes.byref(sg), FAKE, 4096, 0, 0, 0) \
+        == B.LORA_INVALID_ARGUMENT

@@ -429,6 +429,17 @@ int local_grid(int tiles, int ks, int nc) {
   return 8 * per_xcd_tiles * (ks + nc);
 }
 
+// A batch whose expand moves more than four times the bytes of its shrink
+// per tile, for the widest projection (32 tokens of y read and written plus
+// the expand weights, against 32 tokens of x plus the shrink weights).
+bool expand_heavy(const FwdCall& c, const std::vector<ActiveSeg>& segs, size_t base, int ns, int n_widest) {
+  int r = 0;
+  for (int i = 0; i < ns; ++i) r = std::max(r, segs[base + i].rank);
+  const double expand = (double)n_widest * (4.0 * kTileM + 2.0 * r);
+  const double shrink = (double)c.K * (2.0 * kTileM + 2.0 * r);
+  return expand > 4.0 * shrink;
+}
+
 int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int>& slot_of,
             Launcher& launcher) {
   if (segs.empty()) return LORA_OK;
@@ -531,6 +542,31 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
         P.xcd_local = fp.local && dev.xccs == 8 ? 1 : 0;
         P.grid = P.xcd_local ? local_grid(tiles, P.ks, P.nc) : P.n_items_a + P.n_items_b;
         if (fp.spin >= 0) P.spin_ticks = fp.spin;
+      } else if (4 * tiles <= cus && expand_heavy(c, segs, base, ns, n_widest)) {
+        // small batch whose expand moves far more bytes than its shrink
+        // (e.g. an MLP-up projection): the split layout with the items of
+        // every tile spread over all XCDs, so that the expand's y and weight
+        // traffic is shared by every XCD's L2 and fabric port rather than
+        // concentrated on the XCDs that hold two tiles; the parts go through
+        // device-scope stores and loads. Parts of about 320 columns, at most
+        // as many as one batch of the expand's part loads takes (8, 4, 2
+        // for rank <= 32, 64, 128), and the expand items of each tile fill
+        // about two workgroups per CU. (Measured on the decode gate_up
+        // projection, 2560 -> 19456 with 11 tiles: 16.8 us against 18.7 us
+        // for the XCD-local layout; parts of 256 columns: 19.1-19.9 us.)
+        P.mode = kModeFusedDep;
+        int rmax_l = 0;
+        for (int i = 0; i < ns; ++i) rmax_l = std::max(rmax_l, (int)P.seg_rank[i]);
+        const int rb = rmax_l <= 32 ? 1 : (rmax_l <= 64 ? 2 : 4);
+        int ks = std::max(1, std::min({8 / rb, cdiv(c.K, 320), kMaxPartials / tiles}));
+        P.kchunk = round_up(cdiv(c.K, ks), 64);
+        P.ks = cdiv(c.K, P.kchunk);
+        const int nc = std::max(1, std::min(nblocks, slots / tiles - P.ks));
+        P.nblk = cdiv(nblocks, nc);
+        P.nc = cdiv(nblocks, P.nblk);
+        P.n_items_a = tiles * P.ks;
+        P.n_items_b = tiles * P.nc;
+        P.grid = P.n_items_a + P.n_items_b;
       } else if (4 * tiles <= cus && dev.xccs == 8 && xcd_remap_enabled(true)) {
         // small batch: each tile's shrink is split along k into parts and its
         // expand into column chunks, all on one XCD, so the parts reach the

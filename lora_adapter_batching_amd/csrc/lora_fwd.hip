@@ -907,13 +907,15 @@ __device__ __forceinline__ void sum_parts_to_lds(const PT& P, const TileInfo& t,
   // together
   const __amdgpu_buffer_rsrc_t r = mk_rsrc(partial_ptr(P, t.g, 0), (int64_t)P.ks * kTileM * P.rpad * 4);
   const uint32_t part_bytes = (uint32_t)(kTileM * P.rpad * 4);
+  // a part is stored rank-major, P^T [rpad][32 tokens]: element e of the
+  // first RC rows is (rank e / 32, token e % 32) at float offset e, so the
+  // loads are contiguous across the workgroup
   float s[EPT];
   uint32_t off[EPT];
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const int e = threadIdx.x + kThreads * j;
-    const int n = e / RC, k = e - n * RC;
-    off[j] = (uint32_t)((n * P.rpad + k) * 4);
+    off[j] = (uint32_t)(e * 4);
     s[j] = 0.f;
   }
   constexpr int PD = 8 / RB;
@@ -936,7 +938,7 @@ __device__ __forceinline__ void sum_parts_to_lds(const PT& P, const TileInfo& t,
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const int e = threadIdx.x + kThreads * j;
-    const int n = e / RC, k = e - n * RC;
+    const int k = e / kTileM, n = e - k * kTileM;
     Pl[n * kLdp + k] = s[j] * ps;
   }
   lds_sync();
@@ -964,13 +966,12 @@ __device__ __forceinline__ void item_shrink(const PT& P, const Lds& L, const Til
     return;
   }
   float* part = partial_ptr(P, t.g, c);
-  const int rpad = P.rpad;
   if (P.mode == kModeFusedDep) {
     if (P.xcd_local)
-      reduce_waves<RB>(red, acc, wave, lane, [&](int k, int n, float v) __attribute__((always_inline)) { part[n * rpad + k] = v; });
+      reduce_waves<RB>(red, acc, wave, lane, [&](int k, int n, float v) __attribute__((always_inline)) { part[k * kTileM + n] = v; });
     else
       reduce_waves<RB>(red, acc, wave, lane, [&](int k, int n, float v) __attribute__((always_inline)) {
-        __hip_atomic_store(part + n * rpad + k, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(part + k * kTileM + n, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       });
     asm volatile("" ::: "memory");
     wait_vmcnt<0>();  // this thread's part stores have been performed
@@ -987,7 +988,7 @@ __device__ __forceinline__ void item_shrink(const PT& P, const Lds& L, const Til
   // same ordered sum as the fused hand-off, several parts' loads in flight),
   // writes u and returns the counter to 0
   reduce_waves<RB>(red, acc, wave, lane, [&](int k, int n, float v) __attribute__((always_inline)) {
-    __hip_atomic_store(part + n * rpad + k, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(part + k * kTileM + n, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   });
   asm volatile("" ::: "memory");
   wait_vmcnt<0>();  // this thread's part stores have been performed

@@ -52,7 +52,7 @@ struct FwdHeader {
   int64_t w_slot_elems;
   int64_t v_slot_elems;
   const int32_t* token_rows;  // row of X/Y for each sorted position, or null
-  float* partials;            // split-K partial sums [tile][ks][32][rpad]
+  float* partials;            // split-K partial sums [tile][ks][rpad][32] (rank-major)
   int32_t* counters;          // shrink-only arrival counters (zero on entry and on exit)
   uint64_t* stamps;           // kModeFusedDep: stamp of each shrink part ((launch_id << 8) | XCD)
   uint64_t launch_id;         // unique per launch (56 bits, never 0)

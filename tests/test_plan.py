@@ -135,11 +135,18 @@ def test_fused_plan_covers_every_output_once(name, proj, xccs):
     # every workgroup of the grid is listed once
     assert len(items) == int(items["grid"][0])
     assert np.array_equal(np.sort(items["block"]), np.arange(len(items)))
-    if name == "decode" and xccs == 8:
-        # small batch on 8 XCDs: all items of tile g run on XCD g % 8
+    if name == "decode":
         busy = items[items["kind"] >= 0]
-        assert np.all(busy["block"] % 8 == busy["tile"] % 8)
-        assert np.all(busy["mode"] == 3)
+        if xccs == 8 or proj == "gate_up":
+            assert np.all(busy["mode"] == 3)  # split shrink, parts handed to the expands
+        if proj == "q" and xccs == 8:
+            # small batch on 8 XCDs: all items of tile g run on XCD g % 8
+            assert np.all(busy["block"] % 8 == busy["tile"] % 8)
+        if proj == "gate_up":
+            # an expand-heavy small batch spreads every tile's items over all
+            # XCDs, parts of at most 320 columns (8 per tile at h_in 2560)
+            assert any(len(np.unique(busy[busy["tile"] == g]["block"] % 8)) == 8 for g in np.unique(busy["tile"]))
+            assert int(items["part"][0]) == 8
 
 
 def test_fused_plan_many_segments_and_edge_cases():

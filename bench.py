@@ -296,6 +296,68 @@ def bench_decode_request_order(steps=200, warmup=20, nsets=16):
                   {"note": "wall time per step incl. bookkeeping and the row-table upload"})
 
 
+def bench_decode_graph(steps=200, warmup=20, nsets=16):
+    """The decode step as one replayed HIP graph: the three projections'
+    device-planned calls (lora_sgmv_fused_graph: plan kernel + fused launch
+    each, ids and x/y in request order, every table on the device), captured
+    once per rotation set and replayed; wall time and GPU time per replay."""
+    import torch
+    import lora_adapter_batching_amd as L
+    from workloads import make_c2_projections
+    projs = make_c2_projections(1)
+    p0 = projs["q"]
+    T = int(p0.T)
+    graphs, keep = [], []
+    work_b = work_f = 0
+    perm, starts, adap = L.segments_from_ids(p0.token_ids, p0.N)
+    for name in ("q", "o", "gate_up"):
+        p = projs[name]
+        b, f = fwd_work(p.h_in, p.h_out, p.ranks, starts, adap)
+        work_b += b
+        work_f += f
+    for s in range(nsets):
+        calls = []
+        for name in ("q", "o", "gate_up"):
+            p = projs[name]
+            A = [dev_bf16(a) for a in p.A]
+            B = [dev_bf16(b) for b in p.B]
+            ap = torch.tensor([t.data_ptr() for t in A], dtype=torch.int64, device="cuda")
+            bp = torch.tensor([t.data_ptr() for t in B], dtype=torch.int64, device="cuda")
+            rk = torch.from_numpy(np.asarray(p.ranks, np.int32).copy()).cuda()
+            sc = torch.from_numpy(np.asarray(p.scales, np.float32).copy()).cuda()
+            ga = L.GraphAdapters(ap, bp, rk, sc, p.h_in, p.h_out, int(np.max(p.ranks)))
+            x = dev_bf16(p.x)
+            y = torch.zeros((T, p.h_out), dtype=torch.bfloat16, device="cuda")
+            ids = torch.from_numpy(np.asarray(p.token_ids, np.int32).copy()).cuda()
+            ws = L.new_workspace_graph(ga, T)
+            keep.append((A, B, ap, bp, rk, sc, ga, x, y, ids, ws))
+            calls.append((x, ga, ids, y, ws))
+        for c in calls:  # warm-up outside the capture
+            L.sgmv_fused_graph(*c)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                L.sgmv_fused_graph(*c)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % nsets].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        graphs[i % nsets].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    gpu = e0.elapsed_time(e1) * 1e-3 / steps
+    return _entry("decode_step_graph_replay_device_planned_qwen3_4b_256tok_8x_r32", np.array([sec]), work_b, work_f,
+                  {"gpu_us_per_step": round(gpu * 1e6, 2),
+                   "note": "one HIP graph per step: 3 x (plan kernel + fused launch), ids on the device"})
+
+
 # ---------------------------------------------------------------------------
 # Secondary workloads (HIP events around each call)
 # ---------------------------------------------------------------------------
@@ -535,7 +597,7 @@ def bench_secondary(reps=20):
     import torch
     import lora_adapter_batching_amd as L
     from workloads import make_config
-    out = [bench_decode_request_order()]
+    out = [bench_decode_request_order(), bench_decode_graph()]
     torch.cuda.empty_cache()
     out += bench_multi_projection()
     torch.cuda.empty_cache()

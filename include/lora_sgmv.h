@@ -38,8 +38,9 @@
  *    not be permuted by the caller). u and du always use sorted positions.
  *  - Streams: `stream` is a hipStream_t (NULL = the null stream). Calls only
  *    enqueue work and never synchronise the device. Calls must not be
- *    captured into a HIP graph: each launch carries a fresh hand-off id in
- *    its kernel argument, which a replayed graph would repeat.
+ *    captured into a HIP graph (each launch carries a fresh hand-off id in
+ *    its kernel argument, which a replayed graph would repeat), except
+ *    lora_sgmv_fused_graph(), which takes its id from the device.
  *  - Workspace: size it with lora_workspace_size(). It must be filled with
  *    zero bytes once before its first use; every call returns its counters
  *    to zero when its work completes. The hand-off stamps a call leaves in
@@ -226,6 +227,58 @@ int lora_workspace_size_multi(int32_t num_proj, const lora_adapters_t* const* ad
 int lora_sgmv_fused_multi(const void* x, int64_t ldx, int32_t num_proj,
                           const lora_adapters_t* const* adapters, const lora_segments_t* segments,
                           void* const* y, const int64_t* ldy, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * A decode step that can be captured into a HIP graph and replayed with new
+ * token ids and new weights. The pages' serving engine keeps every tenant's
+ * adapter resident, loads the trained weights in place after each optimizer
+ * step, and keeps decoding the other tenants' requests without a stall
+ * ("Trajectory presenta C-LoRA" (vivodigitale.it), "Come funziona
+ * l'architettura"; the Japanese page, architecture paragraph). Here the
+ * batch is described only by DEVICE data, so nothing the host computes is
+ * baked into a captured launch:
+ *
+ *   lora_sgmv_fused_graph() enqueues two kernels. A one-workgroup plan kernel
+ *   reads token_ids[num_tokens] (request order) and the adapters' device
+ *   ranks, groups the tokens per adapter with a stable counting sort
+ *   (adapters in id order, request order within), writes the tile table and
+ *   the sorted-position -> row table into the workspace, and advances an
+ *   epoch kept in the workspace. The fused shrink + expand launch then reads
+ *   its tiles, rows and hand-off id from the workspace:
+ *     y[t] += s_i B_i (A_i x[t])   for every token t whose id i is active,
+ *   with x and y in request order (rows 0 .. num_tokens-1). A token whose id
+ *   is outside [0, N), or whose adapter has a rank outside [1, max_rank] or
+ *   a null weight address, is left out (its row of y is not written).
+ *
+ * Everything a replay may change lives in device memory: the ids, the
+ * weights (updated in place) and the four per-adapter tables (re-pointed
+ * weights, new ranks up to max_rank, new scales). num_tokens, x, y, the
+ * tables' addresses and the workspace are fixed by the capture. The grid is
+ * laid out for the most tiles num_tokens ids can need, so a replay costs the
+ * same for any id mix. Results equal lora_sgmv_fused() on the same batch.
+ *
+ * The workspace (lora_workspace_size_graph) must be zero-filled once before
+ * its first use and must not be shared with other entry points; calls on
+ * one workspace must be ordered (a graph's replays on one stream are). The
+ * epoch makes every call's hand-off stamps distinct, across replays too.
+ * Errors are reported for the host arguments only; device data are not
+ * checked beyond the rules above.
+ */
+typedef struct lora_graph_adapters_t {
+  int32_t num_adapters;   /* N, 1..256 */
+  int32_t h_in;           /* multiple of 8 */
+  int32_t h_out;          /* multiple of 8 */
+  int32_t max_rank;       /* HOST bound on every rank a replay may use, 1..128 */
+  const uint64_t* A_ptrs; /* DEVICE [N]: bf16 A_i [r_i, h_in] */
+  const uint64_t* B_ptrs; /* DEVICE [N]: bf16 B_i [h_out, r_i] */
+  const int32_t* ranks;   /* DEVICE [N] */
+  const float* scales;    /* DEVICE [N] */
+} lora_graph_adapters_t;
+
+int lora_workspace_size_graph(const lora_graph_adapters_t* adapters, int32_t num_tokens, size_t* bytes);
+int lora_sgmv_fused_graph(const void* x, int64_t ldx, const lora_graph_adapters_t* adapters,
+                          const int32_t* token_ids, int32_t num_tokens, void* y, int64_t ldy, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /*
  * lora_sgmv_fused without a workspace, for callers that cannot allocate

@@ -7,6 +7,7 @@ script and a thin ctypes binding.
 """
 from .binding import (  # noqa: F401
     Adapters,
+    GraphAdapters,
     Segments,
     LoraError,
     GRAD_ACCUMULATE,
@@ -16,15 +17,18 @@ from .binding import (  # noqa: F401
     OP_SHRINK,
     load,
     new_workspace,
+    new_workspace_graph,
     new_workspace_multi,
     packed_backward,
     segments_from_ids,
     sgmv_expand,
     sgmv_fused,
+    sgmv_fused_graph,
     sgmv_fused_multi,
     sgmv_fused_noalloc,
     sgmv_shrink,
     version,
     workspace_size,
+    workspace_size_graph,
     workspace_size_multi,
 )

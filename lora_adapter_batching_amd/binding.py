@@ -46,10 +46,16 @@ class CSegments(ctypes.Structure):
                 ("token_rows", ctypes.c_void_p)]
 
 
+class CGraphAdapters(ctypes.Structure):
+    _fields_ = [("num_adapters", ctypes.c_int32), ("h_in", ctypes.c_int32), ("h_out", ctypes.c_int32),
+                ("max_rank", ctypes.c_int32), ("A_ptrs", ctypes.c_void_p), ("B_ptrs", ctypes.c_void_p),
+                ("ranks", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
 EXPORTS = ["lora_segments_from_ids", "lora_workspace_size", "lora_sgmv_shrink", "lora_sgmv_expand",
            "lora_sgmv_fused", "lora_packed_backward", "lora_workspace_size_multi",
-           "lora_sgmv_fused_multi", "lora_sgmv_fused_noalloc", "lora_status_string", "lora_last_error",
-           "lora_version"]
+           "lora_sgmv_fused_multi", "lora_sgmv_fused_noalloc", "lora_workspace_size_graph",
+           "lora_sgmv_fused_graph", "lora_status_string", "lora_last_error", "lora_version"]
 NOALLOC_SCRATCH_BYTES = 16 << 20  # LORA_NOALLOC_SCRATCH_BYTES
 
 _lib = None
@@ -87,6 +93,10 @@ def load(path: str = LIB_PATH):
                                           P, ctypes.c_size_t, P]
     lib.lora_sgmv_fused_noalloc.argtypes = [P, I64, ctypes.POINTER(CAdapters), ctypes.POINTER(CSegments),
                                             P, I64, P, I64, P]
+    lib.lora_workspace_size_graph.argtypes = [ctypes.POINTER(CGraphAdapters), ctypes.c_int32,
+                                              ctypes.POINTER(ctypes.c_size_t)]
+    lib.lora_sgmv_fused_graph.argtypes = [P, I64, ctypes.POINTER(CGraphAdapters), P, ctypes.c_int32, P, I64,
+                                          P, ctypes.c_size_t, P]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_last_error.restype = ctypes.c_char_p
@@ -258,6 +268,44 @@ def sgmv_fused_noalloc(x, adapters: Adapters, segments: Segments, y, u_save=None
     ldu = u_save.stride(0) if u_save is not None else 0
     _check(lib.lora_sgmv_fused_noalloc(_ptr(x), x.stride(0), adapters.c, segments.c, _ptr(y), y.stride(0),
                                        _ptr(u_save), ldu, _stream_handle(stream)))
+
+
+class GraphAdapters:
+    """Adapters described only by device tables (for lora_sgmv_fused_graph):
+    int64 A/B pointer tables, int32 ranks and float32 scales, all device
+    tensors the caller may rewrite between graph replays, plus the host bound
+    max_rank."""
+
+    def __init__(self, A_ptrs, B_ptrs, ranks, scales, h_in: int, h_out: int, max_rank: int):
+        self.A_ptrs, self.B_ptrs, self.ranks, self.scales = A_ptrs, B_ptrs, ranks, scales
+        self.h_in, self.h_out, self.max_rank = int(h_in), int(h_out), int(max_rank)
+        self._c = CGraphAdapters(int(ranks.numel()), self.h_in, self.h_out, self.max_rank, _ptr(A_ptrs),
+                                 _ptr(B_ptrs), _ptr(ranks), _ptr(scales))
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def workspace_size_graph(adapters: GraphAdapters, num_tokens: int) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check(lib.lora_workspace_size_graph(adapters.c, int(num_tokens), ctypes.byref(n)))
+    return int(n.value)
+
+
+def new_workspace_graph(adapters: GraphAdapters, num_tokens: int, device="cuda"):
+    import torch
+    return torch.zeros(max(workspace_size_graph(adapters, num_tokens), 256), dtype=torch.uint8, device=device)
+
+
+def sgmv_fused_graph(x, adapters: GraphAdapters, token_ids, y, ws, stream=None):
+    """lora_sgmv_fused_graph: x, y in request order, token_ids an int32 device
+    tensor of one adapter id per row of x."""
+    lib = load()
+    wp, wb = _ws(ws)
+    _check(lib.lora_sgmv_fused_graph(_ptr(x), x.stride(0), adapters.c, _ptr(token_ids), int(token_ids.numel()),
+                                     _ptr(y), y.stride(0), wp, wb, _stream_handle(stream)))
 
 
 def _multi_tables(adapters: Sequence[Adapters]):

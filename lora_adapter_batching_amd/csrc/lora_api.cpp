@@ -27,6 +27,7 @@ hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream, const uin
 hipError_t launch_transpose(const TransposePlan& P, hipStream_t stream);
 hipError_t launch_wgrad(const WgradPlan& P, int grid, hipStream_t stream);
 hipError_t launch_wgrad_reduce(const WgradReducePlan& R, hipStream_t stream);
+hipError_t launch_dev_plan(const DevPlanArgs& a, hipStream_t stream);
 int wgrad_items_for_rank(int rank, int h_in, int h_out);
 }  // namespace lora
 
@@ -94,6 +95,7 @@ struct Launcher {
   virtual hipError_t transpose(const TransposePlan& P) = 0;
   virtual hipError_t wgrad(const WgradPlan& P, int grid) = 0;
   virtual hipError_t reduce(const WgradReducePlan& R) = 0;
+  virtual hipError_t dev_plan(const DevPlanArgs& a) = 0;
 };
 
 struct HipLauncher final : Launcher {
@@ -106,6 +108,7 @@ struct HipLauncher final : Launcher {
   hipError_t transpose(const TransposePlan& P) override { return launch_transpose(P, stream); }
   hipError_t wgrad(const WgradPlan& P, int grid) override { return launch_wgrad(P, grid, stream); }
   hipError_t reduce(const WgradReducePlan& R) override { return launch_wgrad_reduce(R, stream); }
+  hipError_t dev_plan(const DevPlanArgs& a) override { return launch_dev_plan(a, stream); }
 };
 
 int round_up(int a, int b) { return (a + b - 1) / b * b; }
@@ -430,14 +433,130 @@ int local_grid(int tiles, int ks, int nc) {
 }
 
 // A batch whose expand moves more than four times the bytes of its shrink
-// per tile, for the widest projection (32 tokens of y read and written plus
-// the expand weights, against 32 tokens of x plus the shrink weights).
-bool expand_heavy(const FwdCall& c, const std::vector<ActiveSeg>& segs, size_t base, int ns, int n_widest) {
-  int r = 0;
-  for (int i = 0; i < ns; ++i) r = std::max(r, segs[base + i].rank);
+// per tile, for the widest output (32 tokens of y read and written plus the
+// expand weights, against 32 tokens of x plus the shrink weights; rank r).
+bool expand_heavy(int K, int n_widest, int r) {
   const double expand = (double)n_widest * (4.0 * kTileM + 2.0 * r);
-  const double shrink = (double)c.K * (2.0 * kTileM + 2.0 * r);
+  const double shrink = (double)K * (2.0 * kTileM + 2.0 * r);
   return expand > 4.0 * shrink;
+}
+
+// Layout of a fused launch over `tiles` 32-token tiles whose largest rank
+// is rmax_l and whose widest output has `nblocks` 32-column blocks: mode,
+// k split, column chunks and grid (the layouts and their measurements are
+// described at each branch).
+void fused_layout(FwdPlan& P, const FwdCall& c, int tiles, int rmax_l, int nblocks, const DeviceInfo& dev) {
+  const int cus = dev.cus;
+  const int slots = 2 * cus;  // resident workgroups at the kernels' occupancy
+  const ForcePlan fp = force_plan();
+  if (fp.mode == kModeFusedTile) {
+    P.mode = kModeFusedTile;
+    P.ks = 1;
+    P.kchunk = round_up(c.K, 64);
+    P.nblk = cdiv(nblocks, std::min(fp.nc, nblocks));
+    P.nc = cdiv(nblocks, P.nblk);
+    P.n_items_a = tiles * P.nc;
+    P.xcd_remap = xcd_remap_enabled(false) ? 1 : 0;
+    P.grid = P.xcd_remap ? round_up(P.n_items_a, 8) : P.n_items_a;
+  } else if (fp.mode == kModeFusedDep && fp.ks <= kMaxKs && tiles * fp.ks <= kMaxPartials) {
+    P.mode = kModeFusedDep;
+    P.kchunk = round_up(cdiv(c.K, fp.ks), 64);
+    P.ks = cdiv(c.K, P.kchunk);
+    P.nblk = cdiv(nblocks, std::min(fp.nc, nblocks));
+    P.nc = cdiv(nblocks, P.nblk);
+    P.n_items_a = tiles * P.ks;
+    P.n_items_b = tiles * P.nc;
+    P.xcd_local = fp.local && dev.xccs == 8 ? 1 : 0;
+    P.grid = P.xcd_local ? local_grid(tiles, P.ks, P.nc) : P.n_items_a + P.n_items_b;
+    if (fp.spin >= 0) P.spin_ticks = fp.spin;
+  } else if (4 * tiles <= cus && expand_heavy(c.K, nblocks * 32, rmax_l)) {
+    // small batch whose expand moves far more bytes than its shrink
+    // (e.g. an MLP-up projection): the split layout with the items of
+    // every tile spread over all XCDs, so that the expand's y and weight
+    // traffic is shared by every XCD's L2 and fabric port rather than
+    // concentrated on the XCDs that hold two tiles; the parts go through
+    // device-scope stores and loads. Parts of about 320 columns, at most
+    // as many as one batch of the expand's part loads takes (8, 4, 2
+    // for rank <= 32, 64, 128), and the expand items of each tile fill
+    // about two workgroups per CU. (Measured on the decode gate_up
+    // projection, 2560 -> 19456 with 11 tiles: 16.8 us against 18.7 us
+    // for the XCD-local layout; parts of 256 columns: 19.1-19.9 us.)
+    P.mode = kModeFusedDep;
+    const int rb = rmax_l <= 32 ? 1 : (rmax_l <= 64 ? 2 : 4);
+    int ks = std::max(1, std::min({8 / rb, cdiv(c.K, 320), kMaxPartials / tiles}));
+    P.kchunk = round_up(cdiv(c.K, ks), 64);
+    P.ks = cdiv(c.K, P.kchunk);
+    const int nc = std::max(1, std::min(nblocks, slots / tiles - P.ks));
+    P.nblk = cdiv(nblocks, nc);
+    P.nc = cdiv(nblocks, P.nblk);
+    P.n_items_a = tiles * P.ks;
+    P.n_items_b = tiles * P.nc;
+    P.grid = P.n_items_a + P.n_items_b;
+  } else if (4 * tiles <= cus && dev.xccs == 8 && xcd_remap_enabled(true)) {
+    // small batch: each tile's shrink is split along k into parts and its
+    // expand into column chunks, all on one XCD, so the parts reach the
+    // expands with plain accesses through that XCD's L2 (the item order
+    // assumes 8 XCDs). About two workgroups per CU.
+    P.mode = kModeFusedDep;
+    const int per_xcd_tiles = (tiles + 7) / 8;
+    const int slots_per_xcd = 2 * cus / 8;
+    int ks = std::max(1, std::min({kMaxKs, cdiv(c.K, 512), kMaxPartials / tiles}));
+    P.kchunk = round_up(cdiv(c.K, ks), 64);
+    P.ks = cdiv(c.K, P.kchunk);
+    const int nc = std::max(1, std::min(nblocks, slots_per_xcd / per_xcd_tiles - P.ks));
+    P.nblk = cdiv(nblocks, nc);
+    P.nc = cdiv(nblocks, P.nblk);
+    P.n_items_a = tiles * P.ks;
+    P.n_items_b = tiles * P.nc;
+    P.xcd_local = 1;
+    P.grid = local_grid(tiles, P.ks, P.nc);
+  } else if (4 * tiles <= cus) {
+    // small batch without the XCD-local layout: each item computes its
+    // tile's full shrink on chip and one column chunk of the expand
+    P.mode = kModeFusedTile;
+    P.ks = 1;
+    P.kchunk = round_up(c.K, 64);
+    P.nblk = cdiv(nblocks, std::max(1, std::min(nblocks, cus / tiles)));
+    P.nc = cdiv(nblocks, P.nblk);
+    P.n_items_a = tiles * P.nc;
+    P.grid = P.n_items_a;
+  } else if (tiles >= 2 * cus || 2 * tiles > kMaxPartials) {
+    // the tiles alone fill every resident slot: keep u on chip, one item
+    // per tile (measured on the packed-training forward, 2048 tiles:
+    // 318 us, against 356 us with one shrink and two expand items per tile)
+    P.mode = kModeFusedTile;
+    P.ks = 1;
+    P.kchunk = round_up(c.K, 64);
+    P.nc = 1;
+    P.nblk = nblocks;
+    P.n_items_a = tiles;
+    P.xcd_remap = xcd_remap_enabled(false) ? 1 : 0;
+    P.grid = P.xcd_remap ? round_up(tiles, 8) : tiles;
+  } else {
+    // medium batch: each tile's shrink in one or two k-parts and its
+    // expand in column items of about kExpandBlocks 32-column blocks (at
+    // least about three workgroups per CU in all) that wait for the
+    // parts, so every CU has work without repeating the shrink. Measured
+    // (prefill 8192 tok 4096->4096: 64 -> 56 us; MLP-up 4096 tok
+    // 4096->14336: 105 -> 85 us) against one item per tile and against
+    // narrower expand items.
+    P.mode = kModeFusedDep;
+    const int ks = c.K >= 2048 ? 2 : 1;
+    P.kchunk = round_up(cdiv(c.K, ks), 64);
+    P.ks = cdiv(c.K, P.kchunk);
+    int nc = std::max({2, (nblocks + kExpandBlocks / 2) / kExpandBlocks, 3 * cus / tiles - 1});
+    // a multiple of 8 column items per tile puts column chunk c of every
+    // tile on one XCD (workgroup b runs on XCD b % 8), so the tiles of an
+    // adapter re-read that chunk's expand-weight slice from one L2
+    // (MLP-up 4096 tok, 32 adapters r8..r128: 8 items 85 us, 9 items 88 us)
+    if (nc >= 6) nc = std::max(8, (nc + 4) / 8 * 8);
+    nc = std::min(nblocks, nc);
+    P.nblk = cdiv(nblocks, nc);
+    P.nc = cdiv(nblocks, P.nblk);
+    P.n_items_a = tiles * P.ks;
+    P.n_items_b = tiles * P.nc;
+    P.grid = P.n_items_a + P.n_items_b;
+  }
 }
 
 int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int>& slot_of,
@@ -521,117 +640,9 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
       P.n_items_a = tiles * P.nc;
       P.grid = P.n_items_a;
     } else {
-      const ForcePlan fp = force_plan();
-      if (fp.mode == kModeFusedTile) {
-        P.mode = kModeFusedTile;
-        P.ks = 1;
-        P.kchunk = round_up(c.K, 64);
-        P.nblk = cdiv(nblocks, std::min(fp.nc, nblocks));
-        P.nc = cdiv(nblocks, P.nblk);
-        P.n_items_a = tiles * P.nc;
-        P.xcd_remap = xcd_remap_enabled(false) ? 1 : 0;
-        P.grid = P.xcd_remap ? round_up(P.n_items_a, 8) : P.n_items_a;
-      } else if (fp.mode == kModeFusedDep && fp.ks <= kMaxKs && tiles * fp.ks <= kMaxPartials) {
-        P.mode = kModeFusedDep;
-        P.kchunk = round_up(cdiv(c.K, fp.ks), 64);
-        P.ks = cdiv(c.K, P.kchunk);
-        P.nblk = cdiv(nblocks, std::min(fp.nc, nblocks));
-        P.nc = cdiv(nblocks, P.nblk);
-        P.n_items_a = tiles * P.ks;
-        P.n_items_b = tiles * P.nc;
-        P.xcd_local = fp.local && dev.xccs == 8 ? 1 : 0;
-        P.grid = P.xcd_local ? local_grid(tiles, P.ks, P.nc) : P.n_items_a + P.n_items_b;
-        if (fp.spin >= 0) P.spin_ticks = fp.spin;
-      } else if (4 * tiles <= cus && expand_heavy(c, segs, base, ns, n_widest)) {
-        // small batch whose expand moves far more bytes than its shrink
-        // (e.g. an MLP-up projection): the split layout with the items of
-        // every tile spread over all XCDs, so that the expand's y and weight
-        // traffic is shared by every XCD's L2 and fabric port rather than
-        // concentrated on the XCDs that hold two tiles; the parts go through
-        // device-scope stores and loads. Parts of about 320 columns, at most
-        // as many as one batch of the expand's part loads takes (8, 4, 2
-        // for rank <= 32, 64, 128), and the expand items of each tile fill
-        // about two workgroups per CU. (Measured on the decode gate_up
-        // projection, 2560 -> 19456 with 11 tiles: 16.8 us against 18.7 us
-        // for the XCD-local layout; parts of 256 columns: 19.1-19.9 us.)
-        P.mode = kModeFusedDep;
-        int rmax_l = 0;
-        for (int i = 0; i < ns; ++i) rmax_l = std::max(rmax_l, (int)P.seg_rank[i]);
-        const int rb = rmax_l <= 32 ? 1 : (rmax_l <= 64 ? 2 : 4);
-        int ks = std::max(1, std::min({8 / rb, cdiv(c.K, 320), kMaxPartials / tiles}));
-        P.kchunk = round_up(cdiv(c.K, ks), 64);
-        P.ks = cdiv(c.K, P.kchunk);
-        const int nc = std::max(1, std::min(nblocks, slots / tiles - P.ks));
-        P.nblk = cdiv(nblocks, nc);
-        P.nc = cdiv(nblocks, P.nblk);
-        P.n_items_a = tiles * P.ks;
-        P.n_items_b = tiles * P.nc;
-        P.grid = P.n_items_a + P.n_items_b;
-      } else if (4 * tiles <= cus && dev.xccs == 8 && xcd_remap_enabled(true)) {
-        // small batch: each tile's shrink is split along k into parts and its
-        // expand into column chunks, all on one XCD, so the parts reach the
-        // expands with plain accesses through that XCD's L2 (the item order
-        // assumes 8 XCDs). About two workgroups per CU.
-        P.mode = kModeFusedDep;
-        const int per_xcd_tiles = (tiles + 7) / 8;
-        const int slots_per_xcd = 2 * cus / 8;
-        int ks = std::max(1, std::min({kMaxKs, cdiv(c.K, 512), kMaxPartials / tiles}));
-        P.kchunk = round_up(cdiv(c.K, ks), 64);
-        P.ks = cdiv(c.K, P.kchunk);
-        const int nc = std::max(1, std::min(nblocks, slots_per_xcd / per_xcd_tiles - P.ks));
-        P.nblk = cdiv(nblocks, nc);
-        P.nc = cdiv(nblocks, P.nblk);
-        P.n_items_a = tiles * P.ks;
-        P.n_items_b = tiles * P.nc;
-        P.xcd_local = 1;
-        P.grid = local_grid(tiles, P.ks, P.nc);
-      } else if (4 * tiles <= cus) {
-        // small batch without the XCD-local layout: each item computes its
-        // tile's full shrink on chip and one column chunk of the expand
-        P.mode = kModeFusedTile;
-        P.ks = 1;
-        P.kchunk = round_up(c.K, 64);
-        P.nblk = cdiv(nblocks, std::max(1, std::min(nblocks, cus / tiles)));
-        P.nc = cdiv(nblocks, P.nblk);
-        P.n_items_a = tiles * P.nc;
-        P.grid = P.n_items_a;
-      } else if (tiles >= 2 * cus || 2 * tiles > kMaxPartials) {
-        // the tiles alone fill every resident slot: keep u on chip, one item
-        // per tile (measured on the packed-training forward, 2048 tiles:
-        // 318 us, against 356 us with one shrink and two expand items per tile)
-        P.mode = kModeFusedTile;
-        P.ks = 1;
-        P.kchunk = round_up(c.K, 64);
-        P.nc = 1;
-        P.nblk = nblocks;
-        P.n_items_a = tiles;
-        P.xcd_remap = xcd_remap_enabled(false) ? 1 : 0;
-        P.grid = P.xcd_remap ? round_up(tiles, 8) : tiles;
-      } else {
-        // medium batch: each tile's shrink in one or two k-parts and its
-        // expand in column items of about kExpandBlocks 32-column blocks (at
-        // least about three workgroups per CU in all) that wait for the
-        // parts, so every CU has work without repeating the shrink. Measured
-        // (prefill 8192 tok 4096->4096: 64 -> 56 us; MLP-up 4096 tok
-        // 4096->14336: 105 -> 85 us) against one item per tile and against
-        // narrower expand items.
-        P.mode = kModeFusedDep;
-        const int ks = c.K >= 2048 ? 2 : 1;
-        P.kchunk = round_up(cdiv(c.K, ks), 64);
-        P.ks = cdiv(c.K, P.kchunk);
-        int nc = std::max({2, (nblocks + kExpandBlocks / 2) / kExpandBlocks, 3 * cus / tiles - 1});
-        // a multiple of 8 column items per tile puts column chunk c of every
-        // tile on one XCD (workgroup b runs on XCD b % 8), so the tiles of an
-        // adapter re-read that chunk's expand-weight slice from one L2
-        // (MLP-up 4096 tok, 32 adapters r8..r128: 8 items 85 us, 9 items 88 us)
-        if (nc >= 6) nc = std::max(8, (nc + 4) / 8 * 8);
-        nc = std::min(nblocks, nc);
-        P.nblk = cdiv(nblocks, nc);
-        P.nc = cdiv(nblocks, P.nblk);
-        P.n_items_a = tiles * P.ks;
-        P.n_items_b = tiles * P.nc;
-        P.grid = P.n_items_a + P.n_items_b;
-      }
+      int rmax_l = 0;
+      for (int i = 0; i < ns; ++i) rmax_l = std::max(rmax_l, (int)P.seg_rank[i]);
+      fused_layout(P, c, tiles, rmax_l, nblocks, dev);
     }
     if (P.grid <= 0) continue;
     if (c.n_proj > 1) {
@@ -1288,6 +1299,134 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
                               ws, ws_bytes, launcher);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Batches planned on the device (graph-capturable decode)
+// ---------------------------------------------------------------------------
+namespace {
+
+struct GraphLayout {
+  size_t counters = 0, partials = 0, tiles = 0, hdr = 0, perm = 0, total = 0;
+  int max_tiles = 0;
+};
+
+// Workspace of lora_sgmv_fused_graph: hand-off words, split-shrink parts for
+// the largest tile count the batch can have (each adapter adds at most one
+// ragged tile), the tile table, a 256-byte header (tile count at +0, the
+// epoch at +8) and the sorted-position -> row table.
+GraphLayout graph_layout(const lora_graph_adapters_t* a, int T) {
+  GraphLayout L;
+  L.max_tiles = std::max(1, cdiv(T, kTileM) + std::min(a->num_adapters, T));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (off + bytes + 255) / 256 * 256;
+    return o;
+  };
+  L.counters = take(kCounterBytes);
+  const int64_t parts = std::min<int64_t>(kMaxPartials, (int64_t)L.max_tiles * kMaxKs);
+  L.partials = take((size_t)parts * kTileM * rpad_for(a->max_rank) * sizeof(float));
+  L.tiles = take((size_t)L.max_tiles * sizeof(DevTile));
+  L.hdr = take(256);
+  L.perm = take((size_t)std::max(T, 1) * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+int check_graph_adapters(const lora_graph_adapters_t* a) {
+  if (!a) return fail(LORA_INVALID_ARGUMENT, "adapters is NULL");
+  if (a->num_adapters < 1 || a->num_adapters > kMaxGraphAdapters)
+    return fail(LORA_INVALID_ARGUMENT, "num_adapters must be in [1, %d]", kMaxGraphAdapters);
+  if (a->h_in <= 0 || a->h_out <= 0 || (a->h_in & 7) || (a->h_out & 7))
+    return fail(LORA_INVALID_ARGUMENT, "h_in (%d) and h_out (%d) must be positive multiples of 8", a->h_in,
+                a->h_out);
+  if (a->max_rank < 1) return fail(LORA_INVALID_ARGUMENT, "max_rank must be >= 1");
+  if (a->max_rank > LORA_MAX_RANK) return fail(LORA_UNSUPPORTED, "max_rank %d exceeds %d", a->max_rank, LORA_MAX_RANK);
+  if (!a->A_ptrs || !a->B_ptrs || !a->ranks || !a->scales)
+    return fail(LORA_INVALID_ARGUMENT, "A_ptrs/B_ptrs/ranks/scales device arrays must not be NULL");
+  return LORA_OK;
+}
+
+int sgmv_fused_graph_impl(const void* x, int64_t ldx, const lora_graph_adapters_t* a, const int32_t* token_ids,
+                          int32_t T, void* y, int64_t ldy, void* ws, size_t ws_bytes, Launcher& launcher) {
+  int st = check_graph_adapters(a);
+  if (st) return st;
+  if (T < 0) return fail(LORA_INVALID_ARGUMENT, "num_tokens must be >= 0");
+  if (T == 0) return LORA_OK;
+  if (!token_ids) return fail(LORA_INVALID_ARGUMENT, "token_ids is NULL");
+  if ((st = check_rows(x, ldx, a->h_in, "x", true))) return st;
+  if ((st = check_rows(y, ldy, a->h_out, "y", true))) return st;
+  // the rows are request rows 0 .. T-1, reached through the in-kernel gather
+  lora_segments_t rows{T, 0, nullptr, nullptr, reinterpret_cast<const int32_t*>(1)};
+  if ((st = check_gather(&rows, ldx, a->h_in, "x", true))) return st;
+  if ((st = check_gather(&rows, ldy, a->h_out, "y", true))) return st;
+  if (x == y) return fail(LORA_INVALID_ARGUMENT, "x and y must not overlap");
+  const GraphLayout G = graph_layout(a, T);
+  if ((st = check_ws(ws, ws_bytes, G.total))) return st;
+  char* wsb = static_cast<char*>(ws);
+  DevPlanArgs D{};
+  D.ids = token_ids;
+  D.A_ptrs = a->A_ptrs; D.B_ptrs = a->B_ptrs; D.ranks = a->ranks; D.scales = a->scales;
+  D.perm = reinterpret_cast<int32_t*>(wsb + G.perm);
+  D.tiles = reinterpret_cast<DevTile*>(wsb + G.tiles);
+  D.count = reinterpret_cast<int32_t*>(wsb + G.hdr);
+  D.epoch = reinterpret_cast<uint64_t*>(wsb + G.hdr + 8);
+  D.T = T; D.N = a->num_adapters; D.max_rank = a->max_rank; D.max_tiles = G.max_tiles;
+  hipError_t e = launcher.dev_plan(D);
+  if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "plan kernel launch failed: %s", hipGetErrorString(e));
+  // the fused launch is laid out for the largest tile count; tiles past the
+  // count the plan kernel writes have no work
+  FwdCall c{};
+  c.mode_op = LORA_OP_FUSED;
+  c.K = a->h_in; c.N = a->h_out;
+  FwdPlan P;
+  std::memset(&P, 0, sizeof(P));
+  P.X = static_cast<const uint16_t*>(x); P.ldx = ldx;
+  P.Y = static_cast<uint16_t*>(y); P.ldy = ldy;
+  P.token_rows = D.perm;
+  P.partials = reinterpret_cast<float*>(wsb + G.partials);
+  P.counters = reinterpret_cast<int32_t*>(wsb + G.counters);
+  P.stamps = reinterpret_cast<uint64_t*>(wsb + G.counters + kStampOffset);
+  P.dev_tiles = D.tiles; P.dev_count = D.count; P.dev_epoch = D.epoch;
+  P.ptrs_in_plan = 1;
+  P.K = a->h_in; P.N = a->h_out; P.v_round = 1;
+  P.rpad = rpad_for(a->max_rank);
+  P.n_seg = 0;
+  P.n_tiles = G.max_tiles;
+  const DeviceInfo dev = launcher.dev();
+  P.spin_ticks = (int)std::min<int64_t>((int64_t)dev.wall_khz * 1000 / 5000, 1 << 30);
+  fused_layout(P, c, G.max_tiles, a->max_rank, cdiv(a->h_out, 32), dev);
+  if (P.mode == kModeFusedDep && (int64_t)G.max_tiles * P.ks > kMaxPartials)
+    return fail(LORA_UNSUPPORTED, "batch too large for the split layout of a device-planned call");
+  const int rbmax = a->max_rank <= 32 ? 1 : (a->max_rank <= 64 ? 2 : 4);
+  e = launcher.fwd(P, rbmax, nullptr, nullptr);
+  if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
+  return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_workspace_size_graph(const lora_graph_adapters_t* adapters, int32_t num_tokens, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(LORA_INVALID_ARGUMENT, "bytes is NULL");
+  int st = check_graph_adapters(adapters);
+  if (st) return st;
+  if (num_tokens < 0) return fail(LORA_INVALID_ARGUMENT, "num_tokens must be >= 0");
+  *bytes = graph_layout(adapters, num_tokens).total;
+  return LORA_OK;
+}
+
+int lora_sgmv_fused_graph(const void* x, int64_t ldx, const lora_graph_adapters_t* adapters,
+                          const int32_t* token_ids, int32_t num_tokens, void* y, int64_t ldy, void* ws,
+                          size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  HipLauncher launcher(stream);
+  return sgmv_fused_graph_impl(x, ldx, adapters, token_ids, num_tokens, y, ldy, ws, ws_bytes, launcher);
+}
+
 // ---------------------------------------------------------------------------
 // Host-only plan inspection (lora_inspect.h)
 // ---------------------------------------------------------------------------
@@ -1380,6 +1519,20 @@ struct Recorder final : Launcher {
       r.part = P.job_part[j]; r.aux = P.job_accum[j];
       put(r);
     }
+    return hipSuccess;
+  }
+  hipError_t dev_plan(const DevPlanArgs& a) override {
+    lora_plan_item_t r{};
+    r.launch = launches++;
+    r.phase = LORA_PHASE_PLAN;
+    r.block = 0;
+    r.grid = 1;
+    r.kind = 0;
+    r.tile = -1;
+    r.adapter = -1;
+    r.ntok = a.T;
+    r.hi = a.max_tiles;
+    put(r);
     return hipSuccess;
   }
   hipError_t reduce(const WgradReducePlan& R) override {

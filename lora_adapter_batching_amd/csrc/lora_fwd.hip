@@ -59,6 +59,30 @@ template <typename PT>
 __device__ __forceinline__ TileInfo tile_info(const PT& P, int g, TileInfo* lds) {
   constexpr int CAP = PlanCap<PT>::v;
   if constexpr (CAP <= kSmallSeg) {
+    if (P.dev_tiles) {
+      // planned on the device: the plan kernel of this call wrote the tile
+      // table before the launch (a tile past its count is empty)
+      const int n = *P.dev_count;
+      const DevTile* d = P.dev_tiles + g;
+      TileInfo t;
+      t.g = g;
+      t.p0 = d->tok0;
+      t.cnt = g < n ? d->cnt : 0;
+      t.adapter = d->adapter;
+      t.rank = d->rank;
+      t.slot = 0;
+      t.proj = 0;
+      t.scale = d->scale;
+      t.wptr = d->wptr;
+      t.vptr = d->vptr;
+      t.g = __builtin_amdgcn_readfirstlane(t.g);
+      t.p0 = __builtin_amdgcn_readfirstlane(t.p0);
+      t.cnt = __builtin_amdgcn_readfirstlane(t.cnt);
+      t.adapter = __builtin_amdgcn_readfirstlane(t.adapter);
+      t.rank = __builtin_amdgcn_readfirstlane(t.rank);
+      t.scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t.scale)));
+      return t;
+    }
     int sel = 0;
 #pragma unroll
     for (int i = 1; i < CAP; ++i)
@@ -881,6 +905,14 @@ __device__ __forceinline__ uint32_t xcc_id() {
 }
 constexpr int kAuxDev = 16;  // sc1: device scope
 
+// The id that stamps this launch's parts: from the host, or (batches planned
+// on the device) from the workspace epoch the plan kernel has just advanced.
+__device__ __forceinline__ uint64_t launch_id(const FwdHeader& P) {
+  if (P.dev_epoch) return __builtin_amdgcn_readfirstlane((uint32_t)*P.dev_epoch) |
+                          ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(*P.dev_epoch >> 32)) << 32);
+  return P.launch_id;
+}
+
 template <typename PT>
 __device__ __forceinline__ float* partial_ptr(const PT& P, int g, int c) {
   return P.partials + ((int64_t)g * P.ks + c) * kTileM * P.rpad;
@@ -977,7 +1009,7 @@ __device__ __forceinline__ void item_shrink(const PT& P, const Lds& L, const Til
     wait_vmcnt<0>();  // this thread's part stores have been performed
     __syncthreads();  // ... and every thread's
     if (threadIdx.x == 0) {
-      const uint64_t stamp = (P.launch_id << 8) | xcc_id();
+      const uint64_t stamp = (launch_id(P) << 8) | xcc_id();
       __hip_atomic_store(P.stamps + (t.g * P.ks + c), stamp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
@@ -1018,7 +1050,7 @@ __device__ __forceinline__ bool wait_and_sum_parts(const PT& P, const Lds& L, co
     // lane q < ks watches the stamp of part q
     const bool mine = lane < P.ks;
     const int idx = t.g * P.ks + (mine ? lane : 0);
-    const uint64_t want = P.launch_id;
+    const uint64_t want = launch_id(P);
     const uint32_t here = xcc_id();
     const uint64_t t0 = wall_clock64();
     bool ready = false, trusted = true;
@@ -1131,6 +1163,7 @@ __global__ __launch_bounds__(kThreads, 2) void sgmv_fwd_kernel(PT P) {
   const int g = it.g, c = it.c, kind = it.kind;
   if (g >= 0) {
     const TileInfo t = tile_info(P, g, L.ti);
+    if (t.cnt <= 0) return;  // a tile past the count of a batch planned on the device
     if (RBMAX == 1 || t.rank <= 32) run_item<1>(P, L, t, kind, c);
     else if (RBMAX == 2 || t.rank <= 64) run_item<(RBMAX >= 2 ? 2 : 1)>(P, L, t, kind, c);
     else run_item<RBMAX>(P, L, t, kind, c);
@@ -1172,6 +1205,114 @@ hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream, const uin
     return launch_fwd_t(Q, rbmax, stream);
   }
   return launch_fwd_t(P, rbmax, stream);
+}
+
+}  // namespace lora
+
+namespace lora {
+
+// ---------------------------------------------------------------------------
+// Device-side planning (one workgroup): groups a request-order batch into
+// per-adapter segments with a stable counting sort (adapters in id order,
+// the tokens of an adapter in request order, tokens without an active adapter
+// last), cuts the segments into 32-token tiles and advances the workspace
+// epoch that stamps the following launch's hand-off. An adapter is active if
+// its rank is in [1, max_rank] and both weight addresses are set; ids outside
+// [0, N) and tokens of inactive adapters are left out of every tile.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kPlanThreads) void dev_plan_kernel(DevPlanArgs a) {
+  __shared__ int cnt[kMaxGraphAdapters + 1];
+  __shared__ int start[kMaxGraphAdapters + 1];
+  __shared__ int tile0[kMaxGraphAdapters + 1];
+  __shared__ int wave_cnt[kPlanThreads / 64][kMaxGraphAdapters + 1];
+  __shared__ int act[kMaxGraphAdapters];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = a.N;
+  const uint64_t epoch0 = tid == 0 ? *a.epoch : 0;
+  for (int i = tid; i <= N; i += kPlanThreads) cnt[i] = 0;
+  for (int i = tid; i < N; i += kPlanThreads) {
+    const int r = a.ranks[i];
+    act[i] = (r >= 1 && r <= a.max_rank && a.A_ptrs[i] != 0 && a.B_ptrs[i] != 0) ? 1 : 0;
+  }
+  __syncthreads();
+  auto key_of = [&](int t) {
+    const int id = a.ids[t];
+    return (id >= 0 && id < N && act[id]) ? id : N;
+  };
+  // pass 1: tokens per key
+  for (int t = tid; t < a.T; t += kPlanThreads) atomicAdd(&cnt[key_of(t)], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int s = 0, nt = 0;
+    for (int i = 0; i <= N; ++i) {
+      start[i] = s;
+      tile0[i] = nt;
+      s += cnt[i];
+      if (i < N) nt += (cnt[i] + kTileM - 1) / kTileM;
+    }
+    *a.count = min(nt, a.max_tiles);
+    *a.epoch = epoch0 + 1;
+  }
+  __syncthreads();
+  // tiles, one adapter per thread
+  for (int i = tid; i < N; i += kPlanThreads) {
+    const int c = cnt[i];
+    if (c == 0) continue;
+    const int r = a.ranks[i];
+    const float sc = a.scales[i];
+    const uint64_t w = a.A_ptrs[i], v = a.B_ptrs[i];
+    for (int j = 0; j < c; j += kTileM) {
+      const int g = tile0[i] + j / kTileM;
+      if (g >= a.max_tiles) break;
+      DevTile d;
+      d.tok0 = start[i] + j;
+      d.cnt = min(kTileM, c - j);
+      d.adapter = i;
+      d.rank = r;
+      d.scale = sc;
+      d.pad = 0;
+      d.wptr = w;
+      d.vptr = v;
+      a.tiles[g] = d;
+    }
+  }
+  // pass 2: stable positions, a chunk of kPlanThreads tokens at a time. Within
+  // a wave, the lanes of one key are ranked by lane order; the waves of a
+  // chunk follow in order; earlier chunks come first.
+  for (int c0 = 0; c0 < a.T; c0 += kPlanThreads) {
+    for (int i = lane; i <= N; i += 64) wave_cnt[wave][i] = 0;
+    const int t = c0 + tid;
+    const int key = t < a.T ? key_of(t) : -1;
+    int rank_in_wave = 0;
+    uint64_t todo = __builtin_amdgcn_ballot_w64(key >= 0);
+    while (todo) {
+      const int leader = __builtin_ctzll(todo);
+      const int k = __builtin_amdgcn_readlane(key, leader);
+      const uint64_t m = __builtin_amdgcn_ballot_w64(key == k);
+      if (key == k) rank_in_wave = __builtin_popcountll(m & ((1ull << lane) - 1ull));
+      if (lane == leader) wave_cnt[wave][k] = __builtin_popcountll(m);
+      todo &= ~m;
+    }
+    __syncthreads();
+    // per key: the waves' offsets in order (one thread per key)
+    for (int k = tid; k <= N; k += kPlanThreads) {
+      int s = start[k];
+      for (int w = 0; w < kPlanThreads / 64; ++w) {
+        const int n = wave_cnt[w][k];
+        wave_cnt[w][k] = s;
+        s += n;
+      }
+      start[k] = s;
+    }
+    __syncthreads();
+    if (key >= 0) a.perm[wave_cnt[wave][key] + rank_in_wave] = t;
+    __syncthreads();
+  }
+}
+
+hipError_t launch_dev_plan(const DevPlanArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(dev_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace lora

@@ -23,7 +23,13 @@
 extern "C" {
 #endif
 
-enum { LORA_PHASE_FWD = 0, LORA_PHASE_WGRAD = 1, LORA_PHASE_REDUCE = 2, LORA_PHASE_TRANSPOSE = 3 };
+enum {
+  LORA_PHASE_FWD = 0,
+  LORA_PHASE_WGRAD = 1,
+  LORA_PHASE_REDUCE = 2,
+  LORA_PHASE_TRANSPOSE = 3,
+  LORA_PHASE_PLAN = 4 /* device planning of a graph call (one workgroup) */
+};
 
 /* Options of lora_inspect_plan(). */
 #define LORA_INSPECT_WITH_U 1u     /* fused: u_save given; backward: u given (else recomputed) */

@@ -38,6 +38,19 @@ enum FwdMode : int32_t {
 constexpr int kCtrTiles = 64;        // per-tile arrival counters start here
 constexpr int kStampOffset = 4096;   // bytes from the counters to the stamps
 
+// One 32-token tile of a batch planned on the device (lora_sgmv_fused_graph):
+// written by the plan kernel into the workspace, read by the fused kernel.
+struct DevTile {
+  int32_t tok0;     // first sorted position
+  int32_t cnt;      // tokens (1..32)
+  int32_t adapter;
+  int32_t rank;
+  float scale;
+  int32_t pad;
+  uint64_t wptr;    // shrink weight A_i
+  uint64_t vptr;    // expand weight B_i
+};
+
 struct FwdHeader {
   const uint16_t* X;  // shrink input rows, bf16 (x forward, dy backward)
   int64_t ldx;
@@ -76,6 +89,12 @@ struct FwdHeader {
   int32_t grid;         // launched workgroups
   int32_t spin_ticks;   // wall-clock ticks an expand waits before computing the shrink itself
   int32_t ptrs_in_plan; // small plans: weight addresses are in seg_wptr / seg_vptr
+  // Batches planned on the device: the tiles, their count and the launch id
+  // come from the workspace (written by the plan kernel just before), and
+  // n_tiles above is only the bound the grid was laid out for. Null otherwise.
+  const DevTile* dev_tiles;
+  const int32_t* dev_count;
+  const uint64_t* dev_epoch;
   // Projections 1 .. kMaxProj-1 of a multi-projection launch (several
   // LoRA-wrapped projections over the same x); projection 0 uses Y, ldy, N,
   // nblk, Wtab and Vtab above, and entry 0 of these arrays is unused.
@@ -187,6 +206,27 @@ __host__ __device__ inline int wgrad_kb(int rank) {
   return k <= 1 ? 1 : (k <= 2 ? 2 : (k <= 4 ? 4 : 8));
 }
 __host__ __device__ inline int wgrad_cw(int rank) { return 4 * 16 * wgrad_qn(wgrad_kb(rank)); }
+
+// Device-side planning of a request-order batch (lora_sgmv_fused_graph): a
+// stable counting sort of the token ids into per-adapter segments, their
+// 32-token tiles, and the launch id of the call.
+constexpr int kMaxGraphAdapters = 256;
+constexpr int kPlanThreads = 1024;
+struct DevPlanArgs {
+  const int32_t* ids;       // DEVICE [T] adapter id per token (request order)
+  const uint64_t* A_ptrs;   // DEVICE [N]
+  const uint64_t* B_ptrs;   // DEVICE [N]
+  const int32_t* ranks;     // DEVICE [N]
+  const float* scales;      // DEVICE [N]
+  int32_t* perm;            // [T] sorted position -> request row (adapter order, request order within)
+  DevTile* tiles;           // [max_tiles]
+  int32_t* count;           // [1] tiles written
+  uint64_t* epoch;          // [1] launch id: incremented by every plan
+  int32_t T;
+  int32_t N;
+  int32_t max_rank;         // adapters whose rank is outside [1, max_rank] are skipped
+  int32_t max_tiles;
+};
 
 // Weight-gradient launch: items are (job, kind, column chunk); a job is one
 // adapter (or part of its segments) whose token reduction the item owns.

@@ -35,7 +35,8 @@ def test_binding_structs_match_the_c_header(tmp_path):
     if cc is None:
         pytest.skip("no C compiler")
     checks = []
-    for cname, py in (("lora_adapters_t", B.CAdapters), ("lora_segments_t", B.CSegments)):
+    for cname, py in (("lora_adapters_t", B.CAdapters), ("lora_segments_t", B.CSegments),
+                      ("lora_graph_adapters_t", B.CGraphAdapters)):
         checks.append((cname, "sizeof", f"sizeof({cname})", ctypes.sizeof(py)))
         for f, _ in py._fields_:
             checks.append((cname, f, f"offsetof({cname}, {f})", getattr(py, f).offset))
@@ -299,3 +300,37 @@ def test_noalloc_refuses_batches_beyond_its_static_scratch():
     # argument errors come first, as for lora_sgmv_fused
     assert lib.lora_sgmv_fused_noalloc(0, 4096, ctypes.byref(ad), ctypes.byref(sg), FAKE, 4096, 0, 0, 0) \
         == B.LORA_INVALID_ARGUMENT
+
+
+def test_graph_call_validation():
+    """lora_sgmv_fused_graph / lora_workspace_size_graph check their host
+    arguments before any HIP call (a zero-byte workspace stops a valid call
+    at the workspace check, so nothing reaches the GPU here)."""
+    lib = L.load()
+
+    def ga(N=8, h_in=64, h_out=32, max_rank=32, tabs=FAKE):
+        return B.CGraphAdapters(N, h_in, h_out, max_rank, tabs, tabs, tabs, tabs)
+
+    def call(a, T=16, x=FAKE, ldx=64, y=FAKE + (1 << 24), ldy=32, ids=FAKE, wsb=0):
+        return lib.lora_sgmv_fused_graph(x, ldx, ctypes.byref(a), ids, T, y, ldy, FAKE, wsb, 0)
+
+    n = ctypes.c_size_t(0)
+    assert lib.lora_workspace_size_graph(ctypes.byref(ga()), 256, ctypes.byref(n)) == 0 and n.value > 0
+    n2 = ctypes.c_size_t(0)
+    assert lib.lora_workspace_size_graph(ctypes.byref(ga()), 16, ctypes.byref(n2)) == 0 and n2.value < n.value
+    assert call(ga()) == B.LORA_WORKSPACE_TOO_SMALL  # every argument valid
+    assert call(ga(), T=0) == B.LORA_OK                # nothing to do
+    assert call(ga(N=0)) == B.LORA_INVALID_ARGUMENT
+    assert call(ga(N=257)) == B.LORA_INVALID_ARGUMENT
+    assert call(ga(max_rank=129)) == B.LORA_UNSUPPORTED
+    assert call(ga(max_rank=0)) == B.LORA_INVALID_ARGUMENT
+    assert call(ga(h_in=60)) == B.LORA_INVALID_ARGUMENT
+    assert call(ga(tabs=0)) == B.LORA_INVALID_ARGUMENT
+    assert call(ga(), T=-1) == B.LORA_INVALID_ARGUMENT
+    assert call(ga(), ids=0) == B.LORA_INVALID_ARGUMENT
+    assert call(ga(), x=FAKE + 2) == B.LORA_INVALID_ARGUMENT
+    assert call(ga(), ldy=16) == B.LORA_INVALID_ARGUMENT
+    assert call(ga(), y=FAKE) == B.LORA_INVALID_ARGUMENT  # y is x
+    # rows 0 .. T-1 must fit the 2 GiB gather window
+    assert call(ga(h_out=19456), T=60000, ldy=19456) == B.LORA_INVALID_ARGUMENT
+    assert "gather limit" in lib.lora_last_error().decode()

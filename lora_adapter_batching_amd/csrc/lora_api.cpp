@@ -409,6 +409,16 @@ bool xcd_remap_enabled(bool small_batch) {
   return env >= 0 ? env == 1 : small_batch;
 }
 
+// Byte budget of dy per backward adapter group (LORA_SGMV_BWD_GROUP_MB; 0:
+// groups limited only by the kMaxSlots adapters a transpose pass holds).
+int64_t bwd_group_bytes() {
+  static const int64_t v = [] {
+    const char* e = std::getenv("LORA_SGMV_BWD_GROUP_MB");
+    return e ? (int64_t)std::atoll(e) << 20 : (int64_t)0;
+  }();
+  return v;
+}
+
 // A launch id that no earlier launch of any process used with the same
 // workspace: split-shrink parts are stamped with it, so a stamp left in the
 // workspace by an earlier call can never be taken for a current one.
@@ -1056,9 +1066,223 @@ static int packed_backward_impl(const void* x, int64_t ldx, const void* dy, int6
     for (const auto& s : segs)
       if (!seen[s.adapter]) { seen[s.adapter] = 1; order.push_back(s.adapter); }
   }
+  // Weight gradients of the adapters marked in `member` (adapters without
+  // tokens among them get zero gradients in overwrite mode).
+  auto run_wgrad = [&](const std::vector<char>& member) -> int {
+    // weight gradients: one job per adapter (several chained jobs if it has
+    // too many segments)
+    struct Job {
+      int adapter, rank, accum;
+      float scale;
+      std::vector<std::pair<int, int>> segs;
+      int part = -1;  // >= 0: a token-range part writing partial slot `part`
+    };
+    std::vector<Job> jobs;
+    std::vector<std::vector<std::pair<int, int>>> per(N);
+    for (const auto& s : segs)
+      if (member[s.adapter]) per[s.adapter].push_back({s.tok0, s.ntok});
+    // Load balance ("Technische Samenvatting: PLoRA" (gist.science),
+    // "Kernelontwerp": balance over heterogeneous adapters): when the jobs
+    // leave at least half of the GPU's resident workgroup slots idle, the
+    // adapters with the longest token walks get their token ranges cut into
+    // parts that run side by side, each into its own partial slot; a reduce
+    // pass adds the parts in slot order, so the result does not depend on
+    // scheduling. Parts go one at a time to the adapter whose part is longest,
+    // while slots and idle workgroup slots last; the split is kept only if it
+    // cuts the longest walk by at least 1.5x (a partial split that leaves an
+    // unsplit adapter as long as before only adds traffic).
+    std::vector<int> nparts(N, 1);
+    {
+      const int slots_gpu = 2 * launcher.dev().cus;
+      int64_t items = 0;
+      std::vector<int> steps(N, 0), it(N, 0);
+      for (int a = 0; a < N; ++a) {
+        if (adapters->ranks[a] == 0 || per[a].empty()) continue;
+        for (auto& p : per[a]) steps[a] += cdiv(p.second, kTileM);
+        it[a] = wgrad_items_for_rank(adapters->ranks[a], adapters->h_in, adapters->h_out);
+        items += it[a];
+      }
+      int free_slots = L.wpart_slots;
+      if (items > 0 && 2 * items <= slots_gpu && free_slots >= 2) {
+        auto part_len = [&](int a) { return cdiv(steps[a], nparts[a]); };
+        int crit0 = 0;
+        for (int a = 0; a < N; ++a) crit0 = std::max(crit0, steps[a]);
+        for (;;) {
+          int best = -1;
+          for (int a = 0; a < N; ++a)
+            if (steps[a] > 0 && (best < 0 || part_len(a) > part_len(best))) best = a;
+          if (best < 0) break;
+          const int np = nparts[best] + 1;
+          const int cost = nparts[best] == 1 ? 2 : 1;  // a split adapter uses a slot per part
+          if ((int)per[best].size() > kMaxJobSeg || steps[best] / np < kSplitMinSteps ||
+              cost > free_slots || items + it[best] > slots_gpu)
+            break;
+          nparts[best] = np;
+          free_slots -= cost;
+          items += it[best];
+        }
+        int crit1 = 0;
+        for (int a = 0; a < N; ++a)
+          if (steps[a] > 0) crit1 = std::max(crit1, part_len(a));
+        if (2 * crit0 < 3 * crit1) std::fill(nparts.begin(), nparts.end(), 1);
+      }
+    }
+    struct Red { int adapter, slot0, nparts; };
+    std::vector<Red> reds;
+    int next_slot = 0;
+    for (int a = 0; a < N; ++a) {
+      if (adapters->ranks[a] == 0 || !member[a]) continue;
+      if (per[a].empty()) {
+        if (!accumulate) jobs.push_back(Job{a, adapters->ranks[a], 0, adapters->scales[a], {}});
+        continue;
+      }
+      if (nparts[a] > 1) {
+        // part p takes 32-token steps [p S / P, (p + 1) S / P) of the adapter's
+        // S steps, in segment order; a segment cut inside keeps whole steps
+        int S = 0;
+        for (auto& p : per[a]) S += cdiv(p.second, kTileM);
+        const int P = nparts[a];
+        reds.push_back(Red{a, next_slot, P});
+        size_t seg = 0;
+        int off = 0;  // tokens of per[a][seg] already given out
+        for (int p = 0; p < P; ++p) {
+          int need = (int)((int64_t)(p + 1) * S / P - (int64_t)p * S / P);
+          Job j{a, adapters->ranks[a], 0, adapters->scales[a], {}, next_slot + p};
+          while (need > 0 && seg < per[a].size()) {
+            const int t0 = per[a][seg].first + off;
+            const int left = per[a][seg].second - off;
+            const int take = std::min(left, need * kTileM);
+            j.segs.push_back({t0, take});
+            need -= cdiv(take, kTileM);
+            off += take;
+            if (off >= per[a][seg].second) { ++seg; off = 0; }
+          }
+          jobs.push_back(std::move(j));
+        }
+        next_slot += P;
+        continue;
+      }
+      for (size_t k = 0; k < per[a].size(); k += kMaxJobSeg) {
+        Job j{a, adapters->ranks[a], (accumulate || k > 0) ? 1 : 0, adapters->scales[a], {}};
+        for (size_t q = k; q < std::min(per[a].size(), k + kMaxJobSeg); ++q) j.segs.push_back(per[a][q]);
+        jobs.push_back(std::move(j));
+      }
+    }
+    // heavy jobs first; continuation jobs of one adapter must land in later launches
+    std::vector<size_t> idx(jobs.size());
+    for (size_t i = 0; i < idx.size(); ++i) idx[i] = i;
+    auto tokens_of = [&](const Job& j) {
+      int64_t n = 0;
+      for (auto& p : j.segs) n += p.second;
+      return n;
+    };
+    std::stable_sort(idx.begin(), idx.end(), [&](size_t p, size_t q) {
+      const Job &a = jobs[p], &b = jobs[q];
+      if (a.accum != b.accum && a.adapter == b.adapter) return a.accum < b.accum;
+      return tokens_of(a) * (int64_t)(a.rank + 16) > tokens_of(b) * (int64_t)(b.rank + 16);
+    });
+    std::vector<int> done(jobs.size(), 0);
+    size_t remaining = jobs.size();
+    while (remaining > 0) {
+      WgradPlan W;
+      std::memset(&W, 0, sizeof(W));
+      W.x = static_cast<const uint16_t*>(x); W.ldx = ldx;
+      W.dy = static_cast<const uint16_t*>(dy); W.lddy = lddy;
+      W.U = Uuse; W.ldu = lduse; W.dU = dU; W.lddu = L.lddu;
+      W.dA_tab = dA_ptrs; W.dB_tab = dB_ptrs; W.token_rows = segments->token_rows;
+      W.h_in = adapters->h_in; W.h_out = adapters->h_out;
+      W.part_base = reinterpret_cast<float*>(wsb + L.wpart);
+      W.part_stride = L.wpart_stride;
+      int nj = 0, nseg = 0, grid = 0;
+      std::vector<int> adapter_in_launch(N, 0);
+      for (size_t ii = 0; ii < idx.size(); ++ii) {
+        const size_t j = idx[ii];
+        if (done[j]) continue;
+        const Job& J = jobs[j];
+        if (nj >= kMaxJobs || nseg + (int)J.segs.size() > kMaxJobSeg) break;
+        if (J.part < 0) {
+          // chained jobs of one adapter: one per launch, in order
+          if (adapter_in_launch[J.adapter]) continue;
+          bool earlier_pending = false;
+          for (size_t q = 0; q < jobs.size(); ++q)
+            if (!done[q] && q != j && jobs[q].adapter == J.adapter && jobs[q].accum < J.accum) earlier_pending = true;
+          if (earlier_pending) continue;
+        }
+        W.job_item0[nj] = grid;
+        W.job_adapter[nj] = J.adapter;
+        W.job_seg0[nj] = nseg;
+        W.job_nseg[nj] = (int)J.segs.size();
+        W.job_nsteps[nj] = 0;
+        for (auto& p : J.segs) W.job_nsteps[nj] += cdiv(p.second, kTileM);
+        W.job_accum[nj] = J.accum;
+        W.job_scale[nj] = J.scale;
+        W.job_rank[nj] = J.rank;
+        W.job_part[nj] = J.part;
+        for (auto& p : J.segs) { W.seg_tok0[nseg] = p.first; W.seg_ntok[nseg] = p.second; ++nseg; }
+        grid += wgrad_items_for_rank(J.rank, adapters->h_in, adapters->h_out);
+        if (J.part < 0) adapter_in_launch[J.adapter] = 1;
+        done[j] = 1;
+        --remaining;
+        ++nj;
+      }
+      if (nj == 0) return fail(LORA_DEVICE_ERROR, "internal planner error (no weight-gradient job placed)");
+      W.n_jobs = nj;
+      W.job_item0[nj] = grid;
+      const hipError_t e = launcher.wgrad(W, grid);
+      if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "weight-gradient launch failed: %s", hipGetErrorString(e));
+    }
+    if (!reds.empty()) {
+      WgradReducePlan R;
+      std::memset(&R, 0, sizeof(R));
+      R.part_base = reinterpret_cast<const float*>(wsb + L.wpart);
+      R.part_stride = L.wpart_stride;
+      R.dA_tab = dA_ptrs; R.dB_tab = dB_ptrs;
+      R.h_in = adapters->h_in; R.h_out = adapters->h_out;
+      R.accumulate = accumulate ? 1 : 0;
+      int grid = 0;
+      for (const Red& r : reds) {
+        const int j = R.n_red++;
+        R.red_item0[j] = grid;
+        R.red_adapter[j] = r.adapter;
+        R.red_rank[j] = adapters->ranks[r.adapter];
+        R.red_slot0[j] = r.slot0;
+        R.red_nparts[j] = r.nparts;
+        grid += (int)cdiv64((int64_t)(adapters->h_in + adapters->h_out) * R.red_rank[j], kReduceElems);
+      }
+      R.red_item0[R.n_red] = grid;
+      const hipError_t e = launcher.reduce(R);
+      if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "weight-gradient reduce launch failed: %s", hipGetErrorString(e));
+    }
+    return LORA_OK;
+  };
+
+  // Adapter groups: at most kMaxSlots adapters, and (with a byte budget set)
+  // at most that many bytes of dy. Each group runs its du/dx pass and then
+  // its weight gradients, so that a group's dy can still be in the
+  // Infinity Cache when the weight-gradient pass reads it a second time.
+  const int64_t budget = bwd_group_bytes();
+  std::vector<int64_t> tok_of(N, 0);
+  for (const auto& s : segs) tok_of[s.adapter] += s.ntok;
+  std::vector<size_t> gstart{0};
+  {
+    int64_t bytes = 0;
+    for (size_t k = 0; k < order.size(); ++k) {
+      const int64_t b = tok_of[order[k]] * (int64_t)adapters->h_out * 2;
+      const size_t n = k - gstart.back();
+      if (n > 0 && (n >= (size_t)kMaxSlots || (budget > 0 && bytes + b > budget))) {
+        gstart.push_back(k);
+        bytes = 0;
+      }
+      bytes += b;
+    }
+    gstart.push_back(order.size());
+  }
+  std::vector<char> has_tokens(N, 0);
+  for (int a : order) has_tokens[a] = 1;
   std::vector<int> slot_of(N, 0);
-  for (size_t g0 = 0; g0 < order.size(); g0 += kMaxSlots) {
-    const int ng = (int)std::min<size_t>(kMaxSlots, order.size() - g0);
+  for (size_t gi = 0; gi + 1 < gstart.size(); ++gi) {
+    const size_t g0 = gstart[gi];
+    const int ng = (int)(gstart[gi + 1] - g0);
     std::vector<int> in_group(N, 0);
     TransposePlan T;
     std::memset(&T, 0, sizeof(T));
@@ -1100,191 +1324,22 @@ static int packed_backward_impl(const void* x, int64_t ldx, const void* dy, int6
     c.token_rows = segments->token_rows;
     c.partials = partials; c.counters = counters; c.rmax = rmax;
     if ((st = run_fwd(c, gsegs, slot_of, launcher))) return st;
+    // the group's weight gradients (the last group also writes the zero
+    // gradients of adapters that have no tokens)
+    const bool last = gi + 2 == gstart.size();
+    std::vector<char> member(N, 0);
+    for (int k = 0; k < ng; ++k) member[order[g0 + k]] = 1;
+    if (last)
+      for (int a2 = 0; a2 < N; ++a2)
+        if (!has_tokens[a2]) member[a2] = 1;
+    if ((st = run_wgrad(member))) return st;
+  }
+  if (order.empty()) {
+    // no tokens at all: only the zero gradients (overwrite mode)
+    std::vector<char> member(N, 1);
+    if ((st = run_wgrad(member))) return st;
   }
 
-  // weight gradients: one job per adapter (several chained jobs if it has
-  // too many segments)
-  struct Job {
-    int adapter, rank, accum;
-    float scale;
-    std::vector<std::pair<int, int>> segs;
-    int part = -1;  // >= 0: a token-range part writing partial slot `part`
-  };
-  std::vector<Job> jobs;
-  std::vector<std::vector<std::pair<int, int>>> per(N);
-  for (const auto& s : segs) per[s.adapter].push_back({s.tok0, s.ntok});
-  // Load balance ("Technische Samenvatting: PLoRA" (gist.science),
-  // "Kernelontwerp": balance over heterogeneous adapters): when the jobs
-  // leave at least half of the GPU's resident workgroup slots idle, the
-  // adapters with the longest token walks get their token ranges cut into
-  // parts that run side by side, each into its own partial slot; a reduce
-  // pass adds the parts in slot order, so the result does not depend on
-  // scheduling. Parts go one at a time to the adapter whose part is longest,
-  // while slots and idle workgroup slots last; the split is kept only if it
-  // cuts the longest walk by at least 1.5x (a partial split that leaves an
-  // unsplit adapter as long as before only adds traffic).
-  std::vector<int> nparts(N, 1);
-  {
-    const int slots_gpu = 2 * launcher.dev().cus;
-    int64_t items = 0;
-    std::vector<int> steps(N, 0), it(N, 0);
-    for (int a = 0; a < N; ++a) {
-      if (adapters->ranks[a] == 0 || per[a].empty()) continue;
-      for (auto& p : per[a]) steps[a] += cdiv(p.second, kTileM);
-      it[a] = wgrad_items_for_rank(adapters->ranks[a], adapters->h_in, adapters->h_out);
-      items += it[a];
-    }
-    int free_slots = L.wpart_slots;
-    if (items > 0 && 2 * items <= slots_gpu && free_slots >= 2) {
-      auto part_len = [&](int a) { return cdiv(steps[a], nparts[a]); };
-      int crit0 = 0;
-      for (int a = 0; a < N; ++a) crit0 = std::max(crit0, steps[a]);
-      for (;;) {
-        int best = -1;
-        for (int a = 0; a < N; ++a)
-          if (steps[a] > 0 && (best < 0 || part_len(a) > part_len(best))) best = a;
-        if (best < 0) break;
-        const int np = nparts[best] + 1;
-        const int cost = nparts[best] == 1 ? 2 : 1;  // a split adapter uses a slot per part
-        if ((int)per[best].size() > kMaxJobSeg || steps[best] / np < kSplitMinSteps ||
-            cost > free_slots || items + it[best] > slots_gpu)
-          break;
-        nparts[best] = np;
-        free_slots -= cost;
-        items += it[best];
-      }
-      int crit1 = 0;
-      for (int a = 0; a < N; ++a)
-        if (steps[a] > 0) crit1 = std::max(crit1, part_len(a));
-      if (2 * crit0 < 3 * crit1) std::fill(nparts.begin(), nparts.end(), 1);
-    }
-  }
-  struct Red { int adapter, slot0, nparts; };
-  std::vector<Red> reds;
-  int next_slot = 0;
-  for (int a = 0; a < N; ++a) {
-    if (adapters->ranks[a] == 0) continue;
-    if (per[a].empty()) {
-      if (!accumulate) jobs.push_back(Job{a, adapters->ranks[a], 0, adapters->scales[a], {}});
-      continue;
-    }
-    if (nparts[a] > 1) {
-      // part p takes 32-token steps [p S / P, (p + 1) S / P) of the adapter's
-      // S steps, in segment order; a segment cut inside keeps whole steps
-      int S = 0;
-      for (auto& p : per[a]) S += cdiv(p.second, kTileM);
-      const int P = nparts[a];
-      reds.push_back(Red{a, next_slot, P});
-      size_t seg = 0;
-      int off = 0;  // tokens of per[a][seg] already given out
-      for (int p = 0; p < P; ++p) {
-        int need = (int)((int64_t)(p + 1) * S / P - (int64_t)p * S / P);
-        Job j{a, adapters->ranks[a], 0, adapters->scales[a], {}, next_slot + p};
-        while (need > 0 && seg < per[a].size()) {
-          const int t0 = per[a][seg].first + off;
-          const int left = per[a][seg].second - off;
-          const int take = std::min(left, need * kTileM);
-          j.segs.push_back({t0, take});
-          need -= cdiv(take, kTileM);
-          off += take;
-          if (off >= per[a][seg].second) { ++seg; off = 0; }
-        }
-        jobs.push_back(std::move(j));
-      }
-      next_slot += P;
-      continue;
-    }
-    for (size_t k = 0; k < per[a].size(); k += kMaxJobSeg) {
-      Job j{a, adapters->ranks[a], (accumulate || k > 0) ? 1 : 0, adapters->scales[a], {}};
-      for (size_t q = k; q < std::min(per[a].size(), k + kMaxJobSeg); ++q) j.segs.push_back(per[a][q]);
-      jobs.push_back(std::move(j));
-    }
-  }
-  // heavy jobs first; continuation jobs of one adapter must land in later launches
-  std::vector<size_t> idx(jobs.size());
-  for (size_t i = 0; i < idx.size(); ++i) idx[i] = i;
-  auto tokens_of = [&](const Job& j) {
-    int64_t n = 0;
-    for (auto& p : j.segs) n += p.second;
-    return n;
-  };
-  std::stable_sort(idx.begin(), idx.end(), [&](size_t p, size_t q) {
-    const Job &a = jobs[p], &b = jobs[q];
-    if (a.accum != b.accum && a.adapter == b.adapter) return a.accum < b.accum;
-    return tokens_of(a) * (int64_t)(a.rank + 16) > tokens_of(b) * (int64_t)(b.rank + 16);
-  });
-  std::vector<int> done(jobs.size(), 0);
-  size_t remaining = jobs.size();
-  while (remaining > 0) {
-    WgradPlan W;
-    std::memset(&W, 0, sizeof(W));
-    W.x = static_cast<const uint16_t*>(x); W.ldx = ldx;
-    W.dy = static_cast<const uint16_t*>(dy); W.lddy = lddy;
-    W.U = Uuse; W.ldu = lduse; W.dU = dU; W.lddu = L.lddu;
-    W.dA_tab = dA_ptrs; W.dB_tab = dB_ptrs; W.token_rows = segments->token_rows;
-    W.h_in = adapters->h_in; W.h_out = adapters->h_out;
-    W.part_base = reinterpret_cast<float*>(wsb + L.wpart);
-    W.part_stride = L.wpart_stride;
-    int nj = 0, nseg = 0, grid = 0;
-    std::vector<int> adapter_in_launch(N, 0);
-    for (size_t ii = 0; ii < idx.size(); ++ii) {
-      const size_t j = idx[ii];
-      if (done[j]) continue;
-      const Job& J = jobs[j];
-      if (nj >= kMaxJobs || nseg + (int)J.segs.size() > kMaxJobSeg) break;
-      if (J.part < 0) {
-        // chained jobs of one adapter: one per launch, in order
-        if (adapter_in_launch[J.adapter]) continue;
-        bool earlier_pending = false;
-        for (size_t q = 0; q < jobs.size(); ++q)
-          if (!done[q] && q != j && jobs[q].adapter == J.adapter && jobs[q].accum < J.accum) earlier_pending = true;
-        if (earlier_pending) continue;
-      }
-      W.job_item0[nj] = grid;
-      W.job_adapter[nj] = J.adapter;
-      W.job_seg0[nj] = nseg;
-      W.job_nseg[nj] = (int)J.segs.size();
-      W.job_nsteps[nj] = 0;
-      for (auto& p : J.segs) W.job_nsteps[nj] += cdiv(p.second, kTileM);
-      W.job_accum[nj] = J.accum;
-      W.job_scale[nj] = J.scale;
-      W.job_rank[nj] = J.rank;
-      W.job_part[nj] = J.part;
-      for (auto& p : J.segs) { W.seg_tok0[nseg] = p.first; W.seg_ntok[nseg] = p.second; ++nseg; }
-      grid += wgrad_items_for_rank(J.rank, adapters->h_in, adapters->h_out);
-      if (J.part < 0) adapter_in_launch[J.adapter] = 1;
-      done[j] = 1;
-      --remaining;
-      ++nj;
-    }
-    if (nj == 0) return fail(LORA_DEVICE_ERROR, "internal planner error (no weight-gradient job placed)");
-    W.n_jobs = nj;
-    W.job_item0[nj] = grid;
-    const hipError_t e = launcher.wgrad(W, grid);
-    if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "weight-gradient launch failed: %s", hipGetErrorString(e));
-  }
-  if (!reds.empty()) {
-    WgradReducePlan R;
-    std::memset(&R, 0, sizeof(R));
-    R.part_base = reinterpret_cast<const float*>(wsb + L.wpart);
-    R.part_stride = L.wpart_stride;
-    R.dA_tab = dA_ptrs; R.dB_tab = dB_ptrs;
-    R.h_in = adapters->h_in; R.h_out = adapters->h_out;
-    R.accumulate = accumulate ? 1 : 0;
-    int grid = 0;
-    for (const Red& r : reds) {
-      const int j = R.n_red++;
-      R.red_item0[j] = grid;
-      R.red_adapter[j] = r.adapter;
-      R.red_rank[j] = adapters->ranks[r.adapter];
-      R.red_slot0[j] = r.slot0;
-      R.red_nparts[j] = r.nparts;
-      grid += (int)cdiv64((int64_t)(adapters->h_in + adapters->h_out) * R.red_rank[j], kReduceElems);
-    }
-    R.red_item0[R.n_red] = grid;
-    const hipError_t e = launcher.reduce(R);
-    if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "weight-gradient reduce launch failed: %s", hipGetErrorString(e));
-  }
   return LORA_OK;
 }
 

@@ -807,26 +807,106 @@ def bench_only(name, reps=5):
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on the host cores
 # ---------------------------------------------------------------------------
-def bench_cpu(bytes_per_step, budget_s=10.0):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _timed(fn, min_s=0.3, max_reps=20):
+    """Seconds per call of fn (repeated until min_s has passed, at least once)."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s or n >= max_reps:
+            return dt / n
+
+
+def bench_cpu(bytes_per_step, budget_s=6.0):
+    """The fp64 oracle timed on the host cores: the headline decode step (the
+    value, in the metric's unit), then every workload once per thread count
+    (all cores, and one thread for the forward workloads) with its tokens/s
+    and GFLOP/s of algorithmic work."""
     from oracle import oracle
-    from workloads import make_c2_projections
+    from workloads import make_c2_projections, make_config
+    threads_all = oracle.num_threads()
     projs = make_c2_projections(1)
     batches = {k: oracle.Batch(p) for k, p in projs.items()}
-    n = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def decode_step():
         for k in ("q", "o", "gate_up"):
             p = projs[k]
             oracle.segments_from_ids(p.token_ids, p.N)
             batches[k].forward()
+
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        decode_step()
         n += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = (time.perf_counter() - t0) / n
-    return {"value": round(bytes_per_step / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    per_config = []
+
+    def record(name, fn, tokens, bytes_, flops, threads):
+        oracle.set_num_threads(threads)
+        sec = _timed(fn)
+        per_config.append({"workload": name, "threads": threads, "seconds": round(sec, 5),
+                           "tokens_per_s": round(tokens / sec, 1), "GFLOP/s": round(flops / sec / 1e9, 3),
+                           "GB/s": round(bytes_ / sec / 1e9, 4)})
+        log(f"cpu {name} threads={threads}: {sec * 1e3:.2f} ms")
+
+    d_b = d_f = 0
+    perm, st, ad = oracle.segments_from_ids(projs["q"].token_ids, projs["q"].N)
+    for k in ("q", "o", "gate_up"):
+        p = projs[k]
+        b, f = fwd_work(p.h_in, p.h_out, p.ranks, st, ad)
+        d_b += b
+        d_f += f
+    fwd_cases = []
+    tiny = make_config("tiny")
+    tb = oracle.Batch(tiny)
+    tperm, tst, tad = oracle.segments_from_ids(tiny.token_ids, tiny.N)
+    fwd_cases.append(("tiny_16tok_256x256_4x_r8", lambda: (oracle.segments_from_ids(tiny.token_ids, tiny.N),
+                                                           tb.forward()), tiny.T,
+                      *fwd_work(tiny.h_in, tiny.h_out, tiny.ranks, tst, tad)))
+    fwd_cases.append(("decode_step_qwen3_4b_256tok_8x_r32", decode_step, 256, d_b, d_f))
+    for name, cfg in (("prefill_llama3_8b_8192tok_4096x4096_8x_r16", "prefill"),
+                      ("hetero_mlp_up_4096tok_4096x14336_32x_r8-128", "hetero")):
+        prob = make_config(cfg)
+        bt = oracle.Batch(prob)
+        b, f = fwd_work(prob.h_in, prob.h_out, prob.ranks, bt.seg_starts, bt.seg_adapter)
+        fwd_cases.append((name, bt.forward, prob.T, b, f))
+    for name, fn, tok, b, f in fwd_cases:
+        for th in (threads_all, 1):
+            record(name, fn, tok, b, f, th)
+    del fwd_cases
+    train = make_config("train")
+    trb = oracle.Batch(train)
+    del train.x, train.dy
+    bf, ff = fwd_work(trb.prob.h_in, trb.prob.h_out, trb.ranks, trb.seg_starts, trb.seg_adapter, save_u=True)
+    bb, fb = bwd_work(trb.prob.h_in, trb.prob.h_out, trb.ranks, trb.seg_starts, trb.seg_adapter)
+
+    def train_step():
+        _, u = trb.forward()
+        trb.backward(u)
+
+    record("train_fwd_bwd_qwen2p5_7b_65536tok_3584x3584_32x_r8-64", train_step, trb.prob.T, bf + bb, ff + fb,
+           threads_all)
+    oracle.set_num_threads(threads_all)
+    return {"value": round(bytes_per_step / dt / 1e9, 4), "unit": "GB/s", "cores": threads_all,
+            "kind": "oracle", "cpu_model": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{n} full decode steps (grouping + q, o, gate_up forward, 256 tokens) in fp64, "
-                      f"{dt * 1e3:.1f} ms per step"}
+                      f"{dt * 1e3:.1f} ms per step",
+            "per_config": per_config}
 
 
 def main():

@@ -1275,7 +1275,7 @@ static int packed_backward_impl(const void* x, int64_t ldx, const void* dy, int6
       }
       bytes += b;
     }
-    gstart.push_back(order.size());
+    if (gstart.back() != order.size()) gstart.push_back(order.size());
   }
   std::vector<char> has_tokens(N, 0);
   for (int a : order) has_tokens[a] = 1;
@@ -1502,6 +1502,7 @@ struct Recorder final : Launcher {
   DeviceInfo dev() override { return d; }
   hipError_t fwd(const FwdPlan& P, int rbmax, const uint64_t*, const uint64_t*) override {
     (void)rbmax;
+    if (P.grid <= 0) return hipErrorInvalidConfiguration;
     const int launch = launches++;
     for (int b = 0; b < P.grid; ++b) {
       lora_plan_item_t r{};
@@ -1532,6 +1533,7 @@ struct Recorder final : Launcher {
     return hipSuccess;
   }
   hipError_t transpose(const TransposePlan& P) override {
+    if (P.n_slots * (P.tiles_b + P.tiles_a) <= 0) return hipErrorInvalidConfiguration;
     const int launch = launches++;
     for (int k = 0; k < P.n_slots; ++k) {
       lora_plan_item_t r{};
@@ -1543,6 +1545,7 @@ struct Recorder final : Launcher {
     return hipSuccess;
   }
   hipError_t wgrad(const WgradPlan& P, int grid) override {
+    if (grid <= 0) return hipErrorInvalidConfiguration;
     const int launch = launches++;
     std::vector<int64_t> first(P.n_jobs);
     for (int j = 0; j < P.n_jobs; ++j) {
@@ -1591,8 +1594,9 @@ struct Recorder final : Launcher {
     return hipSuccess;
   }
   hipError_t reduce(const WgradReducePlan& R) override {
-    const int launch = launches++;
     const int grid = R.red_item0[R.n_red];
+    if (grid <= 0) return hipErrorInvalidConfiguration;
+    const int launch = launches++;
     for (int b = 0; b < grid; ++b) {
       int j = 0;
       while (j + 1 < R.n_red && b >= R.red_item0[j + 1]) ++j;

@@ -352,3 +352,20 @@ def test_hetero_plan_balance_within_bound():
     cu = _per_cu_cost(items, m.h_in, [m.h_out])
     ratio = float(cu.max() / cu.mean())
     assert ratio <= 1.15, f"max/mean predicted per-CU cost {ratio:.3f}"
+
+
+def test_backward_plan_without_tokens_only_zero_fills():
+    """A batch with no active tokens (every id -1, or only rank-0 adapters):
+    the backward plans only the zero-gradient items of adapters with a rank
+    (overwrite mode), and nothing at all in accumulate mode; no launch of
+    the plan has an empty grid."""
+    ranks = np.array([8, 0, 32], np.int32)
+    a = _HostAdapters(ranks, 256, 128)
+    for starts, adap in (([0, 5], [-1]), ([0, 4, 9], [1, -1])):
+        sg = L.Segments(np.array(starts, np.int32), np.array(adap, np.int32))
+        items, ranges = B.inspect_plan(B.OP_BACKWARD, a, sg, B.INSPECT_WITH_DX)
+        assert set(np.unique(items["phase"])) == {B.PHASE_WGRAD}
+        assert sorted(set(int(v) for v in items["adapter"])) == [0, 2]
+        assert len(ranges) == 0
+        items, _ = B.inspect_plan(B.OP_BACKWARD, a, sg, B.INSPECT_WITH_DX | B.INSPECT_ACCUMULATE)
+        assert len(items) == 0

@@ -572,15 +572,36 @@ def bench_multi_projection(reps=200, nsets=16):
         sets.append((x, ads, ys))
     wsm = L.new_workspace_multi(sets[0][1], sg)
     wss = [L.new_workspace(L.OP_FUSED, a, sg) for a in sets[0][1]]
+    # the C arguments of every call are marshalled once, so that the timed
+    # loop submits at the library's own host cost (the binding's per-call
+    # ctypes arrays would otherwise make this a measurement of Python)
+    from lora_adapter_batching_amd import binding as Bd
+    lib = L.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    pre_m, pre_s = [], []
+    for x, ads, ys in sets:
+        tabs = Bd._multi_tables(ads)
+        yp = (ctypes.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
+        ld = (ctypes.c_int64 * len(ys))(*[y.stride(0) for y in ys])
+        pre_m.append((tabs, yp, ld, x.data_ptr(), x.stride(0)))
+        pre_s.append([(x.data_ptr(), x.stride(0), a.c, y.data_ptr(), y.stride(0), w.data_ptr(), w.numel())
+                      for a, y, w in zip(ads, ys, wss)])
+    segp = sg.c
+    wsm_p, wsm_n = wsm.data_ptr(), wsm.numel()
 
     def multi(i):
-        x, ads, ys = sets[i % nsets]
-        L.sgmv_fused_multi(x, ads, sg, ys, wsm)
+        tabs, yp, ld, xp, ldx = pre_m[i % nsets]
+        st = lib.lora_sgmv_fused_multi(xp, ldx, len(probs), ctypes.cast(tabs, ctypes.c_void_p), segp,
+                                       ctypes.cast(yp, ctypes.c_void_p), ctypes.cast(ld, ctypes.c_void_p),
+                                       wsm_p, wsm_n, stream)
+        if st:
+            raise RuntimeError(lib.lora_last_error().decode())
 
     def single(i):
-        x, ads, ys = sets[i % nsets]
-        for a, y, w in zip(ads, ys, wss):
-            L.sgmv_fused(x, a, sg, y, None, w)
+        for xp, ldx, ac, yp, ldy, wp, wn in pre_s[i % nsets]:
+            st = lib.lora_sgmv_fused(xp, ldx, ac, segp, yp, ldy, None, 0, wp, wn, stream)
+            if st:
+                raise RuntimeError(lib.lora_last_error().decode())
     tm = float(_time_region(multi, reps)[0])
     ts = float(_time_region(single, reps)[0])
     # algorithmic bytes: each projection's, with x counted once (it is shared)

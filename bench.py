@@ -298,9 +298,10 @@ def bench_decode_request_order(steps=200, warmup=20, nsets=16):
 
 def bench_decode_graph(steps=200, warmup=20, nsets=16):
     """The decode step as one replayed HIP graph: the three projections'
-    device-planned calls (lora_sgmv_fused_graph: plan kernel + fused launch
-    each, ids and x/y in request order, every table on the device), captured
-    once per rotation set and replayed; wall time and GPU time per replay."""
+    device-planned calls (lora_sgmv_fused_graph: one fused launch each that
+    groups the 256 request-order ids itself, every table on the device),
+    captured once per rotation set and replayed; wall time and GPU time per
+    replay."""
     import torch
     import lora_adapter_batching_amd as L
     from workloads import make_c2_projections
@@ -355,7 +356,7 @@ def bench_decode_graph(steps=200, warmup=20, nsets=16):
     gpu = e0.elapsed_time(e1) * 1e-3 / steps
     return _entry("decode_step_graph_replay_device_planned_qwen3_4b_256tok_8x_r32", np.array([sec]), work_b, work_f,
                   {"gpu_us_per_step": round(gpu * 1e6, 2),
-                   "note": "one HIP graph per step: 3 x (plan kernel + fused launch), ids on the device"})
+                   "note": "one HIP graph per step: 3 fused launches that plan on the device, ids on the device"})
 
 
 # ---------------------------------------------------------------------------

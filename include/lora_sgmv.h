@@ -238,13 +238,14 @@ int lora_sgmv_fused_multi(const void* x, int64_t ldx, int32_t num_proj,
  * batch is described only by DEVICE data, so nothing the host computes is
  * baked into a captured launch:
  *
- *   lora_sgmv_fused_graph() enqueues two kernels. A one-workgroup plan kernel
- *   reads token_ids[num_tokens] (request order) and the adapters' device
- *   ranks, groups the tokens per adapter with a stable counting sort
- *   (adapters in id order, request order within), writes the tile table and
- *   the sorted-position -> row table into the workspace, and advances an
- *   epoch kept in the workspace. The fused shrink + expand launch then reads
- *   its tiles, rows and hand-off id from the workspace:
+ *   lora_sgmv_fused_graph() groups token_ids[num_tokens] (request order)
+ *   per adapter on the device with a stable counting sort (adapters in id
+ *   order, request order within) against the adapters' device tables, cuts
+ *   the groups into 32-token tiles and runs the fused shrink + expand on
+ *   them. Up to 1024 tokens this is ONE launch: every workgroup reads the
+ *   ids and the tables and plans its own tile. Above, a one-workgroup plan
+ *   kernel writes the tile table and the sorted-position -> row table into
+ *   the workspace first, and the fused launch reads them. Either way:
  *     y[t] += s_i B_i (A_i x[t])   for every token t whose id i is active,
  *   with x and y in request order (rows 0 .. num_tokens-1). A token whose id
  *   is outside [0, N), or whose adapter has a rank outside [1, max_rank] or
@@ -259,8 +260,10 @@ int lora_sgmv_fused_multi(const void* x, int64_t ldx, int32_t num_proj,
  *
  * The workspace (lora_workspace_size_graph) must be zero-filled once before
  * its first use and must not be shared with other entry points; calls on
- * one workspace must be ordered (a graph's replays on one stream are). The
- * epoch makes every call's hand-off stamps distinct, across replays too.
+ * one workspace must be ordered (a graph's replays on one stream are). A
+ * workspace sized for num_tokens serves calls of fewer tokens too. An epoch
+ * kept in the workspace makes every call's hand-off stamps distinct, across
+ * replays and batch sizes.
  * Errors are reported for the host arguments only; device data are not
  * checked beyond the rules above.
  */

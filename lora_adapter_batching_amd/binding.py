@@ -277,6 +277,12 @@ class GraphAdapters:
     max_rank."""
 
     def __init__(self, A_ptrs, B_ptrs, ranks, scales, h_in: int, h_out: int, max_rank: int):
+        import torch
+        n = int(ranks.numel())
+        for name, t, dt in (("A_ptrs", A_ptrs, torch.int64), ("B_ptrs", B_ptrs, torch.int64),
+                            ("ranks", ranks, torch.int32), ("scales", scales, torch.float32)):
+            if not t.is_cuda or t.dtype != dt or not t.is_contiguous() or t.numel() != n:
+                raise ValueError(f"{name} must be a contiguous {dt} device tensor of {n} entries")
         self.A_ptrs, self.B_ptrs, self.ranks, self.scales = A_ptrs, B_ptrs, ranks, scales
         self.h_in, self.h_out, self.max_rank = int(h_in), int(h_out), int(max_rank)
         self._c = CGraphAdapters(int(ranks.numel()), self.h_in, self.h_out, self.max_rank, _ptr(A_ptrs),
@@ -302,7 +308,14 @@ def new_workspace_graph(adapters: GraphAdapters, num_tokens: int, device="cuda")
 def sgmv_fused_graph(x, adapters: GraphAdapters, token_ids, y, ws, stream=None):
     """lora_sgmv_fused_graph: x, y in request order, token_ids an int32 device
     tensor of one adapter id per row of x."""
+    import torch
     lib = load()
+    T = int(token_ids.numel())
+    if not token_ids.is_cuda or token_ids.dtype != torch.int32 or not token_ids.is_contiguous():
+        raise ValueError("token_ids must be a contiguous int32 device tensor")
+    for name, t, w in (("x", x, adapters.h_in), ("y", y, adapters.h_out)):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or t.shape[0] < T or t.shape[1] != w or t.stride(1) != 1:
+            raise ValueError(f"{name} must be a bf16 [>= {T}, {w}] matrix with unit column stride")
     wp, wb = _ws(ws)
     _check(lib.lora_sgmv_fused_graph(_ptr(x), x.stride(0), adapters.c, _ptr(token_ids), int(token_ids.numel()),
                                      _ptr(y), y.stride(0), wp, wb, _stream_handle(stream)))

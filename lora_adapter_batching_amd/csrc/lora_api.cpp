@@ -1362,14 +1362,15 @@ int lora_packed_backward(const void* x, int64_t ldx, const void* dy, int64_t ldd
 namespace {
 
 struct GraphLayout {
-  size_t counters = 0, partials = 0, tiles = 0, hdr = 0, perm = 0, total = 0;
+  size_t counters = 0, epoch = 0, partials = 0, tiles = 0, hdr = 0, perm = 0, total = 0;
   int max_tiles = 0;
 };
 
-// Workspace of lora_sgmv_fused_graph: hand-off words, split-shrink parts for
-// the largest tile count the batch can have (each adapter adds at most one
-// ragged tile), the tile table, a 256-byte header (tile count at +0, the
-// epoch at +8) and the sorted-position -> row table.
+// Workspace of lora_sgmv_fused_graph: hand-off words, the epoch's slots
+// (these two at the same offsets for every num_tokens), split-shrink parts
+// for the largest tile count the batch can have (each adapter adds at most
+// one ragged tile), the tile table, a 256-byte header (tile count at +0) and
+// the sorted-position -> row table.
 GraphLayout graph_layout(const lora_graph_adapters_t* a, int T) {
   GraphLayout L;
   L.max_tiles = std::max(1, cdiv(T, kTileM) + std::min(a->num_adapters, T));
@@ -1380,6 +1381,7 @@ GraphLayout graph_layout(const lora_graph_adapters_t* a, int T) {
     return o;
   };
   L.counters = take(kCounterBytes);
+  L.epoch = take((size_t)kEpochSlots * kEpochStride);  // at the same offset for every num_tokens
   const int64_t parts = std::min<int64_t>(kMaxPartials, (int64_t)L.max_tiles * kMaxKs);
   L.partials = take((size_t)parts * kTileM * rpad_for(a->max_rank) * sizeof(float));
   L.tiles = take((size_t)L.max_tiles * sizeof(DevTile));
@@ -1420,18 +1422,23 @@ int sgmv_fused_graph_impl(const void* x, int64_t ldx, const lora_graph_adapters_
   const GraphLayout G = graph_layout(a, T);
   if ((st = check_ws(ws, ws_bytes, G.total))) return st;
   char* wsb = static_cast<char*>(ws);
+  uint64_t* epoch = reinterpret_cast<uint64_t*>(wsb + G.epoch);
+  const bool self_plan = T <= kSelfPlanTokens;
   DevPlanArgs D{};
   D.ids = token_ids;
   D.A_ptrs = a->A_ptrs; D.B_ptrs = a->B_ptrs; D.ranks = a->ranks; D.scales = a->scales;
   D.perm = reinterpret_cast<int32_t*>(wsb + G.perm);
   D.tiles = reinterpret_cast<DevTile*>(wsb + G.tiles);
   D.count = reinterpret_cast<int32_t*>(wsb + G.hdr);
-  D.epoch = reinterpret_cast<uint64_t*>(wsb + G.hdr + 8);
+  D.epoch = epoch;
   D.T = T; D.N = a->num_adapters; D.max_rank = a->max_rank; D.max_tiles = G.max_tiles;
-  hipError_t e = launcher.dev_plan(D);
-  if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "plan kernel launch failed: %s", hipGetErrorString(e));
+  hipError_t e;
+  if (!self_plan) {
+    e = launcher.dev_plan(D);
+    if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "plan kernel launch failed: %s", hipGetErrorString(e));
+  }
   // the fused launch is laid out for the largest tile count; tiles past the
-  // count the plan kernel writes have no work
+  // count of the batch have no work
   FwdCall c{};
   c.mode_op = LORA_OP_FUSED;
   c.K = a->h_in; c.N = a->h_out;
@@ -1439,11 +1446,18 @@ int sgmv_fused_graph_impl(const void* x, int64_t ldx, const lora_graph_adapters_
   std::memset(&P, 0, sizeof(P));
   P.X = static_cast<const uint16_t*>(x); P.ldx = ldx;
   P.Y = static_cast<uint16_t*>(y); P.ldy = ldy;
-  P.token_rows = D.perm;
   P.partials = reinterpret_cast<float*>(wsb + G.partials);
   P.counters = reinterpret_cast<int32_t*>(wsb + G.counters);
   P.stamps = reinterpret_cast<uint64_t*>(wsb + G.counters + kStampOffset);
-  P.dev_tiles = D.tiles; P.dev_count = D.count; P.dev_epoch = D.epoch;
+  P.dev_epoch = epoch;
+  if (self_plan) {
+    P.self_ids = token_ids;
+    P.self_A = a->A_ptrs; P.self_B = a->B_ptrs; P.self_ranks = a->ranks; P.self_scales = a->scales;
+    P.self_T = T; P.self_N = a->num_adapters; P.self_max_rank = a->max_rank;
+  } else {
+    P.token_rows = D.perm;
+    P.dev_tiles = D.tiles; P.dev_count = D.count;
+  }
   P.ptrs_in_plan = 1;
   P.K = a->h_in; P.N = a->h_out; P.v_round = 1;
   P.rpad = rpad_for(a->max_rank);
@@ -1454,6 +1468,8 @@ int sgmv_fused_graph_impl(const void* x, int64_t ldx, const lora_graph_adapters_
   fused_layout(P, c, G.max_tiles, a->max_rank, cdiv(a->h_out, 32), dev);
   if (P.mode == kModeFusedDep && (int64_t)G.max_tiles * P.ks > kMaxPartials)
     return fail(LORA_UNSUPPORTED, "batch too large for the split layout of a device-planned call");
+  if ((uint64_t)P.grid >= kEpochCall)
+    return fail(LORA_UNSUPPORTED, "grid of %d workgroups too large for a device-planned call", P.grid);
   const int rbmax = a->max_rank <= 32 ? 1 : (a->max_rank <= 64 ? 2 : 4);
   e = launcher.fwd(P, rbmax, nullptr, nullptr);
   if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "kernel launch failed: %s", hipGetErrorString(e));

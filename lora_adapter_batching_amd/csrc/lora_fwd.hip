@@ -34,6 +34,8 @@ struct TileInfo {
   int proj;  // projection (multi-projection launches; else 0)
   float scale;
   uint64_t wptr, vptr;  // small plans with ptrs_in_plan: the segment's weight addresses
+  const int* rows;      // batches planned inside the launch: the tile's rows (LDS)
+  uint64_t lid;         // ... and the launch id of the split hand-off
 };
 
 template <typename PT>
@@ -43,12 +45,21 @@ struct PlanCap;
 template <int CAP>
 struct PlanCap<FwdPlanT<CAP>> {
   static constexpr int v = CAP;  // segment capacity of a plan type
+  static constexpr bool self = false;  // launches planned inside themselves
   // byte offsets of the weight-address arrays in the plan, which is the
   // kernel's only explicit argument and so starts the kernel-argument segment
   static constexpr int kOffW = __builtin_offsetof(FwdPlanT<CAP>, seg_wptr);
   static constexpr int kOffV = __builtin_offsetof(FwdPlanT<CAP>, seg_vptr);
 };
 #pragma clang diagnostic pop
+// The plan of launches planned inside themselves: the small plan's layout
+// under a type of its own, so that they get kernel instances of their own
+// and the code of every other launch is left as it is.
+struct FwdPlanSelf : FwdPlanT<kSmallSeg> {};
+template <>
+struct PlanCap<FwdPlanSelf> : PlanCap<FwdPlanT<kSmallSeg>> {
+  static constexpr bool self = true;
+};
 
 // Finds the segment that holds tile g. Small plans (decode batches): a scalar
 // scan of the whole table, which the compiler reads from the kernel
@@ -240,6 +251,8 @@ struct Lds {
   uint8_t* b1;
   TileInfo* ti;
   int* flag;
+  int* rows;      // [kTileM] rows of a tile planned inside the launch
+  uint64_t* lid;  // its launch id
   __device__ float* Pl() const { return reinterpret_cast<float*>(b1); }
   __device__ float* red() const { return reinterpret_cast<float*>(b0); }
 };
@@ -256,7 +269,7 @@ template <typename PT>
 __device__ __forceinline__ TileRows tile_rows(const uint16_t* base, int64_t ld, int width, const PT& P,
                                               const TileInfo& t) {
   TileRows tr;
-  tr.gather = P.token_rows != nullptr;
+  tr.gather = PlanCap<PT>::self || P.token_rows != nullptr;
   tr.ld2 = ld * 2;
   tr.lim = kGatherSpan - (int64_t)width * 2;
   if (tr.gather)
@@ -273,8 +286,174 @@ template <typename PT>
 __device__ __forceinline__ uint32_t row_off(const PT& P, const TileInfo& t, const TileRows& tr, int n) {
   if (n >= t.cnt) return kOff;
   if (!tr.gather) return (uint32_t)((int64_t)n * tr.ld2);
-  const int64_t off = (int64_t)P.token_rows[t.p0 + n] * tr.ld2;
+  int row;
+  if constexpr (PlanCap<PT>::self) row = t.rows[n];
+  else row = P.token_rows[t.p0 + n];
+  const int64_t off = (int64_t)row * tr.ld2;
   return (off < 0 || off > tr.lim) ? kOff : (uint32_t)off;
+}
+
+// ---------------------------------------------------------------------------
+// Grouping a request-order batch by adapter on the device (a stable counting
+// sort: adapters in id order, the tokens of an adapter in request order,
+// tokens without an active adapter last in key N, which gets no tiles).
+// ---------------------------------------------------------------------------
+// Wave-level exclusive scan of the tokens per key, cnt[0..N] (LDS): each lane
+// takes a block of consecutive keys and the blocks' sums are scanned with
+// shuffles. visit(key, first sorted position, first tile, tokens) runs for
+// every key on the lane that holds it. Returns the tile count (all lanes).
+template <typename F>
+__device__ __forceinline__ int scan_keys(const int* cnt, int N, F&& visit) {
+  constexpr int kPer = (kMaxGraphAdapters + 1 + 63) / 64;
+  const int lane = threadIdx.x & 63;
+  int c[kPer], ls = 0, lt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = lane * kPer + j;
+    c[j] = i <= N ? cnt[i] : 0;
+    ls += c[j];
+    lt += i < N ? (c[j] + kTileM - 1) / kTileM : 0;
+  }
+  int ss = ls, st = lt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int us = __shfl_up(ss, o), ut = __shfl_up(st, o);
+    if (lane >= o) {
+      ss += us;
+      st += ut;
+    }
+  }
+  int tok = ss - ls, tile = st - lt;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = lane * kPer + j;
+    if (i <= N) visit(i, tok, tile, c[j]);
+    tok += c[j];
+    tile += i < N ? (c[j] + kTileM - 1) / kTileM : 0;
+  }
+  return __shfl(st, 63);
+}
+
+// Lane 0's 64-bit value in SGPRs. readfirstlane returns a signed int: each
+// half goes back through uint32_t, or a low word with bit 31 set would be
+// sign-extended over the high word.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// An adapter takes part if its rank is in [1, max_rank] and both weight
+// addresses are set; ids outside [0, N) and inactive adapters map to key N.
+__device__ __forceinline__ bool adapter_active(int rank, int max_rank, uint64_t wptr, uint64_t vptr) {
+  return rank >= 1 && rank <= max_rank && wptr != 0 && vptr != 0;
+}
+
+// The tile of a batch planned inside the launch. Every workgroup reads the
+// ids (at most kSelfPlanTokens, kThreads apart per thread) and the adapter
+// tables (thread i: adapter i), counts the tokens per key, finds the key and
+// the place of tile g among its tokens, and ranks the key's tokens in
+// request order to collect the tile's rows in L.rows. A tile past the tile
+// count comes back with cnt 0. old_epoch: thread 0's read of the epoch as
+// it added its share (dep mode).
+template <typename PT>
+__device__ __forceinline__ TileInfo self_tile_info(const PT& P, int g, const Lds& L, uint64_t old_epoch) {
+  constexpr int KPT = kSelfPlanTokens / kThreads;
+  static_assert(kMaxGraphAdapters <= kThreads, "one adapter per thread");
+  static_assert((2 * kMaxGraphAdapters + 1 + 4 * KPT + 4) * 4 <= LdsBytes<1>::b0, "plan scratch fits buffer 0");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = P.self_N, T = P.self_T;
+  int* cnt = reinterpret_cast<int*>(L.b0);  // [N + 1] tokens per key
+  int* act = cnt + kMaxGraphAdapters + 1;   // [N] active adapters
+  int* wtot = act + kMaxGraphAdapters;      // [KPT][4] the tile's key: tokens per (block, wave)
+  int* sel = wtot + 4 * KPT;                // the tile: key, place in the key, count, sorted position
+  // the global reads, all issued together
+  int rk = 0;
+  float sc = 0.f;
+  uint64_t wp = 0, vp = 0;
+  if (tid < N) {
+    rk = P.self_ranks[tid];
+    sc = P.self_scales[tid];
+    wp = P.self_A[tid];
+    vp = P.self_B[tid];
+  }
+  int key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int t = j * kThreads + tid;
+    key[j] = t < T ? P.self_ids[t] : -1;
+  }
+  for (int i = tid; i <= N; i += kThreads) cnt[i] = 0;
+  if (tid < N) act[tid] = adapter_active(rk, P.self_max_rank, wp, vp) ? 1 : 0;
+  if (tid == 0) *L.lid = (old_epoch >> kEpochShift) + 1;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (j * kThreads + tid < T) {
+      const int id = key[j];
+      key[j] = (id >= 0 && id < N && act[id]) ? id : N;
+      atomicAdd(&cnt[key[j]], 1);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int tiles = scan_keys(cnt, N, [&](int i, int tok, int tile, int c) {
+      if (i < N && g >= tile && g < tile + (c + kTileM - 1) / kTileM) {
+        const int j0 = (g - tile) * kTileM;
+        sel[0] = i;
+        sel[1] = j0;
+        sel[2] = min(kTileM, c - j0);
+        sel[3] = tok + j0;
+      }
+    });
+    if (lane == 0 && g >= tiles) {
+      sel[0] = -1;
+      sel[2] = 0;
+    }
+  }
+  __syncthreads();
+  TileInfo t{};
+  t.g = g;
+  t.cnt = __builtin_amdgcn_readfirstlane(sel[2]);
+  if (t.cnt <= 0) return t;
+  const int a = __builtin_amdgcn_readfirstlane(sel[0]);
+  const int j0 = __builtin_amdgcn_readfirstlane(sel[1]);
+  t.p0 = __builtin_amdgcn_readfirstlane(sel[3]);
+  // the key's tokens ranked in request order: by lane within a wave, then by
+  // wave, then by block of kThreads tokens
+  int pre[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(key[j] == a);
+    pre[j] = __builtin_popcountll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wtot[4 * j + wave] = __builtin_popcountll(m);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (key[j] == a) {
+      int r = pre[j] - j0;
+      for (int q = 0; q < 4 * j + wave; ++q) r += wtot[q];
+      if (r >= 0 && r < kTileM) L.rows[r] = j * kThreads + tid;
+    }
+  }
+  if (tid == a) {
+    L.ti->rank = rk;
+    L.ti->scale = sc;
+    L.ti->wptr = wp;
+    L.ti->vptr = vp;
+  }
+  __syncthreads();
+  t.adapter = a;
+  t.rank = __builtin_amdgcn_readfirstlane(L.ti->rank);
+  t.scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, L.ti->scale)));
+  t.wptr = uniform64(L.ti->wptr);
+  t.vptr = uniform64(L.ti->vptr);
+  t.slot = 0;
+  t.proj = 0;
+  t.rows = L.rows;
+  t.lid = uniform64(*L.lid);
+  return t;
 }
 
 // ---------------------------------------------------------------------------
@@ -903,11 +1082,13 @@ __device__ __forceinline__ uint32_t xcc_id() {
 }
 constexpr int kAuxDev = 16;  // sc1: device scope
 
-// The id that stamps this launch's parts: from the host, or (batches planned
-// on the device) from the workspace epoch the plan kernel has just advanced.
-__device__ __forceinline__ uint64_t launch_id(const FwdHeader& P) {
-  if (P.dev_epoch) return __builtin_amdgcn_readfirstlane((uint32_t)*P.dev_epoch) |
-                          ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(*P.dev_epoch >> 32)) << 32);
+// The id that stamps this launch's parts: from the host; for batches planned
+// inside the launch, the one the workgroup took when it advanced the epoch;
+// for batches planned by the plan kernel, from the epoch it has just advanced.
+template <typename PT>
+__device__ __forceinline__ uint64_t launch_id(const PT& P, const TileInfo& t) {
+  if constexpr (PlanCap<PT>::self) return t.lid;
+  if (P.dev_epoch) return uniform64(*P.dev_epoch >> kEpochShift);
   return P.launch_id;
 }
 
@@ -1004,7 +1185,7 @@ __device__ __forceinline__ void item_shrink(const PT& P, const Lds& L, const Til
     wait_vmcnt<0>();  // this thread's part stores have been performed
     __syncthreads();  // ... and every thread's
     if (threadIdx.x == 0) {
-      const uint64_t stamp = (launch_id(P) << 8) | xcc_id();
+      const uint64_t stamp = (launch_id(P, t) << 8) | xcc_id();
       __hip_atomic_store(P.stamps + (t.g * P.ks + c), stamp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
@@ -1044,7 +1225,7 @@ __device__ __forceinline__ bool wait_and_sum_parts(const PT& P, const Lds& L, co
     // lane q < ks watches the stamp of part q
     const bool mine = lane < P.ks;
     const int idx = t.g * P.ks + (mine ? lane : 0);
-    const uint64_t want = launch_id(P);
+    const uint64_t want = launch_id(P, t);
     const uint64_t t0 = wall_clock64();
     bool ready = false;
     while (true) {
@@ -1142,8 +1323,29 @@ __global__ __launch_bounds__(kThreads, 2) void sgmv_fwd_kernel(PT P) {
   __shared__ alignas(16) uint8_t lds_b1[LdsBytes<RBMAX>::b1];
   __shared__ TileInfo lds_ti;
   __shared__ int lds_flag;
-  const Lds L{lds_b0, lds_b1, &lds_ti, &lds_flag};
+  __shared__ int lds_rows[kTileM];
+  __shared__ uint64_t lds_lid;
+  const Lds L{lds_b0, lds_b1, &lds_ti, &lds_flag, lds_rows, &lds_lid};
   const int b = blockIdx.x;
+  // A launch planned inside itself with the split hand-off advances the
+  // epoch by kEpochCall in all: every workgroup, with or without an item,
+  // adds its share once (workgroup 0 the rest); the value read back gives
+  // every workgroup the same launch id.
+  static_assert(kEpochSlots <= 64, "workgroup 0's first wave covers the slots");
+  uint64_t old_epoch = 0;
+  if (PlanCap<PT>::self && P.mode == kModeFusedDep) {
+    constexpr int kSlotWords = kEpochStride / 8;
+    if (threadIdx.x == 0) {
+      const int s = b % kEpochSlots;
+      const uint64_t n_s = (uint64_t)((P.grid - 1 - s) / kEpochSlots + 1);  // workgroups of slot s
+      old_epoch = __hip_atomic_fetch_add(P.dev_epoch + s * kSlotWords, b == s ? kEpochCall - (n_s - 1) : 1ull,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (b == 0 && (int)threadIdx.x >= P.grid && threadIdx.x < kEpochSlots) {
+      // slots no workgroup uses (grids under kEpochSlots) advance in full
+      __hip_atomic_fetch_add(P.dev_epoch + threadIdx.x * kSlotWords, kEpochCall, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   // Read the launch parameters that select the item and its tile in one
   // batch of scalar loads: left to itself the compiler loads them one branch
   // at a time, a memory round trip each, before the item's first data load.
@@ -1153,7 +1355,9 @@ __global__ __launch_bounds__(kThreads, 2) void sgmv_fwd_kernel(PT P) {
   const FwdItem it = fwd_item(P, b);
   const int g = it.g, c = it.c, kind = it.kind;
   if (g >= 0) {
-    const TileInfo t = tile_info(P, g, L.ti);
+    TileInfo t;
+    if constexpr (PlanCap<PT>::self) t = self_tile_info(P, g, L, old_epoch);
+    else t = tile_info(P, g, L.ti);
     if (t.cnt <= 0) return;  // a tile past the count of a batch planned on the device
     if (RBMAX == 1 || t.rank <= 32) run_item<1>(P, L, t, kind, c);
     else if (RBMAX == 2 || t.rank <= 64) run_item<(RBMAX >= 2 ? 2 : 1)>(P, L, t, kind, c);
@@ -1178,6 +1382,11 @@ static hipError_t launch_fwd_t(const PT& P, int rbmax, hipStream_t stream) {
 // header sets ptrs_in_plan.
 hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream, const uint64_t* wptr,
                       const uint64_t* vptr) {
+  if (P.self_ids) {
+    FwdPlanSelf Q{};
+    static_cast<FwdHeader&>(Q) = static_cast<const FwdHeader&>(P);
+    return launch_fwd_t(Q, rbmax, stream);
+  }
   if (P.n_seg <= kSmallSeg) {
     FwdPlanT<kSmallSeg> Q{};
     static_cast<FwdHeader&>(Q) = static_cast<const FwdHeader&>(P);
@@ -1207,9 +1416,8 @@ namespace lora {
 // per-adapter segments with a stable counting sort (adapters in id order,
 // the tokens of an adapter in request order, tokens without an active adapter
 // last), cuts the segments into 32-token tiles and advances the workspace
-// epoch that stamps the following launch's hand-off. An adapter is active if
-// its rank is in [1, max_rank] and both weight addresses are set; ids outside
-// [0, N) and tokens of inactive adapters are left out of every tile.
+// epoch that stamps the following launch's hand-off by kEpochCall. Ids
+// outside [0, N) and tokens of inactive adapters are left out of every tile.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kPlanThreads) void dev_plan_kernel(DevPlanArgs a) {
   __shared__ int cnt[kMaxGraphAdapters + 1];
@@ -1219,51 +1427,54 @@ __global__ __launch_bounds__(kPlanThreads) void dev_plan_kernel(DevPlanArgs a) {
   __shared__ int act[kMaxGraphAdapters];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = a.N;
-  const uint64_t epoch0 = tid == 0 ? *a.epoch : 0;
+  // every global read is issued before the first barrier: the epoch's slots
+  // (one per thread), one adapter's table entries per thread (N <= 256 <
+  // kPlanThreads) and the first chunk's ids, which stay in registers for
+  // both passes
+  uint64_t* const slot = a.epoch + (tid % kEpochSlots) * (kEpochStride / 8);
+  const uint64_t epoch0 = tid < kEpochSlots ? *slot : 0;
+  int rk = 0;
+  float sc = 0.f;
+  uint64_t wp = 0, vp = 0;
+  if (tid < N) {
+    rk = a.ranks[tid];
+    sc = a.scales[tid];
+    wp = a.A_ptrs[tid];
+    vp = a.B_ptrs[tid];
+  }
+  const int id0 = tid < a.T ? a.ids[tid] : -1;
   for (int i = tid; i <= N; i += kPlanThreads) cnt[i] = 0;
-  for (int i = tid; i < N; i += kPlanThreads) {
-    const int r = a.ranks[i];
-    act[i] = (r >= 1 && r <= a.max_rank && a.A_ptrs[i] != 0 && a.B_ptrs[i] != 0) ? 1 : 0;
-  }
+  if (tid < N) act[tid] = adapter_active(rk, a.max_rank, wp, vp) ? 1 : 0;
   __syncthreads();
-  auto key_of = [&](int t) {
-    const int id = a.ids[t];
-    return (id >= 0 && id < N && act[id]) ? id : N;
-  };
+  auto key_of_id = [&](int id) { return (id >= 0 && id < N && act[id]) ? id : N; };
   // pass 1: tokens per key
-  for (int t = tid; t < a.T; t += kPlanThreads) atomicAdd(&cnt[key_of(t)], 1);
+  for (int t = tid; t < a.T; t += kPlanThreads) atomicAdd(&cnt[key_of_id(t == tid ? id0 : a.ids[t])], 1);
   __syncthreads();
-  if (tid == 0) {
-    int s = 0, nt = 0;
-    for (int i = 0; i <= N; ++i) {
-      start[i] = s;
-      tile0[i] = nt;
-      s += cnt[i];
-      if (i < N) nt += (cnt[i] + kTileM - 1) / kTileM;
-    }
-    *a.count = min(nt, a.max_tiles);
-    *a.epoch = epoch0 + 1;
+  // token and tile offsets per key
+  if (wave == 0) {
+    const int tiles = scan_keys(cnt, N, [&](int i, int tok, int tile, int) {
+      start[i] = tok;
+      tile0[i] = tile;
+    });
+    if (lane == 0) *a.count = min(tiles, a.max_tiles);
   }
+  if (tid < kEpochSlots) *slot = epoch0 + kEpochCall;
   __syncthreads();
-  // tiles, one adapter per thread
-  for (int i = tid; i < N; i += kPlanThreads) {
-    const int c = cnt[i];
-    if (c == 0) continue;
-    const int r = a.ranks[i];
-    const float sc = a.scales[i];
-    const uint64_t w = a.A_ptrs[i], v = a.B_ptrs[i];
+  // tiles: thread i writes adapter i's, from the table entries it holds
+  if (tid < N) {
+    const int c = cnt[tid];
     for (int j = 0; j < c; j += kTileM) {
-      const int g = tile0[i] + j / kTileM;
+      const int g = tile0[tid] + j / kTileM;
       if (g >= a.max_tiles) break;
       DevTile d;
-      d.tok0 = start[i] + j;
+      d.tok0 = start[tid] + j;
       d.cnt = min(kTileM, c - j);
-      d.adapter = i;
-      d.rank = r;
+      d.adapter = tid;
+      d.rank = rk;
       d.scale = sc;
       d.pad = 0;
-      d.wptr = w;
-      d.vptr = v;
+      d.wptr = wp;
+      d.vptr = vp;
       a.tiles[g] = d;
     }
   }
@@ -1273,7 +1484,7 @@ __global__ __launch_bounds__(kPlanThreads) void dev_plan_kernel(DevPlanArgs a) {
   for (int c0 = 0; c0 < a.T; c0 += kPlanThreads) {
     for (int i = lane; i <= N; i += 64) wave_cnt[wave][i] = 0;
     const int t = c0 + tid;
-    const int key = t < a.T ? key_of(t) : -1;
+    const int key = t < a.T ? key_of_id(c0 == 0 ? id0 : a.ids[t]) : -1;
     int rank_in_wave = 0;
     uint64_t todo = __builtin_amdgcn_ballot_w64(key >= 0);
     while (todo) {

@@ -37,6 +37,22 @@ enum FwdMode : int32_t {
 // follow at byte offset kStampOffset (one uint64 per (tile, k-chunk)).
 constexpr int kCtrTiles = 64;        // per-tile arrival counters start here
 constexpr int kStampOffset = 4096;   // bytes from the counters to the stamps
+// The epoch of device-planned calls: kEpochSlots uint64 words, one per
+// kEpochStride bytes. Every call adds 1 << kEpochShift to every slot, so
+// between calls all slots hold the same multiple of it, whose high bits
+// count the calls (the id of the n-th call is n, never 0). A call planned
+// inside its launch spreads each slot's sum over the workgroups that use
+// the slot (workgroup b uses slot b % kEpochSlots; each adds 1, the first of
+// a slot the rest), so any value a workgroup reads while adding its share
+// shifts down to the same count, and the adds of a launch are spread over
+// kEpochSlots addresses instead of piling up on one.
+constexpr int kEpochShift = 20;
+constexpr uint64_t kEpochCall = 1ull << kEpochShift;
+constexpr int kEpochSlots = 64;
+constexpr int kEpochStride = 128;  // bytes between slots (one cache line each)
+// Device-planned calls of at most this many tokens are planned inside the
+// fused launch (4 ids per thread of a workgroup), larger ones by the plan kernel.
+constexpr int kSelfPlanTokens = 1024;
 
 // One 32-token tile of a batch planned on the device (lora_sgmv_fused_graph):
 // written by the plan kernel into the workspace, read by the fused kernel.
@@ -94,7 +110,22 @@ struct FwdHeader {
   // n_tiles above is only the bound the grid was laid out for. Null otherwise.
   const DevTile* dev_tiles;
   const int32_t* dev_count;
-  const uint64_t* dev_epoch;
+  // The workspace epoch of device-planned calls (both kinds below): slot 0
+  // of kEpochSlots; bits [kEpochShift, 64) count the calls on the workspace.
+  uint64_t* dev_epoch;
+  // Batches planned inside the launch (device-planned calls of at most
+  // kSelfPlanTokens tokens): every workgroup groups the request-order ids
+  // itself against the device adapter tables and keeps its own tile; the
+  // split hand-off's launch id comes from the epoch, which every workgroup
+  // advances. Null otherwise.
+  const int32_t* self_ids;
+  const uint64_t* self_A;
+  const uint64_t* self_B;
+  const int32_t* self_ranks;
+  const float* self_scales;
+  int32_t self_T;
+  int32_t self_N;
+  int32_t self_max_rank;
   // Projections 1 .. kMaxProj-1 of a multi-projection launch (several
   // LoRA-wrapped projections over the same x); projection 0 uses Y, ldy, N,
   // nblk, Wtab and Vtab above, and entry 0 of these arrays is unused.
@@ -221,7 +252,7 @@ struct DevPlanArgs {
   int32_t* perm;            // [T] sorted position -> request row (adapter order, request order within)
   DevTile* tiles;           // [max_tiles]
   int32_t* count;           // [1] tiles written
-  uint64_t* epoch;          // [1] launch id: incremented by every plan
+  uint64_t* epoch;          // the workspace epoch's slots: each advanced by kEpochCall by every plan
   int32_t T;
   int32_t N;
   int32_t max_rank;         // adapters whose rank is outside [1, max_rank] are skipped

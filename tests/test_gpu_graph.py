@@ -82,6 +82,10 @@ CASES = [
     ("q_2560", 256, 2560, 2560, [32] * 8, 32),
     # expand-heavy MLP-up-like projection, mixed ranks (split layout over all XCDs)
     ("up_1024x8192", 64, 1024, 8192, [8, 16, 0, 64, 32], 64),
+    # the most tokens a launch plans by itself; 13 adapters, one inactive
+    ("q_1024tok_13ad", 1024, 2048, 1024, [16] * 12 + [0], 16),
+    # more tokens than a launch plans by itself: the plan kernel runs first
+    ("o_1500tok_plan_kernel", 1500, 1024, 2048, [32] * 8, 32),
 ]
 
 
@@ -249,3 +253,37 @@ def test_double_buffered_tables_update_during_decode():
     m = prob.token_ids == k
     d = to_f64(y_old) != to_f64(y_new)
     assert np.any(d[m]) and not np.any(d[~m])
+
+
+def test_one_workspace_serves_both_planners():
+    """One workspace, sized for the largest batch, serves calls of several
+    sizes in turn, planned inside the launch (<= 1024 tokens) or by the plan
+    kernel (more): the epoch keeps every call's hand-off distinct across
+    both kinds, and each call gives the same bits as lora_sgmv_fused."""
+    import torch
+    import lora_adapter_batching_amd as L
+    h_in, h_out, ranks = 2048, 2048, [32] * 6 + [16] * 2
+    T_max = 1400
+    big = _problem(31, T_max, h_in, h_out, ranks)
+    tb = _Tables(big, 32)
+    x = dev_bf16(big.x)
+    ws = L.new_workspace_graph(tb.ga, T_max)
+    ad_h = L.Adapters(tb.A, tb.B, big.ranks, big.scales, h_in, h_out)
+    rng = np.random.default_rng(32)
+    for T in (256, 1400, 96, 1024, 1400, 256):
+        need = L.workspace_size_graph(tb.ga, T)
+        assert need <= ws.numel(), (T, need, ws.numel())
+        ids_h = rng.integers(0, big.N, size=T).astype(np.int32)
+        ids = torch.from_numpy(ids_h).cuda()
+        y0 = dev_bf16(big.y0[:T])
+        y_graph = y0.clone()
+        _say(f"shared workspace, {T} tokens")
+        L.sgmv_fused_graph(x[:T], tb.ga, ids, y_graph, ws)
+        perm, st, ad = L.segments_from_ids(ids_h, big.N)
+        sg = L.Segments(st, ad, torch.from_numpy(perm.copy()).cuda())
+        y_fused = y0.clone()
+        L.sgmv_fused(x[:T], ad_h, sg, y_fused, None, L.new_workspace(L.OP_FUSED, ad_h, sg))
+        torch.cuda.synchronize()
+        assert torch.equal(y_graph.view(torch.int16), y_fused.view(torch.int16)), T
+    e = rel_err(to_f64(y_graph), tb.oracle_y(big.x[:T], big.y0[:T], ids_h))
+    assert e <= BF16_TOL, f"y rel err {e:.3e}"

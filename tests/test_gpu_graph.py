@@ -86,6 +86,13 @@ CASES = [
     ("q_1024tok_13ad", 1024, 2048, 1024, [16] * 12 + [0], 16),
     # more tokens than a launch plans by itself: the plan kernel runs first
     ("o_1500tok_plan_kernel", 1500, 1024, 2048, [32] * 8, 32),
+    # ranks 8..128 (every rank-block count), some adapters without weights
+    ("r8_128_40ad_700tok", 700, 1024, 1536, ([8, 16, 32, 64, 128, 0, 24, 40] * 5), 128),
+    # the most adapters a device-planned call takes, rank 4 (V rows shorter
+    # than 16 bytes), about two tokens each
+    ("r4_256ad_512tok", 512, 512, 512, [4] * 256, 4),
+    # a single token
+    ("one_token", 1, 256, 512, [8, 8], 8),
 ]
 
 
@@ -170,7 +177,7 @@ def test_graph_capture_replays_with_new_ids_weights_and_tables(case):
             new_ids = rng.integers(0, N, size=T).astype(np.int32)
         elif rep == 3:
             # re-point adapter N-1 to weights of another rank (<= max_rank)
-            r_new = 16 if int(tb.ranks[N - 1]) != 16 else 8
+            r_new = min(16 if int(tb.ranks[N - 1]) != 16 else 8, max_rank)
             w = make_custom(300 + rep, h_in, h_out, [r_new], ids=np.zeros(1, np.int32))
             A_new, B_new = dev_bf16(w.A[0]), dev_bf16(w.B[0])
             spare.append((A_new, B_new))

@@ -294,3 +294,55 @@ def test_one_workspace_serves_both_planners():
         assert torch.equal(y_graph.view(torch.int16), y_fused.view(torch.int16)), T
     e = rel_err(to_f64(y_graph), tb.oracle_y(big.x[:T], big.y0[:T], ids_h))
     assert e <= BF16_TOL, f"y rel err {e:.3e}"
+
+
+# (T, h_in, h_out, number of adapters): widths multiples of 8 but not of 32,
+# token counts on both sides of the 1024 the fused launch plans by itself
+FUZZ = [(2, 72, 200, 3), (33, 264, 136, 1), (200, 520, 1032, 40), (511, 200, 264, 256), (1024, 1032, 520, 17),
+        (1025, 136, 264, 5), (1900, 264, 1032, 64), (700, 2056, 72, 9)]
+
+
+@pytest.mark.parametrize("case", range(len(FUZZ)))
+def test_graph_call_random_shapes(case):
+    """Seeded random batches through the device-planned call, eagerly and
+    from a replayed capture, against the fp64 oracle: mixed ranks 0..128
+    under a random max_rank, ids -1 and past N, unused adapters."""
+    import torch
+    import lora_adapter_batching_amd as L
+    T, h_in, h_out, N = FUZZ[case]
+    rng = np.random.default_rng(1300 + case)
+    ranks = [int(r) for r in rng.choice([0, 1, 4, 8, 12, 16, 24, 32, 40, 64, 96, 128], size=N)]
+    if max(ranks) == 0:
+        ranks[0] = 8
+    max_rank = int(min(128, max(ranks) + int(rng.integers(0, 16))))
+    ids = rng.integers(-1, N + 2, size=T).astype(np.int32)
+    if N > 2:
+        ids[ids == 1] = 0  # an adapter without tokens
+    prob = make_custom(1350 + case, h_in, h_out, ranks, scales="random", ids=ids, y0=True)
+    tb = _Tables(prob, max_rank)
+    x = dev_bf16(prob.x)
+    idt = torch.from_numpy(ids.copy()).cuda()
+    y = dev_bf16(prob.y0)
+    ws = L.new_workspace_graph(tb.ga, T)
+    _say(f"graph fuzz {case}: T={T} {h_in}->{h_out} N={N} max_rank={max_rank}")
+    L.sgmv_fused_graph(x, tb.ga, idt, y, ws)
+    torch.cuda.synchronize()
+    ref = tb.oracle_y(prob.x, prob.y0, ids)
+    got = to_f64(y)
+    assert rel_err(got, ref) <= BF16_TOL, "eager call"
+    inactive = np.array([not (0 <= i < N and ranks[i] > 0) for i in ids])
+    assert np.array_equal(got[inactive], oracle.widen(prob.y0)[inactive])
+    # the same call replayed from a capture, on new ids
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.sgmv_fused_graph(x, tb.ga, idt, y, ws)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        ids2 = rng.integers(-1, N + 2, size=T).astype(np.int32)
+        idt.copy_(torch.from_numpy(ids2))
+        y.copy_(dev_bf16(prob.y0))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e = rel_err(to_f64(y), tb.oracle_y(prob.x, prob.y0, ids2))
+        assert e <= BF16_TOL, f"replay {rep}: y rel err {e:.3e}"

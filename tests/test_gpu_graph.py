@@ -93,6 +93,8 @@ CASES = [
     ("r4_256ad_512tok", 512, 512, 512, [4] * 256, 4),
     # a single token
     ("one_token", 1, 256, 512, [8, 8], 8),
+    # the decode gate_up projection at full size (the graph-replay bench's widest call)
+    ("gate_up_2560x19456", 256, 2560, 19456, [32] * 8, 32),
 ]
 
 

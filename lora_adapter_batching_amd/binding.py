@@ -406,5 +406,32 @@ def inspect_plan(op: int, adapters, segments: Segments, options: int = 0, cus: i
     return out, rg
 
 
+def inspect_graph(num_adapters: int, h_in: int, h_out: int, max_rank: int, num_tokens: int, tiles: int,
+                  cus: int = 256, xccs: int = 8):
+    """Host-only listing of the workgroups of a device-planned call over
+    num_tokens ids whose batch turns out to have `tiles` tiles (stand-in
+    device tables, never dereferenced). Returns a numpy structured array with
+    the lora_plan_item_t fields."""
+    lib = load()
+    fn = lib.lora_inspect_graph
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.POINTER(CGraphAdapters), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
+    fake = 1 << 40
+    ga = CGraphAdapters(int(num_adapters), int(h_in), int(h_out), int(max_rank), fake, fake + 4096, fake + 8192,
+                        fake + 12288)
+    n = ctypes.c_int64(0)
+    cap = 1 << 12
+    while True:
+        items = (CPlanItem * cap)()
+        _check(fn(ctypes.byref(ga), int(num_tokens), int(tiles), int(cus), int(xccs), ctypes.cast(items, ctypes.c_void_p),
+                  cap, ctypes.byref(n)))
+        if n.value <= cap:
+            break
+        cap = int(n.value)
+    dt = np.dtype([(f, np.int32) for f, _ in CPlanItem._fields_])
+    return np.frombuffer(bytes(items), dtype=dt, count=int(n.value)).copy()
+
+
 def version() -> int:
     return int(load().lora_version())

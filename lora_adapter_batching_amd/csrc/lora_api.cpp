@@ -1470,6 +1470,12 @@ int sgmv_fused_graph_impl(const void* x, int64_t ldx, const lora_graph_adapters_
     return fail(LORA_UNSUPPORTED, "batch too large for the split layout of a device-planned call");
   if ((uint64_t)P.grid >= kEpochCall)
     return fail(LORA_UNSUPPORTED, "grid of %d workgroups too large for a device-planned call", P.grid);
+  if (self_plan && P.mode == kModeFusedDep && 4 * G.max_tiles <= dev.cus) {
+    // the small-batch split layouts: the workgroups re-lay them out for the
+    // tiles the batch has (column chunks per tile; grid and k split kept)
+    P.self_relayout = P.xcd_local ? 1 : 2;
+    P.self_slots = 2 * dev.cus;
+  }
   const int rbmax = a->max_rank <= 32 ? 1 : (a->max_rank <= 64 ? 2 : 4);
   e = launcher.fwd(P, rbmax, nullptr, nullptr);
   if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
@@ -1511,6 +1517,7 @@ struct Recorder final : Launcher {
   int32_t* ranges;
   int64_t rcap, nr = 0;
   int launches = 0;
+  int self_tiles = -1;  // launches planned inside themselves: the tiles their batch is taken to have
   void put(const lora_plan_item_t& r) {
     if (n < cap) items[n] = r;
     ++n;
@@ -1520,6 +1527,33 @@ struct Recorder final : Launcher {
     (void)rbmax;
     if (P.grid <= 0) return hipErrorInvalidConfiguration;
     const int launch = launches++;
+    if (P.self_ids) {
+      // what every workgroup of such a launch does once it has counted
+      // self_tiles tiles (the kernel's entry, on the host)
+      const int tiles = std::max(0, self_tiles);
+      int n_tiles = P.n_tiles, nc = P.nc, n_a = P.n_items_a, n_b = P.n_items_b, nblk = P.nblk;
+      if (self_relayout_needed(P.self_relayout, tiles, P.n_tiles)) {
+        nblk = self_relayout(P.self_relayout, tiles, P.ks, cdiv(P.N, 32), P.self_slots, P.grid, nc);
+        n_tiles = tiles;
+        n_a = tiles * P.ks;
+        n_b = tiles * nc;
+      }
+      for (int b = 0; b < P.grid; ++b) {
+        lora_plan_item_t r{};
+        r.launch = launch; r.phase = LORA_PHASE_FWD; r.block = b; r.grid = P.grid; r.mode = P.mode;
+        r.part = P.ks; r.aux = nc; r.adapter = -1; r.tok0 = -1; r.ntok = -1;
+        const FwdItem it = fwd_item_at(P.mode, P.xcd_local, P.xcd_remap, P.grid, n_tiles, P.ks, nc, n_a, n_b, b);
+        if (it.g < 0 || it.g >= tiles) {
+          r.kind = -1; r.tile = -1;
+        } else {
+          r.kind = it.kind; r.tile = it.g;
+          if (it.kind == kItemShrink) shrink_range(P.K, P.kchunk, it.c, r.lo, r.hi);
+          else expand_cols(P.N, nblk, it.c, r.lo, r.hi);
+        }
+        put(r);
+      }
+      return hipSuccess;
+    }
     for (int b = 0; b < P.grid; ++b) {
       lora_plan_item_t r{};
       r.launch = launch; r.phase = LORA_PHASE_FWD; r.block = b; r.grid = P.grid; r.mode = P.mode;
@@ -1682,6 +1716,29 @@ extern "C" int lora_inspect_plan(int op, int32_t num_proj, const lora_adapters_t
   }
   *n_items = rec.n;
   *n_ranges = rec.nr;
+  return st;
+}
+
+extern "C" int lora_inspect_graph(const lora_graph_adapters_t* adapters, int32_t num_tokens, int32_t tiles,
+                                  int32_t cus, int32_t xccs, lora_plan_item_t* items, int64_t items_cap,
+                                  int64_t* n_items) {
+  g_last_error.clear();
+  if (!adapters || !n_items || (items_cap > 0 && !items)) return fail(LORA_INVALID_ARGUMENT, "NULL argument");
+  if (cus < 8 || xccs < 1) return fail(LORA_INVALID_ARGUMENT, "cus must be >= 8 and xccs >= 1");
+  Recorder rec;
+  rec.d = DeviceInfo{cus, 100000, xccs};
+  rec.items = items; rec.cap = items_cap; rec.ranges = nullptr; rec.rcap = 0;
+  rec.self_tiles = tiles;
+  char* const base = reinterpret_cast<char*>((uintptr_t)1 << 40);
+  int st = check_graph_adapters(adapters);
+  if (!st) {
+    const GraphLayout G = graph_layout(adapters, std::max(num_tokens, 0));
+    st = sgmv_fused_graph_impl(base, adapters->h_in, adapters,
+                               reinterpret_cast<const int32_t*>(base + ((uintptr_t)1 << 36)), num_tokens,
+                               base + ((uintptr_t)2 << 36), adapters->h_out, base + ((uintptr_t)3 << 36), G.total,
+                               rec);
+  }
+  *n_items = rec.n;
   return st;
 }
 

@@ -35,7 +35,8 @@ struct TileInfo {
   float scale;
   uint64_t wptr, vptr;  // small plans with ptrs_in_plan: the segment's weight addresses
   const int* rows;      // batches planned inside the launch: the tile's rows (LDS)
-  uint64_t lid;         // ... and the launch id of the split hand-off
+  uint64_t lid;         // ... the launch id of the split hand-off
+  int nblk;             // ... and the 32-column blocks per expand chunk
 };
 
 template <typename PT>
@@ -178,6 +179,14 @@ __device__ __forceinline__ ProjView proj_view(const PT& P, int p) {
   return v;
 }
 
+// 32-column blocks per expand chunk of the item's projection (launches
+// planned inside themselves: the count their workgroups chose).
+template <typename PT>
+__device__ __forceinline__ int item_nblk(const PT& P, const TileInfo& t) {
+  if constexpr (PlanCap<PT>::self) return t.nblk;
+  return proj_view(P, t.proj).nblk;
+}
+
 template <typename PT>
 __device__ __forceinline__ const uint16_t* w_ptr(const PT& P, const TileInfo& t) {
   if constexpr (PlanCap<PT>::v <= kSmallSeg)
@@ -300,8 +309,9 @@ __device__ __forceinline__ uint32_t row_off(const PT& P, const TileInfo& t, cons
 // ---------------------------------------------------------------------------
 // Wave-level exclusive scan of the tokens per key, cnt[0..N] (LDS): each lane
 // takes a block of consecutive keys and the blocks' sums are scanned with
-// shuffles. visit(key, first sorted position, first tile, tokens) runs for
-// every key on the lane that holds it. Returns the tile count (all lanes).
+// shuffles. visit(j, key, first sorted position, first tile, tokens) runs
+// for each of the lane's kPer slots j (key = lane * kPer + j; slots past
+// key N carry no tokens). Returns the tile count (all lanes).
 template <typename F>
 __device__ __forceinline__ int scan_keys(const int* cnt, int N, F&& visit) {
   constexpr int kPer = (kMaxGraphAdapters + 1 + 63) / 64;
@@ -327,7 +337,7 @@ __device__ __forceinline__ int scan_keys(const int* cnt, int N, F&& visit) {
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int i = lane * kPer + j;
-    if (i <= N) visit(i, tok, tile, c[j]);
+    visit(j, i, tok, tile, c[j]);
     tok += c[j];
     tile += i < N ? (c[j] + kTileM - 1) / kTileM : 0;
   }
@@ -349,24 +359,57 @@ __device__ __forceinline__ bool adapter_active(int rank, int max_rank, uint64_t 
   return rank >= 1 && rank <= max_rank && wptr != 0 && vptr != 0;
 }
 
-// The tile of a batch planned inside the launch. Every workgroup reads the
-// ids (at most kSelfPlanTokens, kThreads apart per thread) and the adapter
-// tables (thread i: adapter i), counts the tokens per key, finds the key and
-// the place of tile g among its tokens, and ranks the key's tokens in
-// request order to collect the tile's rows in L.rows. A tile past the tile
-// count comes back with cnt 0. old_epoch: thread 0's read of the epoch as
-// it added its share (dep mode).
+// Planning inside the launch. Every workgroup reads the ids (at most
+// kSelfPlanTokens, kThreads apart per thread) and the adapter tables
+// (thread i: adapter i) and counts the tokens per key; wave 0 scans the
+// counts, picks the workgroup's item (for the split layouts, re-laid out for
+// the tiles the batch has) and finds the key and the place of the item's
+// tile among the key's tokens; the key's tokens are then ranked in request
+// order to collect the tile's rows in L.rows. Five barriers. The scratch
+// lives in LDS buffer 0, which the item reuses afterwards.
+constexpr int kSelfKPT = kSelfPlanTokens / kThreads;
+constexpr int kSelfCW = 4 * kSelfKPT;  // (token block, wave) pairs
+struct SelfLds {
+  int* cnt;       // [N + 1] tokens per key
+  int* cw;        // [kSelfCW] tokens of the tile's key in each (block of kThreads tokens, wave)
+  int* rank;      // [N] the adapter tables, with rank 0 for inactive adapters
+  float* scale;   // [N]
+  uint64_t* wp;   // [N]
+  uint64_t* vp;   // [N]
+  int* pick;      // item tile, chunk, kind, blocks per chunk; tile's key, place in the key, count, position
+};
+__device__ __forceinline__ SelfLds self_lds(const Lds& L) {
+  constexpr int K1 = kMaxGraphAdapters + 1;
+  static_assert((K1 + kSelfCW + 6 * kMaxGraphAdapters + 8) * 4 <= LdsBytes<1>::b0, "plan scratch fits buffer 0");
+  uint64_t* q = reinterpret_cast<uint64_t*>(L.b0);
+  SelfLds S;
+  S.wp = q;
+  S.vp = q + kMaxGraphAdapters;
+  int* p = reinterpret_cast<int*>(q + 2 * kMaxGraphAdapters);
+  S.rank = p;
+  S.scale = reinterpret_cast<float*>(p + kMaxGraphAdapters);
+  S.cnt = p + 2 * kMaxGraphAdapters;
+  S.cw = S.cnt + K1;
+  S.pick = S.cw + kSelfCW;
+  return S;
+}
+
+struct SelfItem {
+  FwdItem it;  // g < 0: no item
+  TileInfo t;
+};
+
+// The item and tile of workgroup b. item0: its item in the host's layout
+// (laid out for the most tiles), kept where re-laying out would not change
+// the column chunks. old_epoch: thread 0's read of the epoch as it added the
+// workgroup's share (dep mode), kept for the launch id.
 template <typename PT>
-__device__ __forceinline__ TileInfo self_tile_info(const PT& P, int g, const Lds& L, uint64_t old_epoch) {
-  constexpr int KPT = kSelfPlanTokens / kThreads;
+__device__ __forceinline__ SelfItem self_plan(const PT& P, const Lds& L, int b, FwdItem item0, uint64_t old_epoch) {
   static_assert(kMaxGraphAdapters <= kThreads, "one adapter per thread");
-  static_assert((2 * kMaxGraphAdapters + 1 + 4 * KPT + 4) * 4 <= LdsBytes<1>::b0, "plan scratch fits buffer 0");
+  constexpr int K1 = kMaxGraphAdapters + 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = P.self_N, T = P.self_T;
-  int* cnt = reinterpret_cast<int*>(L.b0);  // [N + 1] tokens per key
-  int* act = cnt + kMaxGraphAdapters + 1;   // [N] active adapters
-  int* wtot = act + kMaxGraphAdapters;      // [KPT][4] the tile's key: tokens per (block, wave)
-  int* sel = wtot + 4 * KPT;                // the tile: key, place in the key, count, sorted position
+  const SelfLds S = self_lds(L);
   // the global reads, all issued together
   int rk = 0;
   float sc = 0.f;
@@ -377,83 +420,110 @@ __device__ __forceinline__ TileInfo self_tile_info(const PT& P, int g, const Lds
     wp = P.self_A[tid];
     vp = P.self_B[tid];
   }
-  int key[KPT];
+  int key[kSelfKPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
+  for (int j = 0; j < kSelfKPT; ++j) {
     const int t = j * kThreads + tid;
     key[j] = t < T ? P.self_ids[t] : -1;
   }
-  for (int i = tid; i <= N; i += kThreads) cnt[i] = 0;
-  if (tid < N) act[tid] = adapter_active(rk, P.self_max_rank, wp, vp) ? 1 : 0;
+  for (int i = tid; i < K1; i += kThreads) S.cnt[i] = 0;
+  if (tid < N) {
+    S.rank[tid] = adapter_active(rk, P.self_max_rank, wp, vp) ? rk : 0;
+    S.scale[tid] = sc;
+    S.wp[tid] = wp;
+    S.vp[tid] = vp;
+  }
   if (tid == 0) *L.lid = (old_epoch >> kEpochShift) + 1;
   __syncthreads();
+  // keys and the count per key
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
+  for (int j = 0; j < kSelfKPT; ++j) {
     if (j * kThreads + tid < T) {
       const int id = key[j];
-      key[j] = (id >= 0 && id < N && act[id]) ? id : N;
-      atomicAdd(&cnt[key[j]], 1);
+      key[j] = (id >= 0 && id < N && S.rank[id] > 0) ? id : N;
+      atomicAdd(&S.cnt[key[j]], 1);
     }
   }
   __syncthreads();
+  // wave 0: tile offsets per key, the item, and the key of the item's tile
   if (wave == 0) {
-    const int tiles = scan_keys(cnt, N, [&](int i, int tok, int tile, int c) {
-      if (i < N && g >= tile && g < tile + (c + kTileM - 1) / kTileM) {
-        const int j0 = (g - tile) * kTileM;
-        sel[0] = i;
-        sel[1] = j0;
-        sel[2] = min(kTileM, c - j0);
-        sel[3] = tok + j0;
-      }
+    constexpr int kPer = (kMaxGraphAdapters + 1 + 63) / 64;
+    int kt[kPer], kk[kPer], kc[kPer];
+    const int tiles = scan_keys(S.cnt, N, [&](int j, int i, int tok, int tile, int c) {
+      kt[j] = tile;
+      kk[j] = tok;
+      kc[j] = i < N ? c : 0;  // key N (no adapter) has no tiles
     });
-    if (lane == 0 && g >= tiles) {
-      sel[0] = -1;
-      sel[2] = 0;
+    FwdItem it = item0;
+    int nblk = P.nblk;
+    if (self_relayout_needed(P.self_relayout, tiles, P.n_tiles)) {
+      int nc;
+      nblk = self_relayout(P.self_relayout, tiles, P.ks, (P.N + 31) >> 5, P.self_slots, P.grid, nc);
+      it = fwd_item_at(P.mode, P.xcd_local, P.xcd_remap, P.grid, tiles, P.ks, nc, tiles * P.ks, tiles * nc, b);
+    }
+    if (it.g >= tiles) it.g = -1;  // a tile past the batch's
+    if (lane == 0) {
+      S.pick[0] = it.g;
+      S.pick[1] = it.c;
+      S.pick[2] = it.kind;
+      S.pick[3] = nblk;
+    }
+    if (it.g >= 0) {
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int i = lane * kPer + q;
+        if (i < N && it.g >= kt[q] && it.g < kt[q] + (kc[q] + kTileM - 1) / kTileM) {
+          const int j0 = (it.g - kt[q]) * kTileM;
+          S.pick[4] = i;
+          S.pick[5] = j0;
+          S.pick[6] = min(kTileM, kc[q] - j0);
+          S.pick[7] = kk[q] + j0;
+        }
+      }
     }
   }
   __syncthreads();
-  TileInfo t{};
-  t.g = g;
-  t.cnt = __builtin_amdgcn_readfirstlane(sel[2]);
-  if (t.cnt <= 0) return t;
-  const int a = __builtin_amdgcn_readfirstlane(sel[0]);
-  const int j0 = __builtin_amdgcn_readfirstlane(sel[1]);
-  t.p0 = __builtin_amdgcn_readfirstlane(sel[3]);
-  // the key's tokens ranked in request order: by lane within a wave, then by
-  // wave, then by block of kThreads tokens
-  int pre[KPT];
+  SelfItem R;
+  R.it.g = __builtin_amdgcn_readfirstlane(S.pick[0]);
+  R.it.c = __builtin_amdgcn_readfirstlane(S.pick[1]);
+  R.it.kind = __builtin_amdgcn_readfirstlane(S.pick[2]);
+  if (R.it.g < 0) return R;
+  TileInfo& t = R.t;
+  t.g = R.it.g;
+  t.nblk = __builtin_amdgcn_readfirstlane(S.pick[3]);
+  const int a = __builtin_amdgcn_readfirstlane(S.pick[4]);
+  const int j0 = __builtin_amdgcn_readfirstlane(S.pick[5]);
+  t.cnt = __builtin_amdgcn_readfirstlane(S.pick[6]);
+  t.p0 = __builtin_amdgcn_readfirstlane(S.pick[7]);
+  // this thread's tokens of key a, placed in request order: by lane within
+  // a wave, then by wave, then by block of kThreads tokens
+  int pre[kSelfKPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
+  for (int j = 0; j < kSelfKPT; ++j) {
     const uint64_t m = __builtin_amdgcn_ballot_w64(key[j] == a);
     pre[j] = __builtin_popcountll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wtot[4 * j + wave] = __builtin_popcountll(m);
+    if (lane == 0) S.cw[4 * j + wave] = __builtin_popcountll(m);
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
+  for (int j = 0; j < kSelfKPT; ++j) {
     if (key[j] == a) {
       int r = pre[j] - j0;
-      for (int q = 0; q < 4 * j + wave; ++q) r += wtot[q];
+      for (int q = 0; q < 4 * j + wave; ++q) r += S.cw[q];
       if (r >= 0 && r < kTileM) L.rows[r] = j * kThreads + tid;
     }
   }
-  if (tid == a) {
-    L.ti->rank = rk;
-    L.ti->scale = sc;
-    L.ti->wptr = wp;
-    L.ti->vptr = vp;
-  }
-  __syncthreads();
   t.adapter = a;
-  t.rank = __builtin_amdgcn_readfirstlane(L.ti->rank);
-  t.scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, L.ti->scale)));
-  t.wptr = uniform64(L.ti->wptr);
-  t.vptr = uniform64(L.ti->vptr);
+  t.rank = __builtin_amdgcn_readfirstlane(S.rank[a]);
+  t.scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, S.scale[a])));
+  t.wptr = uniform64(S.wp[a]);
+  t.vptr = uniform64(S.vp[a]);
   t.slot = 0;
   t.proj = 0;
   t.rows = L.rows;
   t.lid = uniform64(*L.lid);
-  return t;
+  __syncthreads();
+  return R;
 }
 
 // ---------------------------------------------------------------------------
@@ -802,7 +872,7 @@ __device__ __forceinline__ StgCtx<RB> stg_ctx(const PT& P, const TileInfo& t, in
     C.vrow[j] = (uint16_t)row;
     C.vlds[j] = (uint16_t)(row * G::RP + 8 * (f - row * rv));
   }
-  expand_cols(pv.N, pv.nblk, c, C.c0, C.c1);
+  expand_cols(pv.N, item_nblk(P, t), c, C.c0, C.c1);
   C.oscale = P.scale_in_shrink ? 1.f : t.scale;
   return C;
 }
@@ -965,7 +1035,7 @@ __device__ __forceinline__ ExpCtx<RB> exp_ctx(const PT& P, const TileInfo& t, in
   C.vr = mk_rsrc(v_ptr(P, t), (int64_t)pv.N * C.ldv * 2);
   C.rank = t.rank;
   C.kbn = (t.rank + 15) >> 4;
-  expand_cols(pv.N, pv.nblk, c, C.c0, C.c1);
+  expand_cols(pv.N, item_nblk(P, t), c, C.c0, C.c1);
   C.nb = (C.c1 - C.c0 + 31) >> 5;
   C.oscale = P.scale_in_shrink ? 1.f : t.scale;
   return C;
@@ -1013,8 +1083,6 @@ __device__ __forceinline__ void store_u_from_lds(const PT& P, const TileInfo& t,
 // stores cover whole rows.
 template <int RB>
 __device__ __forceinline__ bool direct_expand(int nblk) { return nblk <= 4; }
-template <typename PT>
-__device__ __forceinline__ int item_nblk(const PT& P, const TileInfo& t) { return proj_view(P, t.proj).nblk; }
 
 template <int RB, typename PT>
 __device__ __forceinline__ void expand_from_lds(const PT& P, const TileInfo& t, int c, const float* Pl,
@@ -1352,16 +1420,24 @@ __global__ __launch_bounds__(kThreads, 2) void sgmv_fwd_kernel(PT P) {
   asm volatile("" ::"s"(P.mode), "s"(P.xcd_local), "s"(P.xcd_remap), "s"(P.n_tiles), "s"(P.ks),
                "s"(P.nc), "s"(P.n_items_a), "s"(P.n_items_b), "s"(P.grid), "s"(P.n_seg),
                "s"(P.ptrs_in_plan), "s"(P.seg_tile0[0]), "s"(P.seg_tok0[0]), "s"(P.seg_ntok[0]));
-  const FwdItem it = fwd_item(P, b);
-  const int g = it.g, c = it.c, kind = it.kind;
-  if (g >= 0) {
-    TileInfo t;
-    if constexpr (PlanCap<PT>::self) t = self_tile_info(P, g, L, old_epoch);
-    else t = tile_info(P, g, L.ti);
-    if (t.cnt <= 0) return;  // a tile past the count of a batch planned on the device
-    if (RBMAX == 1 || t.rank <= 32) run_item<1>(P, L, t, kind, c);
-    else if (RBMAX == 2 || t.rank <= 64) run_item<(RBMAX >= 2 ? 2 : 1)>(P, L, t, kind, c);
-    else run_item<RBMAX>(P, L, t, kind, c);
+  if constexpr (PlanCap<PT>::self) {
+    // every workgroup plans: its item depends on the tiles the batch has
+    const SelfItem R = self_plan(P, L, b, fwd_item(P, b), old_epoch);
+    if (R.it.g < 0) return;  // no item, or a tile past the batch's
+    const TileInfo& t = R.t;
+    if (RBMAX == 1 || t.rank <= 32) run_item<1>(P, L, t, R.it.kind, R.it.c);
+    else if (RBMAX == 2 || t.rank <= 64) run_item<(RBMAX >= 2 ? 2 : 1)>(P, L, t, R.it.kind, R.it.c);
+    else run_item<RBMAX>(P, L, t, R.it.kind, R.it.c);
+  } else {
+    const FwdItem it = fwd_item(P, b);
+    const int g = it.g, c = it.c, kind = it.kind;
+    if (g >= 0) {
+      const TileInfo t = tile_info(P, g, L.ti);
+      if (t.cnt <= 0) return;  // a tile past the count of a batch planned on the device
+      if (RBMAX == 1 || t.rank <= 32) run_item<1>(P, L, t, kind, c);
+      else if (RBMAX == 2 || t.rank <= 64) run_item<(RBMAX >= 2 ? 2 : 1)>(P, L, t, kind, c);
+      else run_item<RBMAX>(P, L, t, kind, c);
+    }
   }
 }
 
@@ -1452,9 +1528,11 @@ __global__ __launch_bounds__(kPlanThreads) void dev_plan_kernel(DevPlanArgs a) {
   __syncthreads();
   // token and tile offsets per key
   if (wave == 0) {
-    const int tiles = scan_keys(cnt, N, [&](int i, int tok, int tile, int) {
-      start[i] = tok;
-      tile0[i] = tile;
+    const int tiles = scan_keys(cnt, N, [&](int, int i, int tok, int tile, int) {
+      if (i <= N) {
+        start[i] = tok;
+        tile0[i] = tile;
+      }
     });
     if (lane == 0) *a.count = min(tiles, a.max_tiles);
   }

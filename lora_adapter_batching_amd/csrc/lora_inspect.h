@@ -72,6 +72,17 @@ int lora_inspect_plan(int op, int32_t num_proj, const lora_adapters_t* const* ad
                       lora_plan_item_t* items, int64_t items_cap, int64_t* n_items, int32_t* ranges,
                       int64_t ranges_cap, int64_t* n_ranges);
 
+/* The workgroups of a device-planned call (lora_sgmv_fused_graph) over
+ * num_tokens ids whose batch has `tiles` 32-token tiles: the launch the call
+ * makes (for up to 1024 tokens, the fused launch with the item each
+ * workgroup picks once it has counted the tiles; above, the plan kernel and
+ * then the fused launch). Items carry launch, phase, block, grid, mode,
+ * kind, tile and the k range (shrink parts) or column range (expands);
+ * adapter, tok0 and ntok are -1 (they depend on the ids). The adapter
+ * tables are never dereferenced. Host only. */
+int lora_inspect_graph(const lora_graph_adapters_t* adapters, int32_t num_tokens, int32_t tiles, int32_t cus,
+                       int32_t xccs, lora_plan_item_t* items, int64_t items_cap, int64_t* n_items);
+
 #ifdef __cplusplus
 }
 #endif

@@ -126,6 +126,13 @@ struct FwdHeader {
   int32_t self_T;
   int32_t self_N;
   int32_t self_max_rank;
+  // How such a launch re-lays its split layout out for the tiles the batch
+  // turns out to have (the grid, laid out for the most tiles, and the k
+  // split stay): 0 keeps the host layout, 1 the XCD-local and 2 the spread
+  // small-batch layouts with the column chunks per tile recomputed
+  // (self_relayout); self_slots = resident workgroups of the GPU.
+  int32_t self_relayout;
+  int32_t self_slots;
   // Projections 1 .. kMaxProj-1 of a multi-projection launch (several
   // LoRA-wrapped projections over the same x); projection 0 uses Y, ldy, N,
   // nblk, Wtab and Vtab above, and entry 0 of these arrays is unused.
@@ -174,43 +181,88 @@ struct FwdItem {
   int kind;  // ItemKind
 };
 
-// Item of workgroup b.
-__host__ __device__ __forceinline__ FwdItem fwd_item(const FwdHeader& P, int b) {
+// Item of workgroup b in a layout of n_tiles tiles, ks shrink parts and nc
+// column chunks per tile (split modes: n_items_a parts, n_items_b expands).
+__host__ __device__ __forceinline__ FwdItem fwd_item_at(int mode, int xcd_local, int xcd_remap, int grid,
+                                                         int n_tiles, int ks, int nc, int n_items_a,
+                                                         int n_items_b, int b) {
   FwdItem it{-1, 0, kItemShrink};
-  if (P.mode == kModeFusedDep) {
-    if (P.xcd_local) {
+  if (mode == kModeFusedDep) {
+    if (xcd_local) {
       // XCD x = b % 8 runs tiles x, x + 8, ...: their shrink parts first,
       // then their expands (workgroup b runs on XCD b % 8)
       const int x = b & 7, j = b >> 3;
-      const int tx = (P.n_tiles - x + 7) >> 3;
-      if (j < tx * P.ks) {
-        const int i = j / P.ks;
-        it = FwdItem{x + 8 * i, j - i * P.ks, kItemShrink};
-      } else if (j < tx * (P.ks + P.nc)) {
-        const int j2 = j - tx * P.ks, i = j2 / P.nc;
-        it = FwdItem{x + 8 * i, j2 - i * P.nc, kItemExpandWait};
+      const int tx = (n_tiles - x + 7) >> 3;
+      if (j < tx * ks) {
+        const int i = j / ks;
+        it = FwdItem{x + 8 * i, j - i * ks, kItemShrink};
+      } else if (j < tx * (ks + nc)) {
+        const int j2 = j - tx * ks, i = j2 / nc;
+        it = FwdItem{x + 8 * i, j2 - i * nc, kItemExpandWait};
       }
-    } else if (b < P.n_items_a) {
-      const int g = b / P.ks;
-      it = FwdItem{g, b - g * P.ks, kItemShrink};
-    } else if (b < P.n_items_a + P.n_items_b) {
-      const int i = b - P.n_items_a, g = i / P.nc;
-      it = FwdItem{g, i - g * P.nc, kItemExpandWait};
+    } else if (b < n_items_a) {
+      const int g = b / ks;
+      it = FwdItem{g, b - g * ks, kItemShrink};
+    } else if (b < n_items_a + n_items_b) {
+      const int i = b - n_items_a, g = i / nc;
+      it = FwdItem{g, i - g * nc, kItemExpandWait};
     }
     return it;
   }
   int i = b;
-  if (P.xcd_remap) {
-    const int q = P.grid >> 3;
+  if (xcd_remap) {
+    const int q = grid >> 3;
     i = (b & 7) * q + (b >> 3);
   }
-  const int per = P.mode == kModeShrink ? P.ks : P.nc;
-  const int kind = P.mode == kModeShrink ? kItemShrink : (P.mode == kModeExpand ? kItemExpand : kItemFusedTile);
-  if (i < P.n_items_a) {
+  const int per = mode == kModeShrink ? ks : nc;
+  const int kind = mode == kModeShrink ? kItemShrink : (mode == kModeExpand ? kItemExpand : kItemFusedTile);
+  if (i < n_items_a) {
     const int g = i / per;
     it = FwdItem{g, i - g * per, kind};
   }
   return it;
+}
+
+// Item of workgroup b.
+__host__ __device__ __forceinline__ FwdItem fwd_item(const FwdHeader& P, int b) {
+  return fwd_item_at(P.mode, P.xcd_local, P.xcd_remap, P.grid, P.n_tiles, P.ks, P.nc, P.n_items_a, P.n_items_b,
+                     b);
+}
+
+// Whether a launch planned inside itself re-lays out for `tiles` tiles (its
+// grid laid out for max_tiles): the column chunks change with the tile count
+// only through the tiles per XCD (kind 1, XCD-local) or the tiles (kind 2);
+// otherwise the host's layout, whose items of tiles past the count are
+// idle, is kept.
+__host__ __device__ inline bool self_relayout_needed(int kind, int tiles, int max_tiles) {
+  if (kind == 0 || tiles <= 0) return false;
+  return kind == 1 ? ((tiles + 7) >> 3) != ((max_tiles + 7) >> 3) : tiles != max_tiles;
+}
+
+// Column chunks per tile of a launch planned inside itself, for the `tiles`
+// tiles its batch has (1 <= tiles <= the tiles its grid was laid out for):
+// the host's small-batch rule (about two resident workgroups per CU; for
+// the XCD-local layout per XCD) on the actual tiles, clamped so that every
+// item still falls inside the grid. kind: 1 XCD-local, 2 spread. Returns
+// nblk (32-column blocks per chunk); nc = the chunks.
+__host__ __device__ inline int self_relayout(int kind, int tiles, int ks, int nblocks, int slots, int grid,
+                                             int& nc) {
+  int n;
+  if (kind == 1) {
+    const int per_xcd = (tiles + 7) / 8;
+    n = slots / 8 / per_xcd - ks;
+    const int fit = grid / (8 * per_xcd) - ks;
+    n = n < fit ? n : fit;
+  } else {
+    n = slots / tiles - ks;
+    const int fit = grid / tiles - ks;
+    n = n < fit ? n : fit;
+  }
+  n = n < nblocks ? n : nblocks;
+  n = n > 1 ? n : 1;
+  const int nblk = (nblocks + n - 1) / n;
+  nc = (nblocks + nblk - 1) / nblk;
+  return nblk;
 }
 
 // k range [kb, ke) of shrink part c.

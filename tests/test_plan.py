@@ -369,3 +369,50 @@ def test_backward_plan_without_tokens_only_zero_fills():
         assert len(ranges) == 0
         items, _ = B.inspect_plan(B.OP_BACKWARD, a, sg, B.INSPECT_WITH_DX | B.INSPECT_ACCUMULATE)
         assert len(items) == 0
+
+
+GRAPH_CASES = [
+    # (adapters, h_in, h_out, max_rank, tokens): decode q and gate_up, many small adapters, odd widths
+    (8, 2560, 2560, 32, 256),
+    (8, 2560, 19456, 32, 256),
+    (13, 2048, 1024, 16, 1024),
+    (40, 1024, 1536, 128, 700),
+    (256, 512, 512, 4, 512),
+    (3, 200, 264, 64, 37),
+]
+
+
+@pytest.mark.parametrize("case", GRAPH_CASES, ids=[f"{c[0]}ad_{c[1]}x{c[2]}_r{c[3]}_{c[4]}tok" for c in GRAPH_CASES])
+@pytest.mark.parametrize("xccs", [8, 1])
+def test_device_planned_layout_covers_every_tile_count(case, xccs):
+    """A device-planned launch of up to 1024 tokens lays its grid out for the
+    most tiles the ids could need; its workgroups then re-lay the split
+    layout out for the tiles the batch has. For every possible tile count:
+    each tile's shrink parts cover [0, h_in) once, its expand items cover
+    [0, h_out) once, no item names a tile past the count, and every item
+    lies inside the grid (the listing has exactly one record per
+    workgroup)."""
+    N, h_in, h_out, max_rank, T = case
+    max_tiles = -(-T // 32) + min(N, T)
+    grids = set()
+    for tiles in range(0, max_tiles + 1):
+        items = B.inspect_graph(N, h_in, h_out, max_rank, T, tiles, cus=256, xccs=xccs)
+        f = items[items["phase"] == B.PHASE_FWD]
+        assert len(f) == int(f["grid"][0]), "one record per workgroup"
+        assert np.array_equal(np.sort(f["block"]), np.arange(len(f)))
+        grids.add(int(f["grid"][0]))
+        busy = f[f["kind"] >= 0]
+        assert np.all(busy["tile"] < tiles), "an item past the batch's tiles"
+        split = np.any(busy["kind"] == 0)
+        for g in range(tiles):
+            mine = busy[busy["tile"] == g]
+            if split:
+                cov = np.zeros(h_in, np.int32)
+                for r in mine[mine["kind"] == 0]:
+                    cov[r["lo"]:r["hi"]] += 1
+                assert np.all(cov == 1), f"tiles={tiles}: shrink parts of tile {g}"
+            cov = np.zeros(h_out, np.int32)
+            for r in mine[mine["kind"] != 0]:
+                cov[r["lo"]:r["hi"]] += 1
+            assert np.all(cov == 1), f"tiles={tiles}: expand columns of tile {g}"
+    assert len(grids) == 1, "the grid depends only on the token count"

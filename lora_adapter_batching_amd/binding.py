@@ -369,7 +369,7 @@ class CPlanItem(ctypes.Structure):
 
 
 INSPECT_WITH_U, INSPECT_WITH_DX, INSPECT_ACCUMULATE = 1, 2, 4
-PHASE_FWD, PHASE_WGRAD, PHASE_REDUCE, PHASE_TRANSPOSE = 0, 1, 2, 3
+PHASE_FWD, PHASE_WGRAD, PHASE_REDUCE, PHASE_TRANSPOSE, PHASE_PLAN = 0, 1, 2, 3, 4
 
 
 def inspect_plan(op: int, adapters, segments: Segments, options: int = 0, cus: int = 256, xccs: int = 8):

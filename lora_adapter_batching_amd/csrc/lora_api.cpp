@@ -1527,9 +1527,9 @@ struct Recorder final : Launcher {
     (void)rbmax;
     if (P.grid <= 0) return hipErrorInvalidConfiguration;
     const int launch = launches++;
-    if (P.self_ids) {
-      // what every workgroup of such a launch does once it has counted
-      // self_tiles tiles (the kernel's entry, on the host)
+    if (P.self_ids || P.dev_tiles) {
+      // a device-planned launch: what its workgroups do once the batch has
+      // self_tiles tiles (counted by each workgroup, or by the plan kernel)
       const int tiles = std::max(0, self_tiles);
       int n_tiles = P.n_tiles, nc = P.nc, n_a = P.n_items_a, n_b = P.n_items_b, nblk = P.nblk;
       if (self_relayout_needed(P.self_relayout, tiles, P.n_tiles)) {

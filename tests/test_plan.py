@@ -379,6 +379,7 @@ GRAPH_CASES = [
     (40, 1024, 1536, 128, 700),
     (256, 512, 512, 4, 512),
     (3, 200, 264, 64, 37),
+    (8, 1024, 2048, 32, 1500),  # more tokens than a launch plans by itself: the plan kernel's tiles
 ]
 
 
@@ -397,6 +398,7 @@ def test_device_planned_layout_covers_every_tile_count(case, xccs):
     grids = set()
     for tiles in range(0, max_tiles + 1):
         items = B.inspect_graph(N, h_in, h_out, max_rank, T, tiles, cus=256, xccs=xccs)
+        assert np.any(items["phase"] == B.PHASE_PLAN) == (T > 1024)
         f = items[items["phase"] == B.PHASE_FWD]
         assert len(f) == int(f["grid"][0]), "one record per workgroup"
         assert np.array_equal(np.sort(f["block"]), np.arange(len(f)))

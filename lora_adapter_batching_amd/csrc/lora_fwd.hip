@@ -692,17 +692,21 @@ struct PFrags {
 
 // B-operand fragments of P^T from the LDS tile Pl[token][k]: lane supplies
 // P[token = lane%32][16kb + 8(lane/32) + e], zero for k >= rank.
+// The 8 values of a lane are read as two 16-byte vectors (the tile holds
+// 32 * RB columns, so every read is inside it) and the columns past the
+// rank are zeroed in registers.
 template <int RB>
 __device__ __forceinline__ void build_pfrags(const float* Pl, int rank, int lane, PFrags<RB>& F) {
   const int n = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int kb = 0; kb < 2 * RB; ++kb) {
-    float f[8];
+    const int k0 = 16 * kb + 8 * h;
+    const float4 a = *reinterpret_cast<const float4*>(Pl + n * kLdp + k0);
+    const float4 b = *reinterpret_cast<const float4*>(Pl + n * kLdp + k0 + 4);
+    float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = 16 * kb + 8 * h + e;
-      f[e] = (k < rank) ? Pl[n * kLdp + k] : 0.f;
-    }
+    for (int e = 0; e < 8; ++e)
+      if (k0 + e >= rank) f[e] = 0.f;
     split8(f, F.hi[kb], F.lo[kb]);
   }
 }

@@ -1191,39 +1191,49 @@ __device__ __forceinline__ void sum_parts_to_lds(const PT& P, const TileInfo& t,
   const __amdgpu_buffer_rsrc_t r = mk_rsrc(partial_ptr(P, t.g, 0), (int64_t)P.ks * kTileM * P.rpad * 4);
   const uint32_t part_bytes = (uint32_t)(kTileM * P.rpad * 4);
   // a part is stored rank-major, P^T [rpad][32 tokens]: element e of the
-  // first RC rows is (rank e / 32, token e % 32) at float offset e, so the
-  // loads are contiguous across the workgroup
+  // first RC rows is (rank e / 32, token e % 32) at float offset e. A thread
+  // loads 16-byte vectors (elements 4v .. 4v + 3, one rank, four tokens),
+  // so the loads are contiguous across the workgroup
+  constexpr int VPT = EPT / 4;  // vectors per thread
   float s[EPT];
-  uint32_t off[EPT];
+  uint32_t off[VPT];
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int e = threadIdx.x + kThreads * j;
-    off[j] = (uint32_t)(e * 4);
-    s[j] = 0.f;
-  }
+  for (int j = 0; j < VPT; ++j) off[j] = (uint32_t)((threadIdx.x + kThreads * j) * 16);
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) s[j] = 0.f;
   constexpr int PD = 8 / RB;
   for (int q0 = 0; q0 < P.ks; q0 += PD) {
-    float v[PD][EPT];
+    u32x4 v[PD][VPT];
 #pragma unroll
     for (int d = 0; d < PD; ++d)
 #pragma unroll
-      for (int j = 0; j < EPT; ++j) {
+      for (int j = 0; j < VPT; ++j) {
         const uint32_t o = q0 + d < P.ks ? (uint32_t)(q0 + d) * part_bytes + off[j] : kOff;
-        v[d][j] = __builtin_bit_cast(float, device_scope ? __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, kAuxDev)
-                                                         : __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0));
+        v[d][j] = device_scope ? __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, kAuxDev)
+                               : __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0);
       }
 #pragma unroll
     for (int d = 0; d < PD; ++d)
 #pragma unroll
-      for (int j = 0; j < EPT; ++j)
-        if (q0 + d < P.ks) s[j] = (q0 + d == 0) ? v[d][j] : s[j] + v[d][j];
+      for (int j = 0; j < VPT; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q0 + d < P.ks) {
+            // through a named value: a bit cast of the vector element
+            // itself is compiled as a read of element 0
+            const uint32_t w = v[d][j][q];
+            const float f = __builtin_bit_cast(float, w);
+            s[4 * j + q] = (q0 + d == 0) ? f : s[4 * j + q] + f;
+          }
   }
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int e = threadIdx.x + kThreads * j;
-    const int k = e / kTileM, n = e - k * kTileM;
-    Pl[n * kLdp + k] = s[j] * ps;
-  }
+  for (int j = 0; j < VPT; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * (threadIdx.x + kThreads * j) + q;
+      const int k = e / kTileM, n = e - k * kTileM;
+      Pl[n * kLdp + k] = s[4 * j + q] * ps;
+    }
   lds_sync();
 }
 

@@ -72,3 +72,20 @@ def test_no_scratch(fwd_asm, bwd_asm):
     for text in (fwd_asm, bwd_asm):
         sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", text)
         assert sizes and all(int(v) == 0 for v in sizes), sizes
+
+
+def test_part_loads_are_whole_device_scope_vectors(fwd_asm):
+    """The split hand-off sums its parts from 16-byte device-scope loads:
+    every forward kernel instance has some, and no part is read with
+    narrower device-scope loads (a bit cast of a vector element once turned
+    the vector loads into single-word reads of element 0)."""
+    kernels = re.split(r"\n(?=_ZN4lora15sgmv_fwd_kernel\S*:)", fwd_asm)
+    n = 0
+    for k in kernels:
+        if not k.startswith("_ZN4lora15sgmv_fwd_kernel"):
+            continue
+        body = k.split(".Lfunc_end")[0]
+        n += 1
+        assert re.search(r"buffer_load_dwordx4 .*\bsc1\b", body), k.split(":")[0]
+        assert not re.search(r"buffer_load_dword v\d+, .*\bsc1\b", body), k.split(":")[0]
+    assert n > 0

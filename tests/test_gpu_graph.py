@@ -298,6 +298,63 @@ def test_one_workspace_serves_both_planners():
     assert e <= BF16_TOL, f"y rel err {e:.3e}"
 
 
+# Batches far above the 1024 tokens a launch plans by itself, in the layouts
+# the planner picks for them: the medium split (a prefill-sized batch; an
+# MLP-up batch with ranks to 128) and one on-chip item per tile (more tiles
+# than resident workgroups).
+BIG = [
+    ("prefill_8192tok_4096", 8192, 4096, 4096, [16] * 8, 16),
+    ("mlp_up_4096tok_r8_128", 4096, 4096, 14336, [8, 16, 32, 64, 128, 0, 32, 16] * 4, 128),
+    ("on_chip_20000tok", 20000, 1024, 1024, [8, 16, 32, 64] * 4, 64),
+]
+
+
+@pytest.mark.parametrize("case", BIG, ids=[c[0] for c in BIG])
+def test_graph_call_large_batches(case):
+    """Large request-order batches through the plan kernel: the eager call
+    gives the same bits as lora_sgmv_fused and matches the oracle; a replay
+    of its capture on new ids (some -1) matches the oracle too."""
+    import torch
+    import lora_adapter_batching_amd as L
+    name, T, h_in, h_out, ranks, max_rank = case
+    prob = _problem(41, T, h_in, h_out, ranks)
+    tb = _Tables(prob, max_rank)
+    x = dev_bf16(prob.x)
+    ids = torch.from_numpy(prob.token_ids.copy()).cuda()
+    y = dev_bf16(prob.y0)
+    ws = L.new_workspace_graph(tb.ga, T)
+    _say(f"graph call eager {name}")
+    L.sgmv_fused_graph(x, tb.ga, ids, y, ws)
+    perm, st, ad = L.segments_from_ids(prob.token_ids, prob.N)
+    ad_h = L.Adapters(tb.A, tb.B, prob.ranks, prob.scales, h_in, h_out)
+    sg = L.Segments(st, ad, torch.from_numpy(perm.copy()).cuda())
+    y_fused = dev_bf16(prob.y0)
+    _say(f"lora_sgmv_fused {name}")
+    L.sgmv_fused(x, ad_h, sg, y_fused, None, L.new_workspace(L.OP_FUSED, ad_h, sg))
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_fused.view(torch.int16))
+    e = rel_err(to_f64(y), tb.oracle_y(prob.x, prob.y0, prob.token_ids))
+    assert e <= BF16_TOL, f"eager: y rel err {e:.3e}"
+    g = torch.cuda.CUDAGraph()
+    _say(f"capture {name}")
+    with torch.cuda.graph(g):
+        L.sgmv_fused_graph(x, tb.ga, ids, y, ws)
+    rng = np.random.default_rng(42)
+    new_ids = rng.integers(0, prob.N, size=T).astype(np.int32)
+    new_ids[rng.random(T) < 0.1] = -1
+    ids.copy_(torch.from_numpy(new_ids))
+    y.copy_(dev_bf16(prob.y0))
+    torch.cuda.synchronize()
+    _say(f"replay {name}")
+    g.replay()
+    torch.cuda.synchronize()
+    got = to_f64(y)
+    e = rel_err(got, tb.oracle_y(prob.x, prob.y0, new_ids))
+    assert e <= BF16_TOL, f"replay: y rel err {e:.3e}"
+    inactive = np.array([not (0 <= i < prob.N and tb.ranks[i] > 0) for i in new_ids])
+    assert np.array_equal(got[inactive], oracle.widen(prob.y0)[inactive])
+
+
 # (T, h_in, h_out, number of adapters): widths multiples of 8 but not of 32,
 # token counts on both sides of the 1024 the fused launch plans by itself
 FUZZ = [(2, 72, 200, 3), (33, 264, 136, 1), (200, 520, 1032, 40), (511, 200, 264, 256), (1024, 1032, 520, 17),

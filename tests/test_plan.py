@@ -418,3 +418,46 @@ def test_device_planned_layout_covers_every_tile_count(case, xccs):
                 cov[r["lo"]:r["hi"]] += 1
             assert np.all(cov == 1), f"tiles={tiles}: expand columns of tile {g}"
     assert len(grids) == 1, "the grid depends only on the token count"
+
+
+GRAPH_BIG = [
+    # (adapters, h_in, h_out, max_rank, tokens): the large batches of the GPU
+    # graph tests (medium split twice, then one on-chip item per tile)
+    (8, 4096, 4096, 16, 8192),
+    (32, 4096, 14336, 128, 4096),
+    (16, 1024, 1024, 64, 20000),
+]
+
+
+@pytest.mark.parametrize("case", GRAPH_BIG, ids=[f"{c[0]}ad_{c[1]}x{c[2]}_r{c[3]}_{c[4]}tok" for c in GRAPH_BIG])
+def test_device_planned_large_batches_cover_every_tile(case):
+    """Above 1024 tokens the plan kernel runs first and the fused launch is
+    laid out for the most tiles the ids could need; a tile past the batch's
+    count has no work (its workgroups return). For a few tile counts: each
+    tile's shrink parts cover [0, h_in) once and its expand items [0, h_out)
+    once, every item lies inside the grid, and the grid does not depend on
+    the tile count."""
+    N, h_in, h_out, max_rank, T = case
+    max_tiles = -(-T // 32) + min(N, T)
+    grids = set()
+    for tiles in sorted({1, max_tiles // 3, max_tiles - 1, max_tiles}):
+        items = B.inspect_graph(N, h_in, h_out, max_rank, T, tiles, cus=256, xccs=8)
+        assert np.any(items["phase"] == B.PHASE_PLAN)
+        f = items[items["phase"] == B.PHASE_FWD]
+        assert len(f) == int(f["grid"][0]), "one record per workgroup"
+        assert np.array_equal(np.sort(f["block"]), np.arange(len(f)))
+        grids.add(int(f["grid"][0]))
+        busy = f[f["kind"] >= 0]
+        assert np.all(busy["tile"] < tiles), "an item past the batch's tiles"
+        parts = busy[busy["kind"] == 0]
+        if len(parts):
+            cov = np.zeros((tiles, h_in + 1), np.int32)
+            np.add.at(cov, (parts["tile"], parts["lo"]), 1)
+            np.add.at(cov, (parts["tile"], parts["hi"]), -1)
+            assert np.all(np.cumsum(cov, axis=1)[:, :h_in] == 1), f"tiles={tiles}: shrink parts"
+        ex = busy[busy["kind"] != 0]
+        cov = np.zeros((tiles, h_out + 1), np.int32)
+        np.add.at(cov, (ex["tile"], ex["lo"]), 1)
+        np.add.at(cov, (ex["tile"], ex["hi"]), -1)
+        assert np.all(np.cumsum(cov, axis=1)[:, :h_out] == 1), f"tiles={tiles}: expand columns"
+    assert len(grids) == 1, "the grid depends only on the token count"

@@ -52,7 +52,7 @@ int fail(int status, const char* fmt, ...) {
 // ---------------------------------------------------------------------------
 constexpr int kMaxKs = 16;            // largest split of the shrink reduction
 constexpr int kMaxDepTiles = 1024 - kCtrTiles;  // counter slots
-constexpr size_t kCounterBytes = kStampOffset + (size_t)kMaxPartials * 8;  // tile counters, then the part stamps
+constexpr size_t kCounterBytes = kStampOffset + (size_t)kMaxPartials * kStampStride;  // tile counters, then the part stamps
 constexpr int kShrinkChunk = 512;     // k elements per item of a split shrink
 constexpr int kExpandBlocks = 48;     // 32-column blocks per expand item of medium batches
 constexpr int kMaxSlots = kMaxJobs;   // adapters per backward group

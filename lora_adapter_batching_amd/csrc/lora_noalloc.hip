@@ -27,7 +27,7 @@ constexpr size_t kScratchBytes = LORA_NOALLOC_SCRATCH_BYTES;
 // layout: tile counters, then one stamp per split-shrink part). Stamps must
 // never equal a current launch's stamp, and launch ids are never 0, so the
 // words are cleared once; partial sums need no clearing.
-constexpr size_t kHandoffBytes = kStampOffset + (size_t)kMaxPartials * 8;
+constexpr size_t kHandoffBytes = kStampOffset + (size_t)kMaxPartials * kStampStride;
 static_assert(kHandoffBytes % 16 == 0 && kHandoffBytes < kScratchBytes, "hand-off words fit the scratch");
 
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];

@@ -34,9 +34,13 @@ enum FwdMode : int32_t {
 
 // Counter layout inside the workspace (int32 words): per-tile arrival
 // counters of split shrink-only calls. The part stamps of kModeFusedDep
-// follow at byte offset kStampOffset (one uint64 per (tile, k-chunk)).
+// follow at byte offset kStampOffset: one uint64 per (tile, k-chunk), each
+// on a cache line of its own (kStampStride bytes apart), so that the
+// expands polling one part's stamp do not share a line with the polls and
+// stores of other parts' stamps.
 constexpr int kCtrTiles = 64;        // per-tile arrival counters start here
 constexpr int kStampOffset = 4096;   // bytes from the counters to the stamps
+constexpr int kStampStride = 128;    // bytes from one part's stamp to the next
 // The epoch of device-planned calls: kEpochSlots uint64 words, one per
 // kEpochStride bytes. Every call adds 1 << kEpochShift to every slot, so
 // between calls all slots hold the same multiple of it, whose high bits

@@ -184,8 +184,9 @@ def test_workspace_size_bounds():
             sizes[(T, op)] = n.value
     assert sizes[(16, B.OP_EXPAND)] == 0
     # forward workspaces grow with the batch's tile count up to a fixed cap
-    # (2048 split-shrink parts of 32 x 64 fp32 here, plus 20 KiB of hand-off words)
-    cap = 2048 * 32 * 64 * 4 + 20 * 1024
+    # (2048 split-shrink parts of 32 x 64 fp32 here, plus 260 KiB of hand-off
+    # words: 4 KiB of counters, then 2048 stamps on 128-byte lines)
+    cap = 2048 * 32 * 64 * 4 + 260 * 1024
     assert sizes[(16, B.OP_FUSED)] < sizes[(4096, B.OP_FUSED)] == sizes[(65536, B.OP_FUSED)] <= cap + 512
     assert sizes[(16, B.OP_BACKWARD)] < sizes[(65536, B.OP_BACKWARD)]
     n = ctypes.c_size_t(0)

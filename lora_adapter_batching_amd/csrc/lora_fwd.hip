@@ -115,6 +115,9 @@ __device__ __forceinline__ TileInfo tile_info(const PT& P, int g, TileInfo* lds)
     // a byte entry indexed by value is otherwise read with a vector load)
     const auto* kb = (const char __attribute__((address_space(4)))*)__builtin_amdgcn_kernarg_segment_ptr();
     {
+      static_assert(CAP % 4 == 0 && PlanCap<PT>::kOffRank % 4 == 0 && PlanCap<PT>::kOffSlot % 4 == 0 &&
+                        PlanCap<PT>::kOffProj % 4 == 0,
+                    "a byte entry's word lies inside its array");
       typedef const uint32_t __attribute__((address_space(4)))* KWord;
       const int word = sel & ~3, shift = 8 * (sel & 3);
       t.rank = (int)((*reinterpret_cast<KWord>(kb + PlanCap<PT>::kOffRank + word) >> shift) & 0xffu);

@@ -131,6 +131,37 @@ def test_weight_addresses_from_device_tables_and_host_copies():
         assert np.array_equal(a, b, equal_nan=True)
 
 
+@pytest.mark.parametrize("n_adapters", [16, 17])
+@pytest.mark.parametrize("host_tables", [True, False])
+def test_small_plan_capacity_edge(n_adapters, host_tables):
+    """A batch of exactly as many segments as the small plan holds (16) and
+    one more (17, the large plan): every segment a different rank, scale
+    and weight address, so that each entry of the plan's tables (including
+    the byte entries packed four to a word) is read for its own segment.
+    Fused, shrink and expand against the oracle."""
+    L = _L()
+    import torch
+    ranks = [1, 8, 12, 16, 24, 32, 40, 64, 96, 128, 4, 20, 48, 72, 100, 2, 56][:n_adapters]
+    rng = np.random.default_rng(1600 + n_adapters)
+    ids = np.concatenate([np.arange(n_adapters), rng.integers(0, n_adapters, size=80)]).astype(np.int32)
+    rng.shuffle(ids)
+    prob = make_custom(160 + n_adapters, 520, 264, ranks, scales="random", ids=ids, y0=True)
+    gp = GpuProblem(prob, host_tables=host_tables)
+    lens = np.diff(np.asarray(gp.seg_starts))
+    active = [a for a, n in zip(gp.seg_adapter, lens) if a >= 0 and n > 0]
+    assert len(active) == n_adapters  # segments with tokens and an adapter
+    ob = oracle_batch(prob)
+    _say(f"small-plan edge: {n_adapters} segments, host_tables={host_tables}")
+    y, u = _run_fused(gp)
+    _check_forward(gp, ob, y, u)
+    u2 = gp.new_u()
+    L.sgmv_shrink(gp.x, gp.adapters, gp.segments, u2, L.new_workspace(L.OP_SHRINK, gp.adapters, gp.segments))
+    y2 = gp.new_y()
+    L.sgmv_expand(u2, gp.adapters, gp.segments, y2)
+    torch.cuda.synchronize()
+    _check_forward(gp, ob, y2, u2)
+
+
 @pytest.mark.parametrize("host_tables", [True, False])
 def test_in_place_weight_update_and_table_swap(host_tables):
     """Adapters stay registered while their weights change: (1) new values

@@ -747,6 +747,9 @@ MULTI_CASES = [
     (100, 264, (72, 520), 3, (0, 1, 12, 40, 64), False, False),   # ragged widths, rank 0 in some projections
     (3000, 1032, (1032, 200, 3080, 8), 6, (8, 16, 24, 128), True, True),  # medium batch, four projections
     (18000, 264, (200, 264), 5, (8, 16, 32), False, True),        # large batch (one on-chip item per tile)
+    # four projections of four adapters: 16 segments, the small plan's
+    # capacity, so projection 3 sits in the last entries of its tables
+    (200, 520, (264, 72, 136, 200), 4, (8, 16, 32, 64), False, True),
 ]
 
 

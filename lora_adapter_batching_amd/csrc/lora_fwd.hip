@@ -324,6 +324,22 @@ __device__ __forceinline__ uint32_t row_off(const PT& P, const TileInfo& t, cons
 // shuffles. visit(j, key, first sorted position, first tile, tokens) runs
 // for each of the lane's kPer slots j (key = lane * kPer + j; slots past
 // key N carry no tokens). Returns the tile count (all lanes).
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
+// 1, 2, 4 and 8 lanes inside each row of 16 (a lane shifted in from outside
+// its row reads 0), then the last lane of row 0 added to row 1 (and of row 2
+// to row 3), then the last lane of row 1 to rows 2 and 3. Lane shuffles,
+// which go through the LDS crossbar, made the in-launch planner's scan
+// about 0.3 us longer per launch.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return v;
+}
+
 template <typename F>
 __device__ __forceinline__ int scan_keys(const int* cnt, int N, F&& visit) {
   constexpr int kPer = (kMaxGraphAdapters + 1 + 63) / 64;
@@ -336,15 +352,7 @@ __device__ __forceinline__ int scan_keys(const int* cnt, int N, F&& visit) {
     ls += c[j];
     lt += i < N ? (c[j] + kTileM - 1) / kTileM : 0;
   }
-  int ss = ls, st = lt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int us = __shfl_up(ss, o), ut = __shfl_up(st, o);
-    if (lane >= o) {
-      ss += us;
-      st += ut;
-    }
-  }
+  const int ss = wave_incl_scan(ls), st = wave_incl_scan(lt);
   int tok = ss - ls, tile = st - lt;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -353,7 +361,7 @@ __device__ __forceinline__ int scan_keys(const int* cnt, int N, F&& visit) {
     tok += c[j];
     tile += i < N ? (c[j] + kTileM - 1) / kTileM : 0;
   }
-  return __shfl(st, 63);
+  return __builtin_amdgcn_readlane(st, 63);
 }
 
 // Lane 0's 64-bit value in SGPRs. readfirstlane returns a signed int: each
@@ -461,11 +469,13 @@ __device__ __forceinline__ SelfItem self_plan(const PT& P, const Lds& L, int b, 
   if (wave == 0) {
     constexpr int kPer = (kMaxGraphAdapters + 1 + 63) / 64;
     int kt[kPer], kk[kPer], kc[kPer];
-    const int tiles = scan_keys(S.cnt, N, [&](int j, int i, int tok, int tile, int c) {
+    // (the tile count cannot exceed the bound the grid was laid out for;
+    // the clamp keeps every item inside the workspace regardless)
+    const int tiles = min(scan_keys(S.cnt, N, [&](int j, int i, int tok, int tile, int c) {
       kt[j] = tile;
       kk[j] = tok;
       kc[j] = i < N ? c : 0;  // key N (no adapter) has no tiles
-    });
+    }), P.n_tiles);
     FwdItem it = item0;
     int nblk = P.nblk;
     if (self_relayout_needed(P.self_relayout, tiles, P.n_tiles)) {
@@ -1647,7 +1657,10 @@ __global__ __launch_bounds__(kPlanThreads) void dev_plan_kernel(DevPlanArgs a) {
       start[k] = s;
     }
     __syncthreads();
-    if (key >= 0) a.perm[wave_cnt[wave][key] + rank_in_wave] = t;
+    if (key >= 0) {
+      const int pos = wave_cnt[wave][key] + rank_in_wave;
+      if (pos >= 0 && pos < a.T) a.perm[pos] = t;  // always inside; the check keeps it so
+    }
     __syncthreads();
   }
 }

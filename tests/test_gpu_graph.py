@@ -95,6 +95,10 @@ CASES = [
     ("one_token", 1, 256, 512, [8, 8], 8),
     # the decode gate_up projection at full size (the graph-replay bench's widest call)
     ("gate_up_2560x19456", 256, 2560, 19456, [32] * 8, 32),
+    # the widest count scan (256 adapters: keys in every lane of the wave),
+    # planned inside the launch at its token limit and by the plan kernel
+    ("scan_256ad_1024tok", 1024, 512, 264, [8, 16, 4, 32, 0, 24, 12, 40] * 32, 40),
+    ("scan_256ad_2048tok", 2048, 264, 512, [16, 8, 32, 4] * 64, 32),
 ]
 
 

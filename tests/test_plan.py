@@ -426,6 +426,7 @@ GRAPH_BIG = [
     (8, 4096, 4096, 16, 8192),
     (32, 4096, 14336, 128, 4096),
     (16, 1024, 1024, 64, 20000),
+    (256, 264, 512, 32, 2048),  # the widest count scan, through the plan kernel
 ]
 
 

@@ -147,15 +147,18 @@ def dev_bf16(bits):
 class DecodeStep:
     """Pre-marshalled C-ABI calls for one decode step over a rotation set."""
 
-    def __init__(self, projs, nsets, request_order=False):
+    def __init__(self, projs, nsets, request_order=False, host_rows=False):
         import torch
         import lora_adapter_batching_amd as L
         from lora_adapter_batching_amd import binding as Bd
         self.lib = L.load()
         # request_order: x and y stay in the order the tokens arrived; every
         # step uploads its sorted-position -> row table (from the step's own
-        # bookkeeping) and the kernels gather x rows and scatter y rows
+        # bookkeeping) and the kernels gather x rows and scatter y rows.
+        # host_rows: the table is passed as the host copy instead, which the
+        # small decode launches carry in their arguments (no upload)
         self.request_order = request_order
+        self.host_rows = request_order and host_rows
         self.Bd = Bd
         p0 = projs["q"]
         self.ids = np.ascontiguousarray(p0.token_ids, np.int32)
@@ -170,7 +173,10 @@ class DecodeStep:
         self.names = ["q", "o", "gate_up"]
         self.sets = []
         self.keep = []
-        if request_order:
+        if self.host_rows:
+            self.cseg_host = Bd.CSegments(self.T, self.N + 1, self.starts.ctypes.data, self.adap.ctypes.data, 0,
+                                          self.perm.ctypes.data)
+        elif request_order:
             # one pinned host table, device table and event per rotation set:
             # a slot's host table is rewritten only after its last upload ended
             self.rows_host = [torch.zeros(self.T, dtype=torch.int32).pin_memory() for _ in range(nsets)]
@@ -210,7 +216,7 @@ class DecodeStep:
         lib = self.lib
         k = i % len(self.sets)
         perm_ptr = self.perm.ctypes.data
-        if self.request_order:
+        if self.request_order and not self.host_rows:
             if self.rows_ev[k] is not None:
                 self.rows_ev[k].synchronize()
             perm_ptr = self.rows_host[k].data_ptr()
@@ -220,7 +226,9 @@ class DecodeStep:
             raise RuntimeError(lib.lora_last_error().decode())
         calls = self.sets[k]
         segp = ctypes.byref(self.cseg)
-        if self.request_order:
+        if self.host_rows:
+            segp = ctypes.byref(self.cseg_host)
+        elif self.request_order:
             import torch
             self.rows_dev[k].copy_(self.rows_host[k], non_blocking=True)
             ev = torch.cuda.Event()
@@ -277,23 +285,32 @@ def bench_decode(steps, warmup, nsets=16):
 
 
 def bench_decode_request_order(steps=200, warmup=20, nsets=16):
-    """The decode step with x and y left in request order: the step's
-    bookkeeping writes the row table into pinned memory, it is uploaded, and
-    the kernels gather x rows and scatter y rows through it."""
+    """The decode step with x and y left in request order, the kernels
+    gathering x rows and scattering y rows: with the row table as the host
+    copy that the launches carry in their arguments (no upload), and with
+    the table uploaded to the device every step."""
     import torch
     from workloads import make_c2_projections
-    ds = DecodeStep(make_c2_projections(1), nsets, request_order=True)
-    for i in range(warmup):
-        ds.step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ds.step(warmup + i)
-    torch.cuda.synchronize()
-    sec = (time.perf_counter() - t0) / steps
-    return _entry("decode_request_order_token_rows_qwen3_4b_256tok_8x_r32", np.array([sec]),
-                  ds.bytes_per_step, ds.flops_per_step,
-                  {"note": "wall time per step incl. bookkeeping and the row-table upload"})
+    projs = make_c2_projections(1)
+    out = []
+    for host_rows, name, note in (
+            (True, "decode_request_order_token_rows_qwen3_4b_256tok_8x_r32",
+             "wall time per step incl. bookkeeping; row table carried in the launch arguments"),
+            (False, "decode_request_order_token_rows_uploaded_qwen3_4b_256tok_8x_r32",
+             "wall time per step incl. bookkeeping and the row-table upload")):
+        ds = DecodeStep(projs, nsets, request_order=True, host_rows=host_rows)
+        for i in range(warmup):
+            ds.step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ds.step(warmup + i)
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / steps
+        out.append(_entry(name, np.array([sec]), ds.bytes_per_step, ds.flops_per_step, {"note": note}))
+        del ds
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_decode_graph(steps=200, warmup=20, nsets=16):
@@ -619,7 +636,7 @@ def bench_secondary(reps=20):
     import torch
     import lora_adapter_batching_amd as L
     from workloads import make_config
-    out = [bench_decode_request_order(), bench_decode_graph()]
+    out = bench_decode_request_order() + [bench_decode_graph()]
     torch.cuda.empty_cache()
     out += bench_multi_projection()
     torch.cuda.empty_cache()

@@ -132,6 +132,17 @@ typedef struct lora_segments_t {
                                  inside it is treated as absent (it reads as zero
                                  and is never written; the offset is computed in
                                  64 bits, so it cannot wrap onto another row). */
+  const int32_t* token_rows_host; /* HOST [T] or NULL: the same rows as token_rows (the
+                                 same rules apply). A forward launch of at most 16
+                                 segments over at most 256 tokens then carries the
+                                 rows in its launch arguments and reads no device
+                                 table, so a request-order decode batch needs no
+                                 upload of its rows: token_rows may be NULL for
+                                 lora_sgmv_shrink, _expand, _fused, _fused_multi and
+                                 _fused_noalloc calls of that size (larger ones are
+                                 refused with LORA_INVALID_ARGUMENT).
+                                 lora_packed_backward always needs token_rows. The
+                                 library only reads the copy during the call. */
 } lora_segments_t;
 
 /*

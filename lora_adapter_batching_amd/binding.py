@@ -43,7 +43,7 @@ class CAdapters(ctypes.Structure):
 class CSegments(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("num_segments", ctypes.c_int32),
                 ("seg_starts", ctypes.c_void_p), ("seg_adapter", ctypes.c_void_p),
-                ("token_rows", ctypes.c_void_p)]
+                ("token_rows", ctypes.c_void_p), ("token_rows_host", ctypes.c_void_p)]
 
 
 class CGraphAdapters(ctypes.Structure):
@@ -172,17 +172,26 @@ class Segments:
     """A batch in sorted-position order cut into one-adapter segments.
 
     seg_starts [S+1] and seg_adapter [S] are host arrays; token_rows is an
-    optional int32 device tensor (row of x/y used by each sorted position).
+    optional int32 device tensor (row of x/y used by each sorted position);
+    token_rows_host an optional int32 host array with the same rows (small
+    forward launches carry it in their arguments; token_rows may then be
+    None for them).
     """
 
-    def __init__(self, seg_starts, seg_adapter, token_rows=None):
+    def __init__(self, seg_starts, seg_adapter, token_rows=None, token_rows_host=None):
         self.seg_starts = np.ascontiguousarray(seg_starts, dtype=np.int32)
         self.seg_adapter = np.ascontiguousarray(seg_adapter, dtype=np.int32)
         self.token_rows = token_rows
         S = int(self.seg_adapter.shape[0])
         T = int(self.seg_starts[-1]) if self.seg_starts.size else 0
+        self.token_rows_host = None
+        if token_rows_host is not None:
+            self.token_rows_host = np.ascontiguousarray(token_rows_host, dtype=np.int32)
+            if self.token_rows_host.shape != (T,):
+                raise ValueError(f"token_rows_host must hold {T} rows, got shape {self.token_rows_host.shape}")
         self._c = CSegments(T, S, self.seg_starts.ctypes.data if S or self.seg_starts.size else 0,
-                            self.seg_adapter.ctypes.data if S else 0, _ptr(token_rows))
+                            self.seg_adapter.ctypes.data if S else 0, _ptr(token_rows),
+                            self.token_rows_host.ctypes.data if self.token_rows_host is not None else 0)
 
     @property
     def num_tokens(self) -> int:

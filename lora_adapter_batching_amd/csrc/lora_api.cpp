@@ -23,7 +23,7 @@
 
 namespace lora {
 hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream, const uint64_t* wptr,
-                      const uint64_t* vptr);
+                      const uint64_t* vptr, const int32_t* rows, int n_rows);
 hipError_t launch_transpose(const TransposePlan& P, hipStream_t stream);
 hipError_t launch_wgrad(const WgradPlan& P, int grid, hipStream_t stream);
 hipError_t launch_wgrad_reduce(const WgradReducePlan& R, hipStream_t stream);
@@ -91,7 +91,10 @@ DeviceInfo device_info() {
 struct Launcher {
   virtual ~Launcher() = default;
   virtual DeviceInfo dev() = 0;
-  virtual hipError_t fwd(const FwdPlan& P, int rbmax, const uint64_t* wptr, const uint64_t* vptr) = 0;
+  // rows (host, n_rows entries) or null: the token-row table a small launch
+  // carries in its arguments
+  virtual hipError_t fwd(const FwdPlan& P, int rbmax, const uint64_t* wptr, const uint64_t* vptr,
+                         const int32_t* rows, int n_rows) = 0;
   virtual hipError_t transpose(const TransposePlan& P) = 0;
   virtual hipError_t wgrad(const WgradPlan& P, int grid) = 0;
   virtual hipError_t reduce(const WgradReducePlan& R) = 0;
@@ -102,8 +105,9 @@ struct HipLauncher final : Launcher {
   hipStream_t stream;
   explicit HipLauncher(void* s) : stream(static_cast<hipStream_t>(s)) {}
   DeviceInfo dev() override { return device_info(); }
-  hipError_t fwd(const FwdPlan& P, int rbmax, const uint64_t* wptr, const uint64_t* vptr) override {
-    return launch_fwd(P, rbmax, stream, wptr, vptr);
+  hipError_t fwd(const FwdPlan& P, int rbmax, const uint64_t* wptr, const uint64_t* vptr, const int32_t* rows,
+                 int n_rows) override {
+    return launch_fwd(P, rbmax, stream, wptr, vptr, rows, n_rows);
   }
   hipError_t transpose(const TransposePlan& P) override { return launch_transpose(P, stream); }
   hipError_t wgrad(const WgradPlan& P, int grid) override { return launch_wgrad(P, grid, stream); }
@@ -199,12 +203,24 @@ int check_rows(const void* p, int64_t ld, int width, const char* name, bool need
 // fit in that span is refused here (a row past the span would be read as
 // zero and not written).
 int check_gather(const lora_segments_t* s, int64_t ld, int width, const char* name, bool needed) {
-  if (!needed || !s->token_rows || s->num_tokens == 0) return LORA_OK;
+  if (!needed || (!s->token_rows && !s->token_rows_host) || s->num_tokens == 0) return LORA_OK;
   const int64_t span = ((int64_t)(s->num_tokens - 1) * ld + width) * 2;
   if (span > kGatherSpan)
     return fail(LORA_INVALID_ARGUMENT,
                 "%s: with token_rows, %d rows of stride %lld span %lld bytes, above the %lld-byte gather limit",
                 name, s->num_tokens, (long long)ld, (long long)span, (long long)kGatherSpan);
+  return LORA_OK;
+}
+
+// A call given only the host copy of the row table (no device table) must
+// fit in one small launch, which carries the rows in its arguments.
+int check_host_rows(const lora_segments_t* s, size_t n_active, const char* what) {
+  if (!s->token_rows_host || s->token_rows) return LORA_OK;
+  if (n_active > (size_t)kSmallSeg || s->num_tokens > kPlanRows)
+    return fail(LORA_INVALID_ARGUMENT,
+                "%s: token_rows is NULL and the host copy alone serves only batches of at most %d segments "
+                "and %d tokens (this one: %zu segments, %d tokens)",
+                what, kSmallSeg, kPlanRows, n_active, s->num_tokens);
   return LORA_OK;
 }
 
@@ -356,6 +372,8 @@ struct FwdCall {
   int scale_in_shrink;
   int K, N;
   const int32_t* token_rows;
+  const int32_t* rows_host;  // host copy of the row table (small launches carry it), or null
+  int n_rows;                // its entries (the batch's tokens)
   float* partials;
   int32_t* counters;
   int rmax;  // largest rank of the adapters (partials row length)
@@ -680,7 +698,16 @@ int run_fwd(const FwdCall& c, std::vector<ActiveSeg> segs, const std::vector<int
       }
       P.ptrs_in_plan = 1;
     }
-    const hipError_t e = P.ptrs_in_plan ? launcher.fwd(P, rbmax, wq, vq) : launcher.fwd(P, rbmax, nullptr, nullptr);
+    // a small launch over at most kPlanRows positions carries the rows from
+    // the caller's host copy: no device table is read, none need be uploaded
+    const bool rows_in_plan = c.rows_host && ns <= kSmallSeg && c.n_rows <= kPlanRows;
+    if (rows_in_plan) P.token_rows = nullptr;
+    else if (c.rows_host && !c.token_rows)
+      return fail(LORA_INVALID_ARGUMENT, "internal planner error (host row table on a large launch)");
+    const int32_t* rows = rows_in_plan ? c.rows_host : nullptr;
+    const int n_rows = rows_in_plan ? c.n_rows : 0;
+    const hipError_t e = P.ptrs_in_plan ? launcher.fwd(P, rbmax, wq, vq, rows, n_rows)
+                                        : launcher.fwd(P, rbmax, nullptr, nullptr, rows, n_rows);
     if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
   }
   return LORA_OK;
@@ -785,6 +812,7 @@ static int sgmv_shrink_impl(const void* x, int64_t ldx, const lora_adapters_t* a
   if ((st = check_gather(segments, ldx, adapters->h_in, "x", true))) return st;
   if ((st = check_u(u, ldu, max_rank_used(segs), "u"))) return st;
   if (!adapters->A_ptrs) return fail(LORA_INVALID_ARGUMENT, "A_ptrs is NULL");
+  if ((st = check_host_rows(segments, segs.size(), "lora_sgmv_shrink"))) return st;
   const WsLayout L = ws_layout(LORA_OP_SHRINK, adapters, segments);
   if ((st = check_ws(ws, ws_bytes, L.total))) return st;
   FwdCall c{};
@@ -795,6 +823,7 @@ static int sgmv_shrink_impl(const void* x, int64_t ldx, const lora_adapters_t* a
   if (adapters->A_ptrs_host && adapters->B_ptrs_host) c.Wtab_host = adapters->A_ptrs_host;
   c.K = adapters->h_in; c.N = adapters->h_out;
   c.token_rows = segments->token_rows;
+  c.rows_host = segments->token_rows_host; c.n_rows = segments->num_tokens;
   c.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
   c.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.counters);
   c.rmax = max_rank_all(adapters);
@@ -811,6 +840,7 @@ static int sgmv_expand_impl(const float* u, int64_t ldu, const lora_adapters_t* 
   if ((st = check_gather(segments, ldy, adapters->h_out, "y", true))) return st;
   if ((st = check_u(u, ldu, max_rank_used(segs), "u"))) return st;
   if (!adapters->B_ptrs) return fail(LORA_INVALID_ARGUMENT, "B_ptrs is NULL");
+  if ((st = check_host_rows(segments, segs.size(), "lora_sgmv_expand"))) return st;
   FwdCall c{};
   c.mode_op = LORA_OP_EXPAND;
   c.Y = static_cast<uint16_t*>(y); c.ldy = ldy;
@@ -819,6 +849,7 @@ static int sgmv_expand_impl(const float* u, int64_t ldu, const lora_adapters_t* 
   if (adapters->A_ptrs_host && adapters->B_ptrs_host) c.Vtab_host = adapters->B_ptrs_host;
   c.K = adapters->h_in; c.N = adapters->h_out;
   c.token_rows = segments->token_rows;
+  c.rows_host = segments->token_rows_host; c.n_rows = segments->num_tokens;
   c.rmax = max_rank_all(adapters);
   return run_fwd(c, segs, {}, launcher);
 }
@@ -836,6 +867,7 @@ static int sgmv_fused_impl(const void* x, int64_t ldx, const lora_adapters_t* ad
   if ((st = check_gather(segments, ldx, adapters->h_in, "x", true))) return st;
   if ((st = check_gather(segments, ldy, adapters->h_out, "y", true))) return st;
   if (u_save && (st = check_u(u_save, ldu, max_rank_used(segs), "u_save"))) return st;
+  if ((st = check_host_rows(segments, segs.size(), "lora_sgmv_fused"))) return st;
   if (!adapters->A_ptrs || !adapters->B_ptrs) return fail(LORA_INVALID_ARGUMENT, "A_ptrs/B_ptrs is NULL");
   const WsLayout L = ws_layout(LORA_OP_FUSED, adapters, segments);
   if (src) {
@@ -861,6 +893,7 @@ static int sgmv_fused_impl(const void* x, int64_t ldx, const lora_adapters_t* ad
   }
   c.K = adapters->h_in; c.N = adapters->h_out;
   c.token_rows = segments->token_rows;
+  c.rows_host = segments->token_rows_host; c.n_rows = segments->num_tokens;
   c.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
   c.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.counters);
   c.rmax = max_rank_all(adapters);
@@ -959,6 +992,7 @@ static int sgmv_fused_multi_impl(const void* x, int64_t ldx, int32_t num_proj,
   if (segs.empty()) return LORA_OK;
   if ((st = check_rows(x, ldx, adapters[0]->h_in, "x", true))) return st;
   if ((st = check_gather(segments, ldx, adapters[0]->h_in, "x", true))) return st;
+  if ((st = check_host_rows(segments, segs.size(), "lora_sgmv_fused_multi"))) return st;
   // every output is written: no two may share a base address, and none may be x
   for (int p = 0; p < num_proj; ++p) {
     if (y[p] == x) return fail(LORA_INVALID_ARGUMENT, "y[%d] is x: outputs must not overlap x", p);
@@ -987,6 +1021,7 @@ static int sgmv_fused_multi_impl(const void* x, int64_t ldx, int32_t num_proj,
     }
   }
   c.token_rows = segments->token_rows;
+  c.rows_host = segments->token_rows_host; c.n_rows = segments->num_tokens;
   const size_t part_off = (kCounterBytes + 255) / 256 * 256;
   c.counters = reinterpret_cast<int32_t*>(ws);
   c.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + part_off);
@@ -1029,6 +1064,8 @@ static int packed_backward_impl(const void* x, int64_t ldx, const void* dy, int6
     if ((st = check_gather(segments, ldx, adapters->h_in, "x", true))) return st;
     if ((st = check_gather(segments, lddy, adapters->h_out, "dy", true))) return st;
     if ((st = check_gather(segments, lddx, adapters->h_in, "dx", dx != nullptr))) return st;
+    if (segments->token_rows_host && !segments->token_rows)
+      return fail(LORA_INVALID_ARGUMENT, "lora_packed_backward: the row table must be in device memory (token_rows)");
     if (u && (st = check_u(u, ldu, max_rank_used(segs), "u"))) return st;
     if (!adapters->A_ptrs || !adapters->B_ptrs) return fail(LORA_INVALID_ARGUMENT, "A_ptrs/B_ptrs is NULL");
   }
@@ -1477,7 +1514,7 @@ int sgmv_fused_graph_impl(const void* x, int64_t ldx, const lora_graph_adapters_
     P.self_slots = 2 * dev.cus;
   }
   const int rbmax = a->max_rank <= 32 ? 1 : (a->max_rank <= 64 ? 2 : 4);
-  e = launcher.fwd(P, rbmax, nullptr, nullptr);
+  e = launcher.fwd(P, rbmax, nullptr, nullptr, nullptr, 0);
   if (e != hipSuccess) return fail(LORA_DEVICE_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
   return LORA_OK;
 }
@@ -1523,7 +1560,7 @@ struct Recorder final : Launcher {
     ++n;
   }
   DeviceInfo dev() override { return d; }
-  hipError_t fwd(const FwdPlan& P, int rbmax, const uint64_t*, const uint64_t*) override {
+  hipError_t fwd(const FwdPlan& P, int rbmax, const uint64_t*, const uint64_t*, const int32_t*, int) override {
     (void)rbmax;
     if (P.grid <= 0) return hipErrorInvalidConfiguration;
     const int launch = launches++;

@@ -47,6 +47,7 @@ template <int CAP>
 struct PlanCap<FwdPlanT<CAP>> {
   static constexpr int v = CAP;  // segment capacity of a plan type
   static constexpr bool self = false;  // launches planned inside themselves
+  static constexpr bool rows = false;  // plans that carry the token-row table
   // byte offsets of the weight-address arrays in the plan, which is the
   // kernel's only explicit argument and so starts the kernel-argument segment
   static constexpr int kOffW = __builtin_offsetof(FwdPlanT<CAP>, seg_wptr);
@@ -65,6 +66,20 @@ template <>
 struct PlanCap<FwdPlanSelf> : PlanCap<FwdPlanT<kSmallSeg>> {
   static constexpr bool self = true;
 };
+// A small plan that also carries the sorted-position -> row table (from the
+// caller's host copy), so that a request-order batch needs no table in
+// device memory and no upload before the launch.
+struct FwdPlanRows : FwdPlanT<kSmallSeg> {
+  int32_t rows[kPlanRows];
+};
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winvalid-offsetof"
+template <>
+struct PlanCap<FwdPlanRows> : PlanCap<FwdPlanT<kSmallSeg>> {
+  static constexpr bool rows = true;
+  static constexpr int kOffRows = __builtin_offsetof(FwdPlanRows, rows);
+};
+#pragma clang diagnostic pop
 
 // Finds the segment that holds tile g. Small plans (decode batches): a scalar
 // scan of the whole table, which the compiler reads from the kernel
@@ -290,7 +305,7 @@ template <typename PT>
 __device__ __forceinline__ TileRows tile_rows(const uint16_t* base, int64_t ld, int width, const PT& P,
                                               const TileInfo& t) {
   TileRows tr;
-  tr.gather = PlanCap<PT>::self || P.token_rows != nullptr;
+  tr.gather = PlanCap<PT>::self || PlanCap<PT>::rows || P.token_rows != nullptr;
   tr.ld2 = ld * 2;
   tr.lim = kGatherSpan - (int64_t)width * 2;
   if (tr.gather)
@@ -308,8 +323,15 @@ __device__ __forceinline__ uint32_t row_off(const PT& P, const TileInfo& t, cons
   if (n >= t.cnt) return kOff;
   if (!tr.gather) return (uint32_t)((int64_t)n * tr.ld2);
   int row;
-  if constexpr (PlanCap<PT>::self) row = t.rows[n];
-  else row = P.token_rows[t.p0 + n];
+  if constexpr (PlanCap<PT>::self) {
+    row = t.rows[n];
+  } else if constexpr (PlanCap<PT>::rows) {
+    typedef const int32_t __attribute__((address_space(4)))* KRow;
+    const auto* kb = (const char __attribute__((address_space(4)))*)__builtin_amdgcn_kernarg_segment_ptr();
+    row = reinterpret_cast<KRow>(kb + PlanCap<PT>::kOffRows)[t.p0 + n];
+  } else {
+    row = P.token_rows[t.p0 + n];
+  }
   const int64_t off = (int64_t)row * tr.ld2;
   return (off < 0 || off > tr.lim) ? kOff : (uint32_t)off;
 }
@@ -1480,7 +1502,7 @@ __global__ __launch_bounds__(kThreads, 2) void sgmv_fwd_kernel(PT P) {
   // going to memory one after the other (decode gate_up, 2560 -> 19456:
   // 14.8 -> 13.9 us; q and o unchanged).
   if constexpr (!PlanCap<PT>::self && PlanCap<PT>::v <= kSmallSeg) {
-    static_assert(sizeof(PT) <= 17 * 64, "one word per line of the plan");
+    static_assert(sizeof(FwdPlanT<kSmallSeg>) <= 17 * 64, "one word per line of the plan");
     asm volatile("" ::"s"(line(0)), "s"(line(1)), "s"(line(2)), "s"(line(3)), "s"(line(4)), "s"(line(5)),
                  "s"(line(6)), "s"(line(7)), "s"(line(8)), "s"(line(9)), "s"(line(10)), "s"(line(11)),
                  "s"(line(12)), "s"(line(13)), "s"(line(14)), "s"(line(15)), "s"(line(16)), "s"(P.mode),
@@ -1528,28 +1550,42 @@ static hipError_t launch_fwd_t(const PT& P, int rbmax, hipStream_t stream) {
 // the kernel argument, and its size is part of every launch's host cost.
 // wptr / vptr (or null): per segment weight addresses for small plans whose
 // header sets ptrs_in_plan.
+// Copies the segment table of a small launch (and its weight addresses, or
+// zeros) from the host plan.
+static void fill_small_plan(FwdPlanT<kSmallSeg>& Q, const FwdPlan& P, const uint64_t* wptr,
+                            const uint64_t* vptr) {
+  static_cast<FwdHeader&>(Q) = static_cast<const FwdHeader&>(P);
+  for (int i = 0; i < P.n_seg; ++i) {
+    Q.seg_wptr[i] = wptr ? wptr[i] : 0;
+    Q.seg_vptr[i] = vptr ? vptr[i] : 0;
+    Q.seg_tok0[i] = P.seg_tok0[i];
+    Q.seg_ntok[i] = P.seg_ntok[i];
+    Q.seg_tile0[i] = P.seg_tile0[i];
+    Q.seg_adapter[i] = P.seg_adapter[i];
+    Q.seg_scale[i] = P.seg_scale[i];
+    Q.seg_rank[i] = P.seg_rank[i];
+    Q.seg_slot[i] = P.seg_slot[i];
+    Q.seg_proj[i] = P.seg_proj[i];
+  }
+}
+
 hipError_t launch_fwd(const FwdPlan& P, int rbmax, hipStream_t stream, const uint64_t* wptr,
-                      const uint64_t* vptr) {
+                      const uint64_t* vptr, const int32_t* rows, int n_rows) {
   if (P.self_ids) {
     FwdPlanSelf Q{};
     static_cast<FwdHeader&>(Q) = static_cast<const FwdHeader&>(P);
     return launch_fwd_t(Q, rbmax, stream);
   }
+  if (rows) {
+    // the caller guarantees n_seg <= kSmallSeg and n_rows <= kPlanRows
+    FwdPlanRows Q{};
+    fill_small_plan(Q, P, wptr, vptr);
+    for (int i = 0; i < n_rows; ++i) Q.rows[i] = rows[i];
+    return launch_fwd_t(Q, rbmax, stream);
+  }
   if (P.n_seg <= kSmallSeg) {
     FwdPlanT<kSmallSeg> Q{};
-    static_cast<FwdHeader&>(Q) = static_cast<const FwdHeader&>(P);
-    for (int i = 0; i < P.n_seg; ++i) {
-      Q.seg_wptr[i] = wptr ? wptr[i] : 0;
-      Q.seg_vptr[i] = vptr ? vptr[i] : 0;
-      Q.seg_tok0[i] = P.seg_tok0[i];
-      Q.seg_ntok[i] = P.seg_ntok[i];
-      Q.seg_tile0[i] = P.seg_tile0[i];
-      Q.seg_adapter[i] = P.seg_adapter[i];
-      Q.seg_scale[i] = P.seg_scale[i];
-      Q.seg_rank[i] = P.seg_rank[i];
-      Q.seg_slot[i] = P.seg_slot[i];
-      Q.seg_proj[i] = P.seg_proj[i];
-    }
+    fill_small_plan(Q, P, wptr, vptr);
     return launch_fwd_t(Q, rbmax, stream);
   }
   return launch_fwd_t(P, rbmax, stream);

@@ -149,6 +149,7 @@ struct FwdHeader {
 };
 
 constexpr int kSmallSeg = 16;  // capacity of the small plan (decode batches)
+constexpr int kPlanRows = 256; // token rows a small plan can carry (host copy of token_rows)
 
 // Segment table of a launch (struct of arrays), CAP entries. Small plans can
 // also carry each segment's weight addresses (taken from the caller's host

@@ -43,10 +43,13 @@ class GpuProblem:
 
     use_token_rows: keep x/y/dy in request order on the device and pass the
     permutation as token_rows (in-kernel gather/scatter); otherwise rows are
-    permuted on the host before upload.
+    permuted on the host before upload. host_rows ("only" or "both") also
+    passes the permutation as the host copy token_rows_host, alone or beside
+    the device table.
     """
 
-    def __init__(self, prob, use_token_rows: bool = False, y0: bool = False, host_tables: bool = True):
+    def __init__(self, prob, use_token_rows: bool = False, y0: bool = False, host_tables: bool = True,
+                 host_rows: str = ""):
         import torch
         import lora_adapter_batching_amd as L
         self.prob = prob
@@ -69,8 +72,12 @@ class GpuProblem:
         self.adapters = L.Adapters(self.A, self.B, prob.ranks, prob.scales, prob.h_in, prob.h_out,
                                    host_tables=host_tables)
         tr = torch.from_numpy(self.perm.copy()).to("cuda") if use_token_rows else None
+        # host_rows: "" (device table only), "only" (host copy alone), "both"
+        rows_host = self.perm.copy() if use_token_rows and host_rows else None
+        if use_token_rows and host_rows == "only":
+            tr = None
         self.token_rows = tr
-        self.segments = L.Segments(self.seg_starts, self.seg_adapter, tr)
+        self.segments = L.Segments(self.seg_starts, self.seg_adapter, tr, rows_host)
         self.rmax = max(1, int(np.max(prob.ranks)) if prob.N else 1)
 
     def sorted_rows(self, t) -> np.ndarray:

@@ -373,6 +373,51 @@ def test_decode_request_order_token_rows_full():
         _check_forward(gp, ob, y, u)
 
 
+def test_decode_request_order_host_row_copy():
+    """Decode projections in request order with the row table passed only as
+    a host copy (carried in the launch arguments, no device table): the
+    oracle's result, and the same bits as the device-table call."""
+    import torch
+    projs = make_config("decode")
+    for name, prob in projs.items():
+        ob = oracle_batch(prob)
+        outs = []
+        for mode in ("only", ""):
+            gp = GpuProblem(prob, use_token_rows=True, host_rows=mode)
+            assert (gp.token_rows is None) == (mode == "only")
+            _say(f"decode request order {name}, host rows {mode or 'none'}")
+            y, u = _run_fused(gp)
+            _check_forward(gp, ob, y, u)
+            outs.append((y.view(torch.int16).cpu().numpy(), u.cpu().numpy()))
+        assert np.array_equal(outs[0][0], outs[1][0])
+        assert np.array_equal(outs[0][1], outs[1][1], equal_nan=True)
+
+
+@pytest.mark.parametrize("mode", ["only", "both"])
+def test_host_row_copy_shrink_expand_mixed(mode):
+    """Mixed ranks, -1 ids and an empty segment in request order, the row
+    table as a host copy (alone, or beside the device table): fused, shrink
+    and expand against the oracle; rows without an adapter untouched."""
+    L = _L()
+    import torch
+    prob = _mixed_problem(7, T=200)
+    gp = GpuProblem(prob, use_token_rows=True, host_rows=mode)
+    ob = oracle_batch(prob)
+    _say(f"host row copy ({mode}) fused")
+    y, u = _run_fused(gp)
+    _check_forward(gp, ob, y, u)
+    _say(f"host row copy ({mode}) shrink / expand")
+    u2 = gp.new_u()
+    L.sgmv_shrink(gp.x, gp.adapters, gp.segments, u2, L.new_workspace(L.OP_SHRINK, gp.adapters, gp.segments))
+    y2 = gp.new_y()
+    L.sgmv_expand(u2, gp.adapters, gp.segments, y2)
+    torch.cuda.synchronize()
+    _check_forward(gp, ob, y2, u2)
+    a = ob.token_adapter()
+    skip = np.array([i < 0 or prob.ranks[i] == 0 for i in a])
+    assert np.array_equal(gp.sorted_rows(y)[skip], gp.sorted_rows(gp.y_init)[skip])
+
+
 def test_token_rows_far_row_is_absent_not_wrapped():
     """A token_rows entry whose byte offset lies past 4 GiB (row 3 + 2^21 of a
     19456-wide bf16 matrix: the offset is row 3's plus a multiple of 2^32)

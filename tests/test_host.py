@@ -92,12 +92,12 @@ def _adapters(ranks=(8, 16), scales=None, h_in=64, h_out=32, A=FAKE, Bp=FAKE):
     return c, (ranks, scales)
 
 
-def _segments(starts, adapter, T=None, token_rows=0):
+def _segments(starts, adapter, T=None, token_rows=0, token_rows_host=0):
     starts = np.ascontiguousarray(starts, np.int32)
     adapter = np.ascontiguousarray(adapter, np.int32)
     T = int(starts[-1]) if T is None else T
     c = B.CSegments(T, len(adapter), starts.ctypes.data, adapter.ctypes.data if len(adapter) else 0,
-                    token_rows)
+                    token_rows, token_rows_host)
     return c, (starts, adapter)
 
 
@@ -281,6 +281,42 @@ def test_token_rows_gather_span_is_checked_on_the_host():
     st = lib.lora_packed_backward(FAKE, 64, FAKE, 16384, 0, 0, ctypes.byref(ad), ctypes.byref(sg), 0, 0,
                                   FAKE, FAKE, 0, FAKE, 0, 0)
     assert st == B.LORA_INVALID_ARGUMENT and "dy: with token_rows" in lib.lora_last_error().decode()
+
+
+def test_host_row_copy_alone_serves_only_small_launches():
+    """A call given only the host copy of the row table (no device table) must
+    fit in one small launch (at most 16 segments, 256 tokens), which carries
+    the rows; larger ones, and every backward, are refused before any GPU
+    call. With both tables given, large calls use the device one."""
+    lib = L.load()
+    rows = np.arange(400, dtype=np.int32)
+    host = rows.ctypes.data
+
+    def fused(T, n_seg, token_rows=0, token_rows_host=host):
+        cuts = np.linspace(0, T, n_seg + 1).astype(np.int32)
+        ad, ka = _adapters(ranks=[8] * n_seg, h_in=64, h_out=32)
+        sg, ks = _segments(cuts, np.arange(n_seg, dtype=np.int32), token_rows=token_rows,
+                           token_rows_host=token_rows_host)
+        # a zero-byte workspace stops a call that passes every argument check
+        return _fused(ad, sg, wsb=0), (ad, ka, sg, ks)
+
+    assert fused(256, 16)[0] == B.LORA_WORKSPACE_TOO_SMALL, lib.lora_last_error().decode()
+    for T, n_seg in ((257, 2), (64, 17)):
+        st, keep = fused(T, n_seg)
+        assert st == B.LORA_INVALID_ARGUMENT
+        assert "host copy alone" in lib.lora_last_error().decode()
+        st, keep = fused(T, n_seg, token_rows=FAKE)
+        assert st == B.LORA_WORKSPACE_TOO_SMALL, lib.lora_last_error().decode()
+    # shrink-only: the same limit
+    ad, ka = _adapters(ranks=(16, 8), h_in=64, h_out=32)
+    sg, ks = _segments([0, 150, 300], [0, 1], token_rows_host=host)
+    st = lib.lora_sgmv_shrink(FAKE, 64, ctypes.byref(ad), ctypes.byref(sg), FAKE, 16, FAKE, 0, 0)
+    assert st == B.LORA_INVALID_ARGUMENT and "host copy alone" in lib.lora_last_error().decode()
+    # the backward reads rows in kernels that take no plan rows
+    sg, ks = _segments([0, 3, 5], [0, 1], token_rows_host=host)
+    st = lib.lora_packed_backward(FAKE, 64, FAKE, 32, 0, 0, ctypes.byref(ad), ctypes.byref(sg), 0, 0,
+                                  FAKE, FAKE, 0, FAKE, 1 << 30, 0)
+    assert st == B.LORA_INVALID_ARGUMENT and "device memory" in lib.lora_last_error().decode()
 
 
 def test_noalloc_refuses_batches_beyond_its_static_scratch():

@@ -786,7 +786,7 @@ def test_backward_split_is_deterministic():
 # Several projections over one x in one launch
 # ---------------------------------------------------------------------------
 MULTI_CASES = [
-    # (T, h_in, outputs, adapters, rank choices, token_rows, host_tables)
+    # (T, h_in, outputs, adapters, rank choices, token_rows (True / "host"), host_tables)
     (256, 2560, (4096, 1024, 1024), 8, (32,), False, True),      # q/k/v-like decode, plan in device tables
     (256, 2560, (4096, 1024, 1024), 4, (8, 16, 32), True, True),  # small plan: weight addresses in the launch
     (100, 264, (72, 520), 3, (0, 1, 12, 40, 64), False, False),   # ragged widths, rank 0 in some projections
@@ -795,6 +795,8 @@ MULTI_CASES = [
     # four projections of four adapters: 16 segments, the small plan's
     # capacity, so projection 3 sits in the last entries of its tables
     (200, 520, (264, 72, 136, 200), 4, (8, 16, 32, 64), False, True),
+    # request order with the row table as a host copy alone (carried in the launch)
+    (200, 520, (264, 72, 136), 4, (8, 16, 32, 64), "host", True),
 ]
 
 
@@ -815,7 +817,8 @@ def test_fused_multi_projection(case):
             pr = copy.copy(pr)
             pr.x = probs[0].x  # one x for every projection
         probs.append(pr)
-    gps = [GpuProblem(pr, use_token_rows=use_rows, host_tables=host_tables) for pr in probs]
+    gps = [GpuProblem(pr, use_token_rows=bool(use_rows), host_tables=host_tables,
+                      host_rows="only" if use_rows == "host" else "") for pr in probs]
     ys = [g.new_y() for g in gps]
     ads = [g.adapters for g in gps]
     ws = L.new_workspace_multi(ads, gps[0].segments)

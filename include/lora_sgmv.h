@@ -32,8 +32,9 @@
  *    h_out must be multiples of 8; u needs 4-byte alignment.
  *  - Token order: the kernels walk tokens in "sorted position" order,
  *    p = 0..T-1, in which every segment is a contiguous run. With
- *    token_rows == NULL, sorted position p is row p of x/y/dx/dy. With a
- *    token_rows table, position p reads and writes row token_rows[p] of
+ *    no row table, sorted position p is row p of x/y/dx/dy. With a
+ *    token_rows table (or its host copy token_rows_host, see
+ *    lora_segments_t), position p reads and writes row token_rows[p] of
  *    x/y/dx/dy (an in-kernel gather/scatter, so a request-order batch need
  *    not be permuted by the caller). u and du always use sorted positions.
  *  - Streams: `stream` is a hipStream_t (NULL = the null stream). Calls only

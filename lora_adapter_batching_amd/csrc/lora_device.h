@@ -70,18 +70,22 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_addr, uint32
   (void)m0_out;
 }
 
-// kNT marks an access non-temporal (data streamed once: activations and
-// outputs), so that it does not displace reused adapter weights from L2.
+// Buffer loads and stores of 16 bytes. The _stream forms set the
+// non-temporal bit: the output rows y, which every launch reads and writes
+// exactly once, go through the caches as streamed data, so they neither
+// displace the adapter weights and the hand-off parts that are reused nor
+// linger as dirty lines. Measured on the decode MLP-up launch (2560 -> 19456,
+// 8 adapters, cold inputs) 13.9 -> 12.0 us, on the MLP-up batch of 32 mixed
+// ranks 85 -> 75 us, on the 8192-token prefill 52 -> 46 us.
 constexpr int kNT = 2;
-__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off, int aux = 0) {
-  return aux ? __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNT)
-             : __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
-__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v, int aux = 0) {
-  if (aux)
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kNT);
-  else
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+__device__ __forceinline__ u32x4 bld16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNT);
+}
+__device__ __forceinline__ void bst16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kNT);
 }
 __device__ __forceinline__ uint32_t bld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);

@@ -791,7 +791,7 @@ __device__ __forceinline__ void stg_load(const StgCtx<RB>& C, int cs, StgRegs<RB
   const bool cv = col < C.c1;
   const uint32_t cbytes = 2u * (uint32_t)col;
 #pragma unroll
-  for (int j = 0; j < G::YV; ++j) R.y[j] = bld16(C.yr, cv ? C.yoff[j] + cbytes : kOff);
+  for (int j = 0; j < G::YV; ++j) R.y[j] = bld16_stream(C.yr, cv ? C.yoff[j] + cbytes : kOff);
   if (C.vec16) {
     // the chunk's V rows [cs, cs + CW) are one contiguous span
     const uint32_t base = (uint32_t)(cs * C.ldv * 2);
@@ -889,7 +889,7 @@ __device__ __forceinline__ void stg_store(const StgCtx<RB>& C, int cs, const uin
   const uint32_t cbytes = 2u * (uint32_t)col;
 #pragma unroll
   for (int j = 0; j < G::YV; ++j)
-    bst16(C.yr, cv ? C.yoff[j] + cbytes : kOff, ld16(ys + (r0 + RPJ * j) * G::CWP + c));
+    bst16_stream(C.yr, cv ? C.yoff[j] + cbytes : kOff, ld16(ys + (r0 + RPJ * j) * G::CWP + c));
 }
 
 template <int RB, typename PT>
@@ -1043,7 +1043,7 @@ __device__ __forceinline__ void exp_load(const ExpCtx<RB>& C, int j, BlkRegs<RB>
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int col = col0 + 16 * r + 8 * h;
-    R.y[r] = bld16(C.yr, off_if_below(C.yrow + 2u * (uint32_t)col, col, C.c1));
+    R.y[r] = bld16_stream(C.yr, off_if_below(C.yrow + 2u * (uint32_t)col, col, C.c1));
   }
 }
 
@@ -1067,7 +1067,7 @@ __device__ __forceinline__ void exp_block(const ExpCtx<RB>& C, const PFrags<RB>&
     unpack8(R.y[r], f);
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = f[i] + C.oscale * acc[8 * r + i];
-    bst16(C.yr, off_if_below(C.yrow + 2u * (uint32_t)col, col, C.c1), pack8(f));
+    bst16_stream(C.yr, off_if_below(C.yrow + 2u * (uint32_t)col, col, C.c1), pack8(f));
   }
 }
 

@@ -138,6 +138,9 @@ __device__ __forceinline__ void wg_load(const WgradPlan& P, const uint16_t* Z, i
   const int lane = threadIdx.x & 63, g = lane >> 4;
   const bool live = c.seg < seg_end;
   const int cnt = live ? min(32, c.tend - c.t0) : 0;  // valid tokens of the step (uniform)
+  // Z (x or dy) is read by this workgroup alone, once: non-temporal loads
+  // (with the streamed dy of the dU/dX pass, the packed-training backward
+  // went from 550 to 539 us).
   // Z: a resource over the step's rows (contiguous positions) or over the
   // whole matrix (token_rows gather: a row is read only if it lies wholly
   // inside the resource, with its offset kept in 64 bits)
@@ -162,11 +165,11 @@ __device__ __forceinline__ void wg_load(const WgradPlan& P, const uint16_t* Z, i
     const uint32_t off = in ? (uint32_t)(row_bytes + (int64_t)ccol * 2) : kOff;
     if constexpr (QN == 4) {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(zr, (int)off, 0, 0);
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(zr, (int)off, 0, kNT);
       R.z[e][0] = v[0];
       R.z[e][1] = v[1];
     } else {
-      R.z[e][0] = __builtin_amdgcn_raw_buffer_load_b32(zr, (int)off, 0, 0);
+      R.z[e][0] = __builtin_amdgcn_raw_buffer_load_b32(zr, (int)off, 0, kNT);
     }
   }
   // Q (fp32, sorted positions): element (tt, k) = (e2 / 16KB, e2 % 16KB)

@@ -69,6 +69,18 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_addr, uint32
                : "memory");
   (void)m0_out;
 }
+// The same with the non-temporal bit, for data that the launch reads once.
+__device__ __forceinline__ void load_lds16_stream(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  int m0_out;
+  i32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] = __builtin_amdgcn_readfirstlane(rsrc[q]);
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen nt lds"
+               : "={m0}"(m0_out)
+               : "s"(lds_addr), "v"(voff), "s"(r)
+               : "memory");
+  (void)m0_out;
+}
 
 // Buffer loads and stores of 16 bytes. The _stream forms set the
 // non-temporal bit: the output rows y, which every launch reads and writes

@@ -600,6 +600,7 @@ struct ShrinkCtx {
   uint32_t roff[Geo<RB>::BPW];  // byte offset of this lane's row in each of the wave's blocks
   uint32_t cbytes;              // this lane's column within a chunk (bytes)
   int kb, ke;
+  bool xs;                      // x rows streamed (read by this item alone)
 };
 
 // Issues the wave's block loads of chunk `chunk` into `buf`.
@@ -614,8 +615,14 @@ __device__ __forceinline__ void shrink_issue(const ShrinkCtx<RB>& C, int chunk, 
   // The LDS destination must be scalar (it goes to M0).
   const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane(
       (int)((uint32_t)reinterpret_cast<uintptr_t>(buf) + (uint32_t)wave * G::BS));
+  if (C.xs) {
 #pragma unroll
-  for (int j = 0; j < G::NBX / 4; ++j) load_lds16(C.xr, base + 4u * j * G::BS, kv ? C.roff[j] + kbytes : kOff);
+    for (int j = 0; j < G::NBX / 4; ++j)
+      load_lds16_stream(C.xr, base + 4u * j * G::BS, kv ? C.roff[j] + kbytes : kOff);
+  } else {
+#pragma unroll
+    for (int j = 0; j < G::NBX / 4; ++j) load_lds16(C.xr, base + 4u * j * G::BS, kv ? C.roff[j] + kbytes : kOff);
+  }
 #pragma unroll
   for (int j = G::NBX / 4; j < G::BPW; ++j)
     load_lds16(C.wr, base + 4u * j * G::BS, kv ? C.roff[j] + kbytes : kOff);
@@ -671,6 +678,12 @@ __device__ __forceinline__ void shrink_lds(const PT& P, const TileInfo& t, int k
   C.cbytes = 16u * (uint32_t)c;
   C.kb = kb;
   C.ke = ke;
+  // one item per tile (large batches, u kept on chip): each x row is read by
+  // this workgroup alone, so it is streamed (packed-training forward, 65536
+  // tokens: 306 -> 299 us). Launches that split a tile's shrink into parts
+  // measured the same or slower with streamed x (8192-token prefill at rank
+  // 64: 57 -> 61 us), so they keep plain loads.
+  C.xs = P.mode == kModeFusedTile && P.nc == 1;
 #pragma unroll
   for (int b = 0; b < RB; ++b) acc[b] = zero_acc16();
   const int nch = __builtin_amdgcn_readfirstlane((ke - kb + G::KC - 1) / G::KC);

@@ -6,6 +6,9 @@ hipcc cross-compiles the device code to assembly; no GPU needed).
   register, and the compiler must not use M0 anywhere else.
 - No kernel spills to scratch memory (a spill would also add vector memory
   operations that the explicit load counts of the shrink do not expect).
+- The output rows y are streamed: every 16-byte buffer store of the forward
+  kernels (the y stores) carries the non-temporal bit, and so do the x loads
+  of one-item-per-tile launches (a second form of the LDS-destination load).
 """
 import os
 import re
@@ -43,7 +46,7 @@ def bwd_asm(tmp_path_factory):
 
 def test_lds_loads_use_scalar_m0_and_descriptor(fwd_asm):
     lines = fwd_asm.splitlines()
-    n_loads = 0
+    n_loads = n_stream = 0
     in_asm = False
     for i, l in enumerate(lines):
         s = l.split(";")[0].strip()
@@ -59,13 +62,22 @@ def test_lds_loads_use_scalar_m0_and_descriptor(fwd_asm):
             m = re.match(r"s_mov_b32 m0, (\S+)", s)
             if m:
                 assert re.fullmatch(r"s\d+", m.group(1)), f"line {i}: M0 from {m.group(1)}"
-            m = re.match(r"buffer_load_dwordx4 v\d+, (\S+), 0 offen lds", s)
+            m = re.match(r"buffer_load_dwordx4 v\d+, (\S+), 0 offen( nt)? lds", s)
             if m:
                 n_loads += 1
+                n_stream += m.group(2) is not None
                 assert re.fullmatch(r"s\[\d+:\d+\]", m.group(1)), f"line {i}: descriptor {m.group(1)}"
         else:
             assert not re.search(r"\bm0\b", s), f"line {i}: compiler use of M0: {s}"
     assert n_loads > 0
+    assert 0 < n_stream < n_loads, (n_stream, n_loads)
+
+
+def test_output_row_stores_are_streamed(fwd_asm):
+    stores = [l.split(";")[0].strip() for l in fwd_asm.splitlines() if "buffer_store_dwordx4" in l]
+    assert stores
+    plain = [s for s in stores if not re.search(r"\bnt\b", s)]
+    assert not plain, plain[:3]
 
 
 def test_no_scratch(fwd_asm, bwd_asm):

@@ -318,14 +318,16 @@ def bench_decode_graph(steps=200, warmup=20, nsets=16):
     device-planned calls (lora_sgmv_fused_graph: one fused launch each that
     groups the 256 request-order ids itself, every table on the device),
     captured once per rotation set and replayed; wall time and GPU time per
-    replay."""
+    replay. A second entry captures eight consecutive steps (24 launches)
+    per graph, as a serving loop that captures a whole step of many layers
+    would: the launches are the same, only the graph boundaries are fewer."""
     import torch
     import lora_adapter_batching_amd as L
     from workloads import make_c2_projections
     projs = make_c2_projections(1)
     p0 = projs["q"]
     T = int(p0.T)
-    graphs, keep = [], []
+    graphs, keep, set_calls = [], [], []
     work_b = work_f = 0
     perm, starts, adap = L.segments_from_ids(p0.token_ids, p0.N)
     for name in ("q", "o", "gate_up"):
@@ -358,6 +360,7 @@ def bench_decode_graph(steps=200, warmup=20, nsets=16):
             for c in calls:
                 L.sgmv_fused_graph(*c)
         graphs.append(g)
+        set_calls.append(calls)
     torch.cuda.synchronize()
     for i in range(warmup):
         graphs[i % nsets].replay()
@@ -371,9 +374,37 @@ def bench_decode_graph(steps=200, warmup=20, nsets=16):
     torch.cuda.synchronize()
     sec = (time.perf_counter() - t0) / steps
     gpu = e0.elapsed_time(e1) * 1e-3 / steps
-    return _entry("decode_step_graph_replay_device_planned_qwen3_4b_256tok_8x_r32", np.array([sec]), work_b, work_f,
+    out = [_entry("decode_step_graph_replay_device_planned_qwen3_4b_256tok_8x_r32", np.array([sec]), work_b, work_f,
                   {"gpu_us_per_step": round(gpu * 1e6, 2),
-                   "note": "one HIP graph per step: 3 fused launches that plan on the device, ids on the device"})
+                   "note": "one HIP graph per step: 3 fused launches that plan on the device, ids on the device"})]
+    # eight steps per graph: rotation sets 0-7 and 8-15
+    per = 8
+    big = []
+    for h in range(nsets // per):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(per * h, per * h + per):
+                for c in set_calls[s]:
+                    L.sgmv_fused_graph(*c)
+        big.append(g)
+    torch.cuda.synchronize()
+    for i in range(max(2, warmup // per)):
+        big[i % len(big)].replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // per)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(reps):
+        big[i % len(big)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / (reps * per)
+    gpu = e0.elapsed_time(e1) * 1e-3 / (reps * per)
+    out.append(_entry("decode_step_in_8_step_graph_device_planned_qwen3_4b_256tok_8x_r32", np.array([sec]),
+                      work_b, work_f,
+                      {"gpu_us_per_step": round(gpu * 1e6, 2),
+                       "note": "eight decode steps (24 device-planned launches) per replayed HIP graph"}))
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -636,7 +667,7 @@ def bench_secondary(reps=20):
     import torch
     import lora_adapter_batching_amd as L
     from workloads import make_config
-    out = bench_decode_request_order() + [bench_decode_graph()]
+    out = bench_decode_request_order() + bench_decode_graph()
     torch.cuda.empty_cache()
     out += bench_multi_projection()
     torch.cuda.empty_cache()

@@ -212,6 +212,56 @@ def test_graph_capture_replays_with_new_ids_weights_and_tables(case):
         assert np.array_equal(got[inactive], oracle.widen(y0)[inactive])
 
 
+
+def test_graph_of_several_steps_shares_workspaces():
+    """Two decode steps of two projections captured in one graph (four
+    device-planned launches), each projection's workspace used by both
+    steps, all calls reading one device id array. Replayed with new ids and
+    fresh outputs; every output matches the oracle on every replay."""
+    import torch
+    import lora_adapter_batching_amd as L
+    T = 256
+    rng = np.random.default_rng(21)
+    ids0 = rng.integers(0, 8, size=T).astype(np.int32)
+    shapes = [(2560, 2560, [32] * 8, 32), (1024, 4096, [8, 16, 0, 64, 32, 16, 8, 24], 64)]
+    projs, tables, wss = [], [], []
+    for j, (h_in, h_out, ranks, max_rank) in enumerate(shapes):
+        prob = make_custom(30 + j, h_in, h_out, ranks, scales="random", ids=ids0, y0=True)
+        projs.append(prob)
+        tables.append(_Tables(prob, max_rank))
+        wss.append(L.new_workspace_graph(tables[-1].ga, T))
+    ids = torch.from_numpy(ids0.copy()).cuda()
+    steps = []  # (projection, x bits, x, y)
+    for s in range(2):
+        for j, prob in enumerate(projs):
+            xb = make_custom(40 + 2 * s + j, prob.h_in, prob.h_out, [8], ids=np.zeros(T, np.int32)).x
+            steps.append((j, xb, dev_bf16(xb), torch.zeros((T, prob.h_out), dtype=torch.bfloat16, device="cuda")))
+    for j, xb, x, y in steps:  # warm-up outside the capture
+        L.sgmv_fused_graph(x, tables[j].ga, ids, y, wss[j])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    _say("capture two steps x two projections")
+    with torch.cuda.graph(g):
+        for j, xb, x, y in steps:
+            L.sgmv_fused_graph(x, tables[j].ga, ids, y, wss[j])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        new_ids = ids0 if rep == 0 else rng.integers(-1, 9, size=T).astype(np.int32)
+        ids.copy_(torch.from_numpy(new_ids))
+        y0s = []
+        for k, (j, xb, x, y) in enumerate(steps):
+            y0 = make_custom(500 + 10 * rep + k, projs[j].h_in, projs[j].h_out, [8], ids=np.zeros(T, np.int32),
+                             y0=True).y0
+            y.copy_(dev_bf16(y0))
+            y0s.append(y0)
+        torch.cuda.synchronize()
+        _say(f"replay {rep} of the two-step graph")
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (j, xb, x, y) in enumerate(steps):
+            e = rel_err(to_f64(y), tables[j].oracle_y(xb, y0s[k], new_ids))
+            assert e <= BF16_TOL, f"replay {rep} call {k}: y rel err {e:.3e}"
+
 def test_double_buffered_tables_update_during_decode():
     """Two table sets differ in one adapter's weight buffers. A decode on
     stream 1 reads set 0 while stream 2 overwrites the other buffer (set 1's)
